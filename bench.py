@@ -1,0 +1,293 @@
+"""Benchmark one Muon / MONA optimizer step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A "step" is one full optimizer step over every matrix of the workload (MONA,
+momentum, normalisation, Newton-Schulz, decoupled update), with gradients and
+state already resident in HBM.  Rank 0 prints one JSON line with the step time
+(the headline value), the dominant kernel's roofline (per-launch durations
+measured with HIP events on the launch stream), and the fp64 CPU oracle timed
+on this host's cores on a bounded sample.
+"""
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "Muon step ms per model + NS TFLOP/s (% MFMA peak), elementwise GB/s"
+PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}   # MI355X dense MFMA
+PEAK_HBM_GBPS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="nanochat_6l_d192")
+    ap.add_argument("--variant", default=None, help="direct | gram (default: the workload's first)")
+    ap.add_argument("--no-graph", action="store_true", help="launch kernels directly instead of a HIP graph")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the oracle timing")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--trace-steps", type=int, default=None, help="steps timed per launch (default: --steps)")
+    return ap.parse_args()
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime torch loaded (same SONAME)."""
+
+    def __init__(self, n):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            h = ctypes.c_void_p()
+            rc = self.hip.hipEventCreateWithFlags(ctypes.byref(h), 0)
+            if rc != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed: %d" % rc)
+            self.arr[i] = h
+        self.n = n
+
+    def elapsed_ms(self, i, j):
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), self.arr[i], self.arr[j])
+        if rc != 0:
+            raise RuntimeError("hipEventElapsedTime failed: %d" % rc)
+        return ms.value
+
+    def close(self):
+        for i in range(self.n):
+            self.hip.hipEventDestroy(self.arr[i])
+
+
+def setup(w, variant, device):
+    import torch
+    from workloads import make_grads, make_state
+    gen_dev = device if w.name.startswith("gram_tall") else "cpu"
+    state = make_state(w, device=gen_dev)
+    grads = make_grads(w, step=1, device=gen_dev)
+    params = []
+    for st, g in zip(state, grads):
+        p = {k: v.to(device) for k, v in st.items()}
+        p["grad"] = g.to(device)
+        params.append(p)
+    torch.cuda.synchronize()
+    return params
+
+
+def step_kwargs(w, variant):
+    divisor, restart = w.settings_for(variant)
+    return dict(lr=w.lr, mu=w.mu, beta_a=w.beta_a, alpha=w.alpha, weight_decay=w.weight_decay,
+                ns_steps=w.ns_steps, variant=variant, ns_dtype=w.ns_dtype, divisor=divisor,
+                restart_every=restart)
+
+
+def coeff_table(w):
+    base = {"cubic": (1.5, -0.5, 0.0), "quintic": (15.0 / 8.0, -5.0 / 4.0, 3.0 / 8.0)}[w.coeffs]
+    return [list(base)] * w.ns_steps
+
+
+def gpu_timing(args, w, variant):
+    import torch
+    import newton_schulz_matrix_momentum_amd as nsm
+    from newton_schulz_matrix_momentum_amd import _lib
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    params = setup(w, variant, dev)
+    kw = step_kwargs(w, variant)
+    coeffs = coeff_table(w)
+    # MONA workloads time steps after the first (D = G - G_prev is live)
+    step_idx = 1 if w.mona else 0
+
+    def one_step():
+        nsm.muon_step(params, coeffs=coeffs, step=step_idx, **kw)
+
+    for _ in range(max(args.warmup, 1)):
+        one_step()
+    torch.cuda.synchronize()
+
+    graph = None
+    if not args.no_graph:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            one_step()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            one_step()
+        for _ in range(2):
+            graph.replay()
+        torch.cuda.synchronize()
+
+    run = graph.replay if graph is not None else one_step
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        run()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = start.elapsed_time(end) / args.steps
+
+    # per-launch durations: HIP events recorded by libmuon around every launch
+    tsteps = args.trace_steps or args.steps
+    cap = 512
+    ev = HipEvents(2 * cap)
+    stages = (ctypes.c_int32 * cap)()
+    work = (ctypes.c_double * cap)()
+    trace = _lib.MuonTrace(events=ctypes.cast(ev.arr, ctypes.POINTER(ctypes.c_void_p)),
+                           stages=ctypes.cast(stages, ctypes.POINTER(ctypes.c_int32)),
+                           work=ctypes.cast(work, ctypes.POINTER(ctypes.c_double)), capacity=cap, count=0)
+    per_stage = {}
+    launches_per_step = 0
+    for _ in range(tsteps):
+        nsm.muon_step(params, coeffs=coeffs, step=step_idx, trace=trace, **kw)
+        torch.cuda.synchronize()
+        n = min(trace.count, cap)
+        launches_per_step = trace.count
+        for i in range(n):
+            name = _lib.STAGE_NAMES[stages[i]]
+            d = per_stage.setdefault(name, {"ms": 0.0, "work": 0.0, "launches": 0})
+            d["ms"] += ev.elapsed_ms(2 * i, 2 * i + 1)
+            d["work"] += work[i]
+            d["launches"] += 1
+    ev.close()
+    for d in per_stage.values():
+        d["ms"] /= tsteps
+        d["work"] /= tsteps
+        d["launches"] /= tsteps
+    return params, ms_per_step, wall, per_stage, launches_per_step, graph is not None
+
+
+def cpu_baseline(args, w, variant, params):
+    """The oracle as it stands, on this host's cores, on a bounded sample:
+    one matrix of each shape class, each repeated until its share of the time
+    budget is spent; the per-step time is extrapolated by matrix counts."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([t.get("num_threads", 1) for t in threadpool_info() if t.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    divisor, restart = w.settings_for(variant)
+    coeffs = oracle.coefficient_table(w.coeffs, w.ns_steps)
+    classes = {}
+    for i, (r, c) in enumerate(w.shapes):
+        classes.setdefault((r, c), []).append(i)
+    budget = args.cpu_seconds / max(len(classes), 1)
+    total_ms = 0.0
+    sample = []
+    for (r, c), idx in classes.items():
+        p = params[idx[0]]
+        snap = {k: v.detach().cpu().double().numpy() for k, v in p.items() if hasattr(v, "detach")}
+        reps, spent = 0, 0.0
+        while spent < budget or reps == 0:
+            t0 = time.perf_counter()
+            oracle.muon_step_matrix(snap["weight"], snap["grad"], snap["momentum"], lr=w.lr, mu=w.mu,
+                                    weight_decay=w.weight_decay, coeffs=coeffs, variant=variant, divisor=divisor,
+                                    restart_every=restart, accel=snap.get("accel"), prev_grad=snap.get("prev_grad"),
+                                    beta_a=w.beta_a, alpha=w.alpha, step=1 if w.mona else 0)
+            spent += time.perf_counter() - t0
+            reps += 1
+        per = spent / reps
+        total_ms += 1e3 * per * len(idx)
+        sample.append("%dx%d x%d reps (of %d)" % (r, c, reps, len(idx)))
+    return {"value": total_ms, "unit": "ms", "cores": int(cores), "kind": "oracle",
+            "sample": "fp64 numpy oracle, one matrix per shape class: " + "; ".join(sample) +
+                      "; per-step time extrapolated by matrix count"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path (got --gpus %d)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from workloads import WORKLOADS
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    w = WORKLOADS[args.workload]
+    variant = args.variant or w.variants[0]
+    print("bench: workload %s variant %s, %d matrices, %d warmup + %d timed steps" %
+          (w.name, variant, len(w.shapes), args.warmup, args.steps), file=sys.stderr, flush=True)
+    params, ms, wall, per_stage, launches, graphed = gpu_timing(args, w, variant)
+    print("bench: gpu timing done (%.4f ms/step)" % ms, file=sys.stderr, flush=True)
+
+    gemm = per_stage.get("gemm", {"ms": 0.0, "work": 0.0, "launches": 0})
+    ew = [per_stage[k] for k in ("e1", "e2", "e3") if k in per_stage]
+    ew_ms = sum(d["ms"] for d in ew)
+    ew_bytes = sum(d["work"] for d in ew)
+    ns_tflops = gemm["work"] / (gemm["ms"] * 1e-3) / 1e12 if gemm["ms"] > 0 else 0.0
+    ew_gbps = ew_bytes / (ew_ms * 1e-3) / 1e9 if ew_ms > 0 else 0.0
+    peak = PEAK_TFLOPS[w.ns_dtype]
+    # dominant kernel by time per step
+    dom = max(per_stage.items(), key=lambda kv: kv[1]["ms"])[0]
+    if dom == "gemm":
+        per_launch_work = gemm["work"] / gemm["launches"]
+        per_launch_ms = gemm["ms"] / gemm["launches"]
+        roof = {"kernel": "ns_gemm_kernel (%s)" % w.ns_dtype, "bound": "mfma",
+                "achieved": per_launch_work / (per_launch_ms * 1e-3) / 1e12, "peak": peak, "unit": "TFLOP/s",
+                "avg_launch_us": per_launch_ms * 1e3, "work_per_launch": per_launch_work, "traffic": None}
+    else:
+        d = per_stage[dom]
+        per_launch_work = d["work"] / d["launches"]
+        per_launch_ms = d["ms"] / d["launches"]
+        roof = {"kernel": dom, "bound": "hbm", "achieved": per_launch_work / (per_launch_ms * 1e-3) / 1e9,
+                "peak": PEAK_HBM_GBPS, "unit": "GB/s", "avg_launch_us": per_launch_ms * 1e3,
+                "work_per_launch": per_launch_work, "traffic": None}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args, w, variant, params)
+        print("bench: cpu baseline done", file=sys.stderr, flush=True)
+
+    out = {
+        "metric": METRIC,
+        "value": ms,
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.ns_dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "matrices": len(w.shapes), "params": w.numel, "variant": variant,
+                   "ns_steps": w.ns_steps, "coeffs": w.coeffs, "grad_dtype": w.grad_dtype, "ns_dtype": w.ns_dtype,
+                   "mona": w.mona, "hip_graph": graphed, "parallelism": "single_gpu"},
+        "ns_tflops": ns_tflops,
+        "ns_frac_of_peak": ns_tflops / peak,
+        "elementwise_gbps": ew_gbps,
+        "elementwise_frac_of_hbm": ew_gbps / PEAK_HBM_GBPS,
+        "launches_per_step": launches,
+        "stages": {k: {"us_per_step": v["ms"] * 1e3, "launches": v["launches"], "work": v["work"]}
+                   for k, v in per_stage.items()},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "wall_s_timed": wall,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

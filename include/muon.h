@@ -1,0 +1,164 @@
+/*
+ * libmuon -- one Muon / MONA optimizer step over a list of weight matrices,
+ * on one AMD Instinct MI355X (gfx950).
+ *
+ * What one call computes, per matrix (rows x cols, row-major):
+ *
+ *   MONA (only when `accel` is given) -- MONA summary (gist.science paper
+ *   2605.26842), section 2 "Methodologie", "Kernalgoritme", steps 1-3:
+ *       D  = G - G_prev          (D = 0 on the first step, opts->step == 0)
+ *       A  = beta_a * A + (1 - beta_a) * D
+ *       G~ = G + alpha * A ;     G_prev = G
+ *   Momentum -- same section, step 4:      M = mu * M + G~
+ *   Orthogonalisation -- same section, step 4, "O = Newton-Schulz(M)";
+ *   polar(X) = U V^T and its Gram form X (X^T X)^{-1/2} with restarts and a
+ *   safety divisor d -- Gram Newton-Schulz post (quant_prune_distill 677):
+ *       X0 = M / (sqrt(d) * ||M||_F)                (X0 = 0 when M = 0)
+ *       K steps of X <- a_k X + (b_k A + c_k A^2) X,   A = X X^T
+ *       (restart before step k when r > 0, k > 1, (k-1) % r == 0: the
+ *        iterate is divided by sqrt(d); the Gram variant also re-forms its
+ *        Gram matrix from the materialised iterate)
+ *   Decoupled update -- MONA summary, step 4:
+ *       W = W - lr * (gamma * O + lambda * W)
+ *
+ * The acceleration is applied before orthogonalisation (MONA summary,
+ * "Ontwerprichtlijnen").
+ *
+ * Conventions for every entry point:
+ *  - All buffer pointers in muon_param are DEVICE pointers owned by the
+ *    caller.  The library never allocates, frees or retains them.
+ *  - All work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *    stream).  No entry point synchronises the stream or the device.
+ *  - Argument errors are reported synchronously, before anything is
+ *    enqueued, and leave every buffer untouched.  Launch failures return
+ *    MUON_ERR_HIP.  Data is not inspected: NaN/Inf in one matrix propagate
+ *    inside that matrix only.
+ *  - Calls that share a workspace must be ordered on one stream (or the
+ *    caller orders them); the workspace may be reused once stream order
+ *    allows.
+ */
+#ifndef LIBMUON_MUON_H
+#define LIBMUON_MUON_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum muon_status {
+  MUON_OK = 0,
+  MUON_ERR_INVALID_ARG = 1,        /* NULL pointer, bad size, non-finite scalar, aliasing */
+  MUON_ERR_UNSUPPORTED = 2,        /* valid request this build cannot serve */
+  MUON_ERR_WORKSPACE_TOO_SMALL = 3,
+  MUON_ERR_HIP = 4                 /* a HIP launch or runtime call failed */
+} muon_status;
+
+typedef enum muon_dtype {
+  MUON_F32 = 0,
+  MUON_F16 = 1,
+  MUON_BF16 = 2
+} muon_dtype;
+
+typedef enum muon_variant {
+  MUON_NS_DIRECT = 0,   /* Newton-Schulz on X itself                             */
+  MUON_NS_GRAM = 1      /* Newton-Schulz on the smaller Gram matrix, with restarts */
+} muon_variant;
+
+/* One weight matrix and its optimizer state.  Every buffer holds rows*cols
+ * elements, row-major, contiguous, on the device; none may overlap another. */
+typedef struct muon_param {
+  float *weight;        /* fp32, updated in place                                  */
+  const void *grad;     /* grad_dtype, read only                                   */
+  float *momentum;      /* fp32 state M, updated in place; zero before step 0       */
+  float *accel;         /* fp32 MONA state A, updated in place; NULL => plain Muon  */
+  void *prev_grad;      /* grad_dtype, previous gradient; NULL iff accel == NULL    */
+  int64_t rows, cols;   /* >= 1                                                     */
+  float gamma;          /* scale on O in the update (gamma of the MONA update)      */
+  float *ortho_out;     /* optional fp32 rows*cols: receives O; NULL => not written */
+} muon_param;
+
+/* Kind of each launch recorded in a muon_trace. */
+typedef enum muon_stage {
+  MUON_STAGE_E1 = 0,     /* MONA + momentum + Frobenius partials              */
+  MUON_STAGE_NORM = 1,   /* per-matrix normalisation scale                     */
+  MUON_STAGE_E2 = 2,     /* X0 in the Newton-Schulz dtype, both orientations   */
+  MUON_STAGE_GEMM = 3,   /* one grouped Newton-Schulz matrix product           */
+  MUON_STAGE_E3 = 4      /* decoupled weight-decay update                      */
+} muon_stage;
+
+/* Optional per-launch timing.  When muon_options.trace is non-NULL the library
+ * records events[2*i] on the stream before launch i and events[2*i+1] after
+ * it, for the first `capacity` launches of the call, and writes each launch's
+ * muon_stage into stages[i] and its algorithmic work into work[i] (FLOPs for
+ * GEMM launches, bytes moved for the others).  The caller creates the events
+ * (hipEventCreate, timing enabled) and reads them after synchronising.
+ * `count` returns the number of launches of the call (which may exceed
+ * capacity; the excess is not recorded). */
+typedef struct muon_trace {
+  void **events;         /* 2 * capacity hipEvent_t handles                   */
+  int32_t *stages;       /* capacity entries, out                             */
+  double *work;          /* capacity entries, out                             */
+  int32_t capacity;
+  int32_t count;         /* out                                               */
+} muon_trace;
+
+/* Settings shared by every matrix of a call.  Pass NULL for the defaults. */
+typedef struct muon_options {
+  muon_dtype grad_dtype;   /* dtype of grad / prev_grad.              default F32     */
+  muon_dtype ns_dtype;     /* dtype of the Newton-Schulz operands.    default F32;
+                              F16 / BF16 use the MFMA matrix cores with fp32 accumulate */
+  const float *coeffs;     /* HOST array [ns_steps][3] of (a, b, c) per step, or NULL
+                              for the quintic (15/8, -5/4, 3/8) at every step            */
+  float divisor;           /* safety divisor d >= 1.                  default 1         */
+  int32_t restart_every;   /* restart period r >= 0 (0 = never).      default 0         */
+  int64_t step;            /* 0-based optimizer step; 0 => MONA's D is zero.  default 0 */
+  muon_trace *trace;       /* optional launch timing (see muon_trace).  default NULL */
+} muon_options;
+
+/* Fill `o` with the defaults listed above. */
+void muon_options_init(muon_options *o);
+
+/* Device bytes of workspace `muon_step` needs for this exact call (same
+ * params shapes, n, ns_steps, variant and options).  Returns 0 when the
+ * request is invalid (muon_last_error() says why).  The size depends only on
+ * shapes and settings, never on pointer values. */
+size_t muon_workspace_size(const muon_param *params, int n, int ns_steps,
+                           muon_variant variant, const muon_options *opts);
+
+/* One optimizer step over `n` matrices (n >= 0; n == 0 is a no-op).
+ *   params     host array of n muon_param (read during the call only)
+ *   lr, mu     learning rate eta and momentum coefficient
+ *   beta_a     MONA EMA coefficient, alpha MONA acceleration scale
+ *              (ignored for matrices with accel == NULL)
+ *   lambda     decoupled weight decay
+ *   ns_steps   Newton-Schulz steps K, 0 <= K <= 64 (K = 0 => O = X0)
+ *   workspace  device buffer of at least muon_workspace_size(...) bytes,
+ *              256-byte aligned, caller-owned; its contents need no
+ *              initialisation and are clobbered
+ *   stream     hipStream_t (void* here so that C callers need no HIP headers)
+ * Errors: MUON_ERR_INVALID_ARG for NULL weight/grad/momentum, accel/prev_grad
+ * given without the other, rows or cols < 1, ns_steps out of range,
+ * non-finite scalars, divisor < 1, restart_every < 0, buffers that overlap;
+ * MUON_ERR_UNSUPPORTED for an unknown dtype; MUON_ERR_WORKSPACE_TOO_SMALL;
+ * MUON_ERR_HIP when a launch fails. */
+muon_status muon_step(const muon_param *params, int n,
+                      float lr, float mu, float beta_a, float alpha, float lambda,
+                      int ns_steps, muon_variant variant, const muon_options *opts,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+/* Static description of a status code. */
+const char *muon_status_string(muon_status s);
+
+/* Thread-local detail about the last non-OK return on this thread ("" if none). */
+const char *muon_last_error(void);
+
+/* Library version string, e.g. "libmuon 0.1.0 gfx950". */
+const char *muon_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBMUON_MUON_H */

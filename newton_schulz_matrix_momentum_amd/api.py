@@ -1,0 +1,150 @@
+"""Python entry points with the C ABI's names, over torch tensors.
+
+``muon_step`` and ``muon_workspace_size`` marshal torch tensors into
+``muon_param`` records and call libmuon; the stream is torch's current stream
+on the tensors' device.  Tensors must be contiguous and live on the GPU.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Dict, List, Optional, Sequence
+
+import torch
+
+from . import _lib
+
+_DT = {torch.float32: _lib.MUON_F32, torch.float16: _lib.MUON_F16, torch.bfloat16: _lib.MUON_BF16}
+_DT_NAMES = {"f32": _lib.MUON_F32, "fp32": _lib.MUON_F32, "float32": _lib.MUON_F32,
+             "f16": _lib.MUON_F16, "fp16": _lib.MUON_F16, "float16": _lib.MUON_F16,
+             "bf16": _lib.MUON_BF16, "bfloat16": _lib.MUON_BF16}
+_VARIANTS = {"direct": _lib.MUON_NS_DIRECT, "gram": _lib.MUON_NS_GRAM}
+
+
+def _ptr(t: Optional[torch.Tensor], name: str, dtype=None, shape=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a GPU tensor (got %s)" % (name, t.device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s must be %s (got %s)" % (name, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    return t.data_ptr()
+
+
+def _dtype_code(x):
+    if x is None:
+        return None
+    if isinstance(x, torch.dtype):
+        return _DT[x]
+    return _DT_NAMES[str(x).lower()]
+
+
+def _marshal(params: Sequence[Dict], ns_dtype, coeffs, divisor, restart_every, step, trace=None):
+    n = len(params)
+    arr = (_lib.MuonParam * max(n, 1))()
+    grad_dtype = None
+    device = None
+    for i, p in enumerate(params):
+        w = p["weight"]
+        if w.dim() != 2:
+            raise ValueError("param %d: weight must be 2-D" % i)
+        rows, cols = w.shape
+        g = p["grad"]
+        if grad_dtype is None:
+            grad_dtype = g.dtype
+        elif g.dtype != grad_dtype:
+            raise ValueError("all grads of one call must share a dtype (param %d is %s, expected %s)"
+                             % (i, g.dtype, grad_dtype))
+        device = device or w.device
+        for key in ("grad", "momentum", "accel", "prev_grad", "ortho_out"):
+            t = p.get(key)
+            if t is not None and t.device != w.device:
+                raise ValueError("param %d: %s is on %s, weight on %s" % (i, key, t.device, w.device))
+        arr[i].weight = _ptr(w, "weight", torch.float32)
+        arr[i].grad = _ptr(g, "grad", None, (rows, cols))
+        arr[i].momentum = _ptr(p["momentum"], "momentum", torch.float32, (rows, cols))
+        arr[i].accel = _ptr(p.get("accel"), "accel", torch.float32, (rows, cols))
+        arr[i].prev_grad = _ptr(p.get("prev_grad"), "prev_grad", grad_dtype, (rows, cols))
+        arr[i].rows = rows
+        arr[i].cols = cols
+        arr[i].gamma = float(p.get("gamma", 1.0))
+        arr[i].ortho_out = _ptr(p.get("ortho_out"), "ortho_out", torch.float32, (rows, cols))
+    opts = _lib.MuonOptions()
+    _lib.load().muon_options_init(ctypes.byref(opts))
+    if grad_dtype is not None:
+        opts.grad_dtype = _DT[grad_dtype]
+    nsd = _dtype_code(ns_dtype)
+    opts.ns_dtype = nsd if nsd is not None else opts.grad_dtype
+    keep = None
+    if coeffs is not None:
+        flat = [float(v) for row in coeffs for v in row]
+        keep = (ctypes.c_float * len(flat))(*flat)
+        opts.coeffs = ctypes.cast(keep, ctypes.POINTER(ctypes.c_float))
+    opts.divisor = float(divisor)
+    opts.restart_every = int(restart_every)
+    opts.step = int(step)
+    if trace is not None:
+        opts.trace = ctypes.pointer(trace)
+    return arr, n, opts, keep, device
+
+
+def muon_workspace_size(params: Sequence[Dict], *, ns_steps: int = 5, variant: str = "direct", ns_dtype=None,
+                        coeffs=None, divisor: float = 1.0, restart_every: int = 0, step: int = 0) -> int:
+    arr, n, opts, keep, _ = _marshal(params, ns_dtype, coeffs, divisor, restart_every, step)
+    size = _lib.load().muon_workspace_size(arr, n, int(ns_steps), _VARIANTS[variant], ctypes.byref(opts))
+    if size == 0 and n > 0:
+        raise _lib.MuonError(_lib.MUON_ERR_INVALID_ARG, _lib.last_error())
+    return int(size)
+
+
+class Workspace:
+    """A reusable device byte buffer for ``muon_step`` (grows on demand)."""
+
+    def __init__(self):
+        self.buf = None
+
+    def get(self, nbytes: int, device) -> torch.Tensor:
+        if self.buf is None or self.buf.numel() < nbytes or self.buf.device != device:
+            self.buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        return self.buf
+
+
+_default_ws: Dict = {}
+
+
+def muon_step(params: Sequence[Dict], *, lr: float, mu: float, beta_a: float = 0.0, alpha: float = 0.0,
+              weight_decay: float = 0.0, ns_steps: int = 5, variant: str = "direct", ns_dtype=None, coeffs=None,
+              divisor: float = 1.0, restart_every: int = 0, step: int = 0,
+              workspace: Optional[torch.Tensor] = None, trace=None) -> None:
+    """One Muon / MONA step over ``params`` (list of dicts of tensors).
+
+    Each dict holds ``weight`` (fp32, updated), ``grad``, ``momentum`` (fp32,
+    updated) and optionally ``accel`` + ``prev_grad`` (MONA state, updated),
+    ``gamma`` (float) and ``ortho_out`` (fp32, receives O).  Enqueued on the
+    current stream; returns without synchronising.  ``trace`` is an optional
+    ``_lib.MuonTrace`` for per-launch HIP-event timing.
+    """
+    arr, n, opts, keep, device = _marshal(params, ns_dtype, coeffs, divisor, restart_every, step, trace)
+    lib = _lib.load()
+    if n == 0:
+        _lib.check(lib.muon_step(arr, 0, lr, mu, beta_a, alpha, weight_decay, int(ns_steps), _VARIANTS[variant],
+                                 ctypes.byref(opts), None, 0, None))
+        return
+    need = lib.muon_workspace_size(arr, n, int(ns_steps), _VARIANTS[variant], ctypes.byref(opts))
+    if need == 0:
+        raise _lib.MuonError(_lib.MUON_ERR_INVALID_ARG, _lib.last_error())
+    if workspace is None:
+        ws = _default_ws.setdefault(device, Workspace()).get(need, device)
+    else:
+        if workspace.device != device or workspace.dtype != torch.uint8:
+            raise ValueError("workspace must be a uint8 tensor on %s" % device)
+        ws = workspace
+    stream = torch.cuda.current_stream(device).cuda_stream
+    _lib.check(lib.muon_step(arr, n, float(lr), float(mu), float(beta_a), float(alpha), float(weight_decay),
+                             int(ns_steps), _VARIANTS[variant], ctypes.byref(opts), ctypes.c_void_p(ws.data_ptr()),
+                             ws.numel(), ctypes.c_void_p(stream)))

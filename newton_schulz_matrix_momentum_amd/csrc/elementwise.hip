@@ -1,0 +1,334 @@
+// HBM-bound stages of the Muon / MONA step for gfx950.
+//
+//   E1  MONA difference + EMA, heavy-ball momentum, Frobenius partials
+//       (MONA summary, section 2 "Kernalgoritme", steps 1-4)
+//   norm_finalize  per-matrix 1 / (sqrt(d) ||M||_F), fixed summation order
+//   E2  X0 = M / (sqrt(d) ||M||_F) rounded to the Newton-Schulz dtype, stored
+//       in both orientations (Gram Newton-Schulz post: the divisor keeps the
+//       Gram's eigenvalues inside [0, 1])
+//   E3  W = W - lr (gamma O + lambda W)  (MONA summary, step 4)
+//
+// All loads and stores are 16-byte vectors where alignment allows; every
+// reduction runs in a fixed order, so results are bitwise reproducible.
+#include "muon_kernels.h"
+
+#include <math.h>
+
+namespace muon {
+namespace {
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t u) { return __uint_as_float((uint32_t)u << 16); }
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  __bf16 h = (__bf16)f;  // round to nearest even
+  return __builtin_bit_cast(uint16_t, h);
+}
+__device__ __forceinline__ float f16_to_f32(uint16_t u) { return (float)__builtin_bit_cast(_Float16, u); }
+__device__ __forceinline__ uint16_t f32_to_f16(float f) {
+  _Float16 h = (_Float16)f;  // round to nearest even
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+template <int DT> struct Elem;
+template <> struct Elem<kF32> {
+  typedef float raw;
+  static __device__ __forceinline__ float to_f32(raw v) { return v; }
+  static __device__ __forceinline__ raw from_f32(float v) { return v; }
+};
+template <> struct Elem<kBF16> {
+  typedef uint16_t raw;
+  static __device__ __forceinline__ float to_f32(raw v) { return bf16_to_f32(v); }
+  static __device__ __forceinline__ raw from_f32(float v) { return f32_to_bf16(v); }
+};
+template <> struct Elem<kF16> {
+  typedef uint16_t raw;
+  static __device__ __forceinline__ float to_f32(raw v) { return f16_to_f32(v); }
+  static __device__ __forceinline__ raw from_f32(float v) { return f32_to_f16(v); }
+};
+
+// Four consecutive elements of a given dtype: 16 bytes (fp32) or 8 bytes.
+template <int DT> struct Vec4;
+template <> struct Vec4<kF32> {
+  typedef float4 type;
+  static __device__ __forceinline__ void unpack(const type &v, float o[4]) { o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w; }
+  static __device__ __forceinline__ type pack(const float o[4]) { return make_float4(o[0], o[1], o[2], o[3]); }
+};
+template <int DT> struct Vec4Half {
+  typedef uint2 type;
+  static __device__ __forceinline__ void unpack(const type &v, float o[4]) {
+    o[0] = Elem<DT>::to_f32((uint16_t)(v.x & 0xffffu));
+    o[1] = Elem<DT>::to_f32((uint16_t)(v.x >> 16));
+    o[2] = Elem<DT>::to_f32((uint16_t)(v.y & 0xffffu));
+    o[3] = Elem<DT>::to_f32((uint16_t)(v.y >> 16));
+  }
+  static __device__ __forceinline__ type pack(const float o[4]) {
+    type v;
+    v.x = (uint32_t)Elem<DT>::from_f32(o[0]) | ((uint32_t)Elem<DT>::from_f32(o[1]) << 16);
+    v.y = (uint32_t)Elem<DT>::from_f32(o[2]) | ((uint32_t)Elem<DT>::from_f32(o[3]) << 16);
+    return v;
+  }
+};
+template <> struct Vec4<kBF16> : Vec4Half<kBF16> {};
+template <> struct Vec4<kF16> : Vec4Half<kF16> {};
+
+__device__ __forceinline__ double wave_sum(double v) {
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// Find the matrix owning block `b` (block_begin is ascending).
+template <typename M>
+__device__ __forceinline__ int find_mat(const M *mats, int n, int b) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (mats[mid].block_begin <= b) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// ------------------------------------------------------------------ E1
+template <int GDT, bool MONA>
+__device__ __forceinline__ void e1_elem(float g, float &m, float &a, float prev, const E1Args &args) {
+  if (MONA) {
+    const float d = args.first_step ? 0.0f : (g - prev);
+    a = args.beta_a * a + (1.0f - args.beta_a) * d;
+    g = g + args.alpha * a;
+  }
+  m = args.mu * m + g;
+}
+
+template <int GDT, bool MONA>
+__global__ __launch_bounds__(kE1Threads) void e1_kernel(E1Args args) {
+  typedef typename Elem<GDT>::raw graw;
+  typedef typename Vec4<GDT>::type gvec;
+  const int mi = find_mat(args.mats, args.nmat, (int)blockIdx.x);
+  const E1Mat &mt = args.mats[mi];
+  const int64_t blk = (int64_t)blockIdx.x - mt.block_begin;
+  const int64_t base = blk * kE1BlockElems;
+  const int64_t numel = mt.numel;
+  const graw *grad = (const graw *)mt.grad;
+  graw *prev = (graw *)mt.prev;
+  float *mom = mt.mom;
+  float *acc = mt.accel;
+  const bool vec_ok = ((((uintptr_t)grad) | ((uintptr_t)mom) | ((uintptr_t)acc) | ((uintptr_t)prev)) & 15) == 0 &&
+                      (sizeof(graw) == 4 || ((((uintptr_t)grad) | ((uintptr_t)prev)) & 7) == 0);
+  float sq = 0.0f;
+#pragma unroll
+  for (int it = 0; it < kE1ElemsPerThread / 4; ++it) {
+    const int64_t e = base + ((int64_t)it * kE1Threads + threadIdx.x) * 4;
+    if (e >= numel) break;
+    if (vec_ok && e + 4 <= numel) {
+      float g[4], m[4], a[4] = {0, 0, 0, 0}, p[4] = {0, 0, 0, 0};
+      const gvec gv = *(const gvec *)(grad + e);
+      Vec4<GDT>::unpack(gv, g);
+      const float4 mv = *(const float4 *)(mom + e);
+      m[0] = mv.x; m[1] = mv.y; m[2] = mv.z; m[3] = mv.w;
+      if (MONA) {
+        const float4 av = *(const float4 *)(acc + e);
+        a[0] = av.x; a[1] = av.y; a[2] = av.z; a[3] = av.w;
+        if (!args.first_step) Vec4<GDT>::unpack(*(const gvec *)(prev + e), p);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        e1_elem<GDT, MONA>(g[q], m[q], a[q], p[q], args);
+        sq += m[q] * m[q];
+      }
+      *(float4 *)(mom + e) = make_float4(m[0], m[1], m[2], m[3]);
+      if (MONA) {
+        *(float4 *)(acc + e) = make_float4(a[0], a[1], a[2], a[3]);
+        *(gvec *)(prev + e) = gv;  // exact copy of the stored gradient
+      }
+    } else {
+      const int64_t end = (e + 4 < numel) ? e + 4 : numel;
+      for (int64_t j = e; j < end; ++j) {
+        const graw graw_v = grad[j];
+        const float g = Elem<GDT>::to_f32(graw_v);
+        float m = mom[j];
+        float a = 0.0f, p = 0.0f;
+        if (MONA) {
+          a = acc[j];
+          if (!args.first_step) p = Elem<GDT>::to_f32(prev[j]);
+        }
+        e1_elem<GDT, MONA>(g, m, a, p, args);
+        sq += m * m;
+        mom[j] = m;
+        if (MONA) {
+          acc[j] = a;
+          prev[j] = graw_v;
+        }
+      }
+    }
+  }
+  // fixed-order block reduction: lanes (fp64 butterfly), then waves in order
+  __shared__ double wsum[kE1Threads / 64];
+  double s = wave_sum((double)sq);
+  if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double t = 0.0;
+#pragma unroll
+    for (int w = 0; w < kE1Threads / 64; ++w) t += wsum[w];
+    args.partials[mt.partial_off + blk] = t;
+  }
+}
+
+// ------------------------------------------------------------------ norm
+__global__ __launch_bounds__(256) void norm_kernel(NormArgs args) {
+  const NormMat &mt = args.mats[blockIdx.x];
+  double s = 0.0;
+  for (int i = threadIdx.x; i < mt.nparts; i += 256) s += args.partials[mt.partial_off + i];
+  __shared__ double wsum[4];
+  s = wave_sum(s);
+  if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const double t = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+    // zero matrix => X0 = 0 (no epsilon); Inf/NaN propagate through the product
+    const double scale = (t == 0.0) ? 0.0 : (double)args.inv_sqrt_d / sqrt(t);
+    args.scales[mt.scale_idx] = (float)(scale * (double)args.store_scale);
+  }
+}
+
+// ------------------------------------------------------------------ E2
+template <int NDT>
+__global__ __launch_bounds__(256) void e2_kernel(E2Args args) {
+  typedef typename Elem<NDT>::raw nraw;
+  typedef typename Vec4<NDT>::type nvec;
+  __shared__ float tile[kE2Tile][kE2Tile + 1];
+  // matrices are found by tile_begin (stored in the block_begin slot's place)
+  int lo = 0, hi = args.nmat - 1;
+  const int b = blockIdx.x;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (args.mats[mid].tile_begin <= b) lo = mid; else hi = mid - 1;
+  }
+  const E2Mat &mt = args.mats[lo];
+  const int t = b - mt.tile_begin;
+  const int tr = t / mt.tiles_c, tc = t - tr * mt.tiles_c;
+  const int r0 = tr * kE2Tile, c0 = tc * kE2Tile;
+  const float scale = args.scales[mt.scale_idx];
+  const int cg = (threadIdx.x & 15) * 4;   // column group within the tile
+  const int rr = threadIdx.x >> 4;         // 0..15
+  nraw *nat = (nraw *)mt.nat;
+  nraw *trn = (nraw *)mt.trn;
+  const bool vec_ok = ((mt.cols & 3) == 0) && ((((uintptr_t)mt.mom) & 15) == 0);
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int r = r0 + rr + 16 * it;
+    const int c = c0 + cg;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    if (r < mt.rows) {
+      const float *src = mt.mom + (int64_t)r * mt.cols;
+      if (vec_ok && c + 4 <= mt.cols) {
+        const float4 x = *(const float4 *)(src + c);
+        v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (c + q < mt.cols) v[q] = src[c + q];
+      }
+    }
+    float o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      // round once to the storage dtype; the LDS copy holds the rounded value
+      o[q] = Elem<NDT>::to_f32(Elem<NDT>::from_f32(v[q] * scale));
+      tile[rr + 16 * it][cg + q] = o[q];
+    }
+    *(nvec *)(nat + (int64_t)r * mt.ld_nat + c) = Vec4<NDT>::pack(o);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int tcol = rr + 16 * it;       // column of M = row of the transposed buffer
+    float o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = tile[cg + q][tcol];
+    *(nvec *)(trn + (int64_t)(c0 + tcol) * mt.ld_trn + r0 + cg) = Vec4<NDT>::pack(o);
+  }
+}
+
+// ------------------------------------------------------------------ E3
+template <int NDT>
+__global__ __launch_bounds__(kE3Threads) void e3_kernel(E3Args args) {
+  typedef typename Elem<NDT>::raw nraw;
+  typedef typename Vec4<NDT>::type nvec;
+  const int mi = find_mat(args.mats, args.nmat, (int)blockIdx.x);
+  const E3Mat &mt = args.mats[mi];
+  const int64_t base = ((int64_t)blockIdx.x - mt.block_begin) * kE3BlockElems;
+  const nraw *o = (const nraw *)mt.o;
+  const float lr = args.lr, wd = args.wd, gamma = mt.gamma, inv = mt.inv_o_scale;
+#pragma unroll
+  for (int it = 0; it < kE3BlockElems / (kE3Threads * 4); ++it) {
+    const int64_t e = base + ((int64_t)it * kE3Threads + threadIdx.x) * 4;
+    if (e >= mt.numel) break;
+    if (mt.vec_ok && e + 4 <= mt.numel) {
+      const int64_t i = e / mt.cols;
+      const int64_t j = e - i * mt.cols;
+      float ov[4];
+      Vec4<NDT>::unpack(*(const nvec *)(o + i * mt.ld_o + j), ov);
+      float4 w = *(const float4 *)(mt.weight + e);
+      float wv[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        ov[q] *= inv;
+        wv[q] = wv[q] - lr * (gamma * ov[q] + wd * wv[q]);
+      }
+      *(float4 *)(mt.weight + e) = make_float4(wv[0], wv[1], wv[2], wv[3]);
+      if (mt.ortho_out) *(float4 *)(mt.ortho_out + e) = make_float4(ov[0], ov[1], ov[2], ov[3]);
+    } else {
+      const int64_t end = (e + 4 < mt.numel) ? e + 4 : mt.numel;
+      for (int64_t x = e; x < end; ++x) {
+        const int64_t i = x / mt.cols;
+        const int64_t j = x - i * mt.cols;
+        const float ov = Elem<NDT>::to_f32(o[i * mt.ld_o + j]) * inv;
+        const float w = mt.weight[x];
+        mt.weight[x] = w - lr * (gamma * ov + wd * w);
+        if (mt.ortho_out) mt.ortho_out[x] = ov;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_e1(const E1Args &args, int blocks, hipStream_t s) {
+  const bool mona = args.mats[0].accel != nullptr;
+  switch (args.grad_dtype * 2 + (mona ? 1 : 0)) {
+    case kF32 * 2 + 0: hipLaunchKernelGGL((e1_kernel<kF32, false>), dim3(blocks), dim3(kE1Threads), 0, s, args); break;
+    case kF32 * 2 + 1: hipLaunchKernelGGL((e1_kernel<kF32, true>), dim3(blocks), dim3(kE1Threads), 0, s, args); break;
+    case kF16 * 2 + 0: hipLaunchKernelGGL((e1_kernel<kF16, false>), dim3(blocks), dim3(kE1Threads), 0, s, args); break;
+    case kF16 * 2 + 1: hipLaunchKernelGGL((e1_kernel<kF16, true>), dim3(blocks), dim3(kE1Threads), 0, s, args); break;
+    case kBF16 * 2 + 0: hipLaunchKernelGGL((e1_kernel<kBF16, false>), dim3(blocks), dim3(kE1Threads), 0, s, args); break;
+    case kBF16 * 2 + 1: hipLaunchKernelGGL((e1_kernel<kBF16, true>), dim3(blocks), dim3(kE1Threads), 0, s, args); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_norm(const NormArgs &args, hipStream_t s) {
+  hipLaunchKernelGGL(norm_kernel, dim3(args.nmat), dim3(256), 0, s, args);
+  return hipGetLastError();
+}
+
+hipError_t launch_e2(const E2Args &args, int blocks, hipStream_t s) {
+  switch (args.ns_dtype) {
+    case kF32: hipLaunchKernelGGL(e2_kernel<kF32>, dim3(blocks), dim3(256), 0, s, args); break;
+    case kF16: hipLaunchKernelGGL(e2_kernel<kF16>, dim3(blocks), dim3(256), 0, s, args); break;
+    case kBF16: hipLaunchKernelGGL(e2_kernel<kBF16>, dim3(blocks), dim3(256), 0, s, args); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_e3(const E3Args &args, int blocks, hipStream_t s) {
+  switch (args.ns_dtype) {
+    case kF32: hipLaunchKernelGGL(e3_kernel<kF32>, dim3(blocks), dim3(kE3Threads), 0, s, args); break;
+    case kF16: hipLaunchKernelGGL(e3_kernel<kF16>, dim3(blocks), dim3(kE3Threads), 0, s, args); break;
+    case kBF16: hipLaunchKernelGGL(e3_kernel<kBF16>, dim3(blocks), dim3(kE3Threads), 0, s, args); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace muon

@@ -1,0 +1,820 @@
+// Host side of libmuon: argument checks, workspace layout and the stage
+// schedules of the Muon / MONA step (C ABI declared in include/muon.h).
+//
+// Order of a step (MONA summary, section 2 "Kernalgoritme"; the acceleration
+// comes before orthogonalisation per "Ontwerprichtlijnen"):
+//   E1    MONA + momentum + Frobenius partials          (HBM-bound)
+//   norm  per-matrix 1 / (sqrt(d) ||M||_F)
+//   E2    X0 in the Newton-Schulz dtype, both orientations (HBM-bound)
+//   NS    direct:  per step  A = X X^T (half) ; B = b A + c A^2 (half) ;
+//                            X^T <- a X^T + X^T B      (writes X and X^T)
+//         Gram:    R = X X^T ; per step P = a I + b R + c R^2 ; Q <- Q P ;
+//                  R <- (R P) P ; restarts re-form Y <- Y Q / sqrt(d) and R ;
+//                  O = Y Q        (Gram Newton-Schulz post, main body)
+//   E3    W <- W - lr (gamma O + lambda W)               (HBM-bound)
+//
+// Matrices are grouped into classes of equal (short side s, long side l);
+// wide and tall matrices of the same (s, l) share a class because the
+// iteration works on both orientations of the iterate.  Every NS launch
+// covers all classes that use the same tile size.
+#include "muon.h"
+#include "muon_kernels.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+using namespace muon;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+muon_status fail(muon_status s, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+constexpr int kMaxSteps = 64;
+constexpr int64_t kMaxDim = int64_t(1) << 20;
+constexpr int64_t kMaxNumel = (int64_t(1) << 31) - 1;
+
+int elem_size(int dt) { return dt == kF32 ? 4 : 2; }
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct Settings {
+  int grad_dtype = kF32;
+  int ns_dtype = kF32;
+  std::vector<double> coeffs;   // 3 * K
+  double divisor = 1.0;
+  int restart_every = 0;
+  int64_t step = 0;
+};
+
+struct ClassInfo {
+  int64_t s = 0, l = 0;
+  int tile = 64;
+  int64_t Sp = 0, Lp = 0;
+  std::vector<int> members;
+  size_t X[2] = {0, 0}, XT[2] = {0, 0};
+  size_t sq[5] = {0, 0, 0, 0, 0};   // direct: A, B ; gram: R, T, P, Q, Qspare
+};
+
+struct Plan {
+  int n = 0;
+  int K = 0;
+  muon_variant variant = MUON_NS_DIRECT;
+  Settings set;
+  std::vector<ClassInfo> classes;
+  std::vector<int> cls_of, idx_in_cls;
+  std::vector<int> e1_blocks, partial_off;
+  size_t off_partials = 0, off_scales = 0, total = 0;
+};
+
+bool is_finite(double v) { return std::isfinite(v); }
+
+muon_status read_options(const muon_options *o, int ns_steps, Settings &s) {
+  s = Settings();
+  muon_options d;
+  muon_options_init(&d);
+  if (!o) o = &d;
+  if (o->grad_dtype != MUON_F32 && o->grad_dtype != MUON_F16 && o->grad_dtype != MUON_BF16)
+    return fail(MUON_ERR_UNSUPPORTED, "unknown grad_dtype %d", (int)o->grad_dtype);
+  if (o->ns_dtype != MUON_F32 && o->ns_dtype != MUON_F16 && o->ns_dtype != MUON_BF16)
+    return fail(MUON_ERR_UNSUPPORTED, "unknown ns_dtype %d", (int)o->ns_dtype);
+  // muon_dtype values equal the internal DType values.
+  s.grad_dtype = (int)o->grad_dtype;
+  s.ns_dtype = (int)o->ns_dtype;
+  if (!is_finite(o->divisor) || o->divisor < 1.0f) return fail(MUON_ERR_INVALID_ARG, "divisor must be finite and >= 1 (got %g)", (double)o->divisor);
+  if (o->restart_every < 0) return fail(MUON_ERR_INVALID_ARG, "restart_every must be >= 0");
+  if (o->step < 0) return fail(MUON_ERR_INVALID_ARG, "step must be >= 0");
+  s.divisor = o->divisor;
+  s.restart_every = o->restart_every;
+  s.step = o->step;
+  s.coeffs.resize(3 * (size_t)ns_steps);
+  for (int k = 0; k < ns_steps; ++k) {
+    for (int j = 0; j < 3; ++j) {
+      double v;
+      if (o->coeffs) {
+        v = o->coeffs[3 * k + j];
+        if (!is_finite(v)) return fail(MUON_ERR_INVALID_ARG, "coeffs[%d][%d] is not finite", k, j);
+      } else {
+        static const double q[3] = {15.0 / 8.0, -5.0 / 4.0, 3.0 / 8.0};
+        v = q[j];
+      }
+      s.coeffs[3 * k + j] = v;
+    }
+  }
+  return MUON_OK;
+}
+
+struct Range {
+  uintptr_t lo, hi;
+  int param;
+  const char *what;
+};
+
+muon_status check_params(const muon_param *p, int n, const Settings &set) {
+  std::vector<Range> ranges;
+  ranges.reserve((size_t)n * 6);
+  for (int i = 0; i < n; ++i) {
+    const muon_param &q = p[i];
+    if (!q.weight || !q.grad || !q.momentum) return fail(MUON_ERR_INVALID_ARG, "param %d: weight, grad and momentum must be non-NULL", i);
+    if ((q.accel == nullptr) != (q.prev_grad == nullptr))
+      return fail(MUON_ERR_INVALID_ARG, "param %d: accel and prev_grad must both be given or both be NULL", i);
+    if (q.rows < 1 || q.cols < 1) return fail(MUON_ERR_INVALID_ARG, "param %d: rows and cols must be >= 1", i);
+    if (q.rows > kMaxDim || q.cols > kMaxDim || q.rows * q.cols > kMaxNumel)
+      return fail(MUON_ERR_UNSUPPORTED, "param %d: %lld x %lld exceeds the supported size", i, (long long)q.rows, (long long)q.cols);
+    if (!is_finite(q.gamma)) return fail(MUON_ERR_INVALID_ARG, "param %d: gamma is not finite", i);
+    const uint64_t ne = (uint64_t)(q.rows * q.cols);
+    const uint64_t gb = ne * (uint64_t)elem_size(set.grad_dtype);
+    ranges.push_back({(uintptr_t)q.weight, (uintptr_t)q.weight + ne * 4, i, "weight"});
+    ranges.push_back({(uintptr_t)q.grad, (uintptr_t)q.grad + gb, i, "grad"});
+    ranges.push_back({(uintptr_t)q.momentum, (uintptr_t)q.momentum + ne * 4, i, "momentum"});
+    if (q.accel) {
+      ranges.push_back({(uintptr_t)q.accel, (uintptr_t)q.accel + ne * 4, i, "accel"});
+      ranges.push_back({(uintptr_t)q.prev_grad, (uintptr_t)q.prev_grad + gb, i, "prev_grad"});
+    }
+    if (q.ortho_out) ranges.push_back({(uintptr_t)q.ortho_out, (uintptr_t)q.ortho_out + ne * 4, i, "ortho_out"});
+  }
+  std::sort(ranges.begin(), ranges.end(), [](const Range &a, const Range &b) { return a.lo < b.lo; });
+  for (size_t i = 1; i < ranges.size(); ++i) {
+    const Range &a = ranges[i - 1], &b = ranges[i];
+    // two read-only grads may not overlap either: every buffer is distinct
+    if (b.lo < a.hi)
+      return fail(MUON_ERR_INVALID_ARG, "buffers overlap: param %d %s and param %d %s", a.param, a.what, b.param, b.what);
+  }
+  return MUON_OK;
+}
+
+muon_status build_plan(const muon_param *p, int n, int ns_steps, muon_variant v, const muon_options *o, Plan &plan) {
+  if (n < 0) return fail(MUON_ERR_INVALID_ARG, "n must be >= 0");
+  if (n > 0 && !p) return fail(MUON_ERR_INVALID_ARG, "params is NULL");
+  if (ns_steps < 0 || ns_steps > kMaxSteps) return fail(MUON_ERR_INVALID_ARG, "ns_steps must be in [0, %d]", kMaxSteps);
+  if (v != MUON_NS_DIRECT && v != MUON_NS_GRAM) return fail(MUON_ERR_INVALID_ARG, "unknown variant %d", (int)v);
+  muon_status st = read_options(o, ns_steps, plan.set);
+  if (st != MUON_OK) return st;
+  st = check_params(p, n, plan.set);
+  if (st != MUON_OK) return st;
+  plan.n = n;
+  plan.K = ns_steps;
+  plan.variant = v;
+  plan.cls_of.assign(n, -1);
+  plan.idx_in_cls.assign(n, -1);
+  plan.e1_blocks.assign(n, 0);
+  plan.partial_off.assign(n, 0);
+  int64_t parts = 0;
+  for (int i = 0; i < n; ++i) {
+    const int64_t s = std::min(p[i].rows, p[i].cols), l = std::max(p[i].rows, p[i].cols);
+    int c = -1;
+    for (size_t k = 0; k < plan.classes.size(); ++k)
+      if (plan.classes[k].s == s && plan.classes[k].l == l) c = (int)k;
+    if (c < 0) {
+      ClassInfo ci;
+      ci.s = s;
+      ci.l = l;
+      ci.tile = s <= 256 ? 64 : 128;
+      ci.Sp = round_up(s, ci.tile);
+      ci.Lp = round_up(l, ci.tile);
+      plan.classes.push_back(ci);
+      c = (int)plan.classes.size() - 1;
+    }
+    plan.cls_of[i] = c;
+    plan.idx_in_cls[i] = (int)plan.classes[c].members.size();
+    plan.classes[c].members.push_back(i);
+    const int64_t ne = p[i].rows * p[i].cols;
+    plan.e1_blocks[i] = (int)((ne + kE1BlockElems - 1) / kE1BlockElems);
+    plan.partial_off[i] = (int)parts;
+    parts += plan.e1_blocks[i];
+  }
+  size_t off = 0;
+  plan.off_partials = off;
+  off = align256(off + (size_t)parts * sizeof(double));
+  plan.off_scales = off;
+  off = align256(off + (size_t)std::max(n, 1) * sizeof(float));
+  const size_t es = (size_t)elem_size(plan.set.ns_dtype);
+  for (ClassInfo &c : plan.classes) {
+    const size_t cnt = c.members.size();
+    const size_t rect = (size_t)c.Sp * (size_t)c.Lp * es * cnt;
+    const size_t sqb = (size_t)c.Sp * (size_t)c.Sp * es * cnt;
+    for (int j = 0; j < 2; ++j) {
+      c.X[j] = off; off = align256(off + rect);
+      c.XT[j] = off; off = align256(off + rect);
+    }
+    const int nsq = (v == MUON_NS_DIRECT) ? 2 : 5;
+    for (int j = 0; j < nsq; ++j) { c.sq[j] = off; off = align256(off + sqb); }
+  }
+  plan.total = std::max<size_t>(off, 256);
+  return MUON_OK;
+}
+
+// ---------------------------------------------------------------- scales
+// fp16 buffers are stored multiplied by a power of two chosen from a bound on
+// their entries, so that small entries stay in fp16's normal range; the
+// scaling is exact and undone in the next epilogue.  bf16 and fp32 have
+// fp32's exponent range and use 1.
+struct Scaler {
+  bool active;
+  double pick(double bound) const {
+    if (!active) return 1.0;
+    if (!(bound > 0.0) || !std::isfinite(bound)) return 1.0;
+    int e = (int)std::floor(std::log2(32768.0 / bound));
+    e = std::max(-14, std::min(24, e));
+    return std::ldexp(1.0, e);
+  }
+};
+
+// sup over x in [0, hi] of |f(x)|, f one of: 0 p(x)=a x+b x^3+c x^5,
+// 1 q(x)=a+b x^2+c x^4, 2 h(x)=b x^2+c x^4, 3 x p(x)
+double sup_poly(double a, double b, double c, double hi, int which) {
+  double best = 0.0;
+  const int N = 4096;
+  for (int i = 0; i <= N; ++i) {
+    const double x = hi * (double)i / N, x2 = x * x;
+    double f;
+    switch (which) {
+      case 0: f = x * (a + x2 * (b + c * x2)); break;
+      case 1: f = a + x2 * (b + c * x2); break;
+      case 2: f = x2 * (b + c * x2); break;
+      default: f = x2 * (a + x2 * (b + c * x2)); break;
+    }
+    best = std::max(best, std::fabs(f));
+  }
+  return best * 1.0001;
+}
+
+bool restart_due(int k, int r) { return r > 0 && k > 1 && (k - 1) % r == 0; }
+
+// Optional per-launch HIP-event timing (muon_trace).
+struct Tracer {
+  muon_trace *t;
+  hipStream_t s;
+  template <typename F>
+  hipError_t run(int stage, double work, F &&launch) {
+    const int i = t ? t->count : 0;
+    const bool rec = t && i < t->capacity;
+    if (rec) {
+      hipError_t e = hipEventRecord((hipEvent_t)t->events[2 * i], s);
+      if (e != hipSuccess) return e;
+    }
+    hipError_t e = launch();
+    if (e != hipSuccess) return e;
+    if (rec) {
+      e = hipEventRecord((hipEvent_t)t->events[2 * i + 1], s);
+      if (e != hipSuccess) return e;
+      t->stages[i] = stage;
+      t->work[i] = work;
+    }
+    if (t) t->count++;
+    return hipSuccess;
+  }
+};
+
+// One NS product for every class: built per class, launched grouped by tile.
+// per_flops[c] is the algorithmic FLOP count of one matrix of class c (true,
+// unpadded sizes; a half product counts only its upper triangle).
+struct StageBuilder {
+  const Plan &plan;
+  char *ws;
+  Tracer &tr;
+  std::vector<GemmClass> per_class;
+  std::vector<double> per_flops;
+  explicit StageBuilder(const Plan &p, char *w, Tracer &t) : plan(p), ws(w), tr(t) {
+    per_class.resize(p.classes.size());
+    per_flops.assign(p.classes.size(), 0.0);
+  }
+  hipError_t launch() {
+    for (int tile : {64, 128}) {
+      GemmArgs args;
+      std::memset(&args, 0, sizeof(args));
+      double flops = 0.0;
+      auto go = [&]() -> hipError_t {
+        const GemmArgs a = args;
+        const int dt = plan.set.ns_dtype;
+        return tr.run(MUON_STAGE_GEMM, flops, [&]() { return launch_gemm(a, dt, tile, tr.s); });
+      };
+      for (size_t c = 0; c < per_class.size(); ++c) {
+        if (plan.classes[c].tile != tile) continue;
+        GemmClass g = per_class[c];
+        if (args.nclass == kGemmMaxClasses) {
+          hipError_t e = go();
+          if (e != hipSuccess) return e;
+          std::memset(&args, 0, sizeof(args));
+          flops = 0.0;
+        }
+        g.tile_begin = args.total_tiles;
+        args.cls[args.nclass++] = g;
+        args.total_tiles += g.tiles_per_mat * g.count;
+        flops += per_flops[c] * (double)g.count;
+      }
+      if (args.nclass > 0) {
+        hipError_t e = go();
+        if (e != hipSuccess) return e;
+      }
+    }
+    return hipSuccess;
+  }
+};
+
+// Algorithmic FLOPs: half product of an s x s result over k: s (s + 1) k;
+// full s x l result over s: 2 s^2 l.
+double half_flops(const ClassInfo &c, int64_t k) { return (double)c.s * (double)(c.s + 1) * (double)k; }
+double full_flops(const ClassInfo &c) { return 2.0 * (double)c.s * (double)c.s * (double)c.l; }
+
+// Fill a GemmClass for class c: C (m x n) = alpha * A B^T + beta * Cin + diag I.
+GemmClass make_gemm(const ClassInfo &c, size_t es, char *ws, size_t a, int64_t a_rows, int64_t a_ld,
+                    size_t b, int64_t b_rows, int64_t b_ld, int64_t K, bool half) {
+  GemmClass g;
+  std::memset(&g, 0, sizeof(g));
+  g.a = ws + a;
+  g.b = ws + b;
+  g.sa = a_rows * a_ld;
+  g.sb = b_rows * b_ld;
+  g.lda = (int32_t)a_ld;
+  g.ldb = (int32_t)b_ld;
+  g.K = (int32_t)K;
+  g.tiles_m = (int32_t)(a_rows / c.tile);
+  g.tiles_n = (int32_t)(b_rows / c.tile);
+  g.half = half ? 1 : 0;
+  g.tiles_per_mat = half ? g.tiles_m * (g.tiles_m + 1) / 2 : g.tiles_m * g.tiles_n;
+  g.count = (int32_t)c.members.size();
+  g.diag_limit = (int32_t)c.s;
+  g.alpha = 1.0f;
+  (void)es;
+  return g;
+}
+
+void set_out(GemmClass &g, char *ws, size_t cbuf, int64_t c_rows, int64_t c_ld, bool has_c) {
+  if (has_c) {
+    g.c = ws + cbuf;
+    g.sc = c_rows * c_ld;
+    g.ldc = (int32_t)c_ld;
+  }
+}
+void set_out2(GemmClass &g, char *ws, size_t cbuf, int64_t c_rows, int64_t c_ld) {
+  g.c2 = ws + cbuf;
+  g.sc2 = c_rows * c_ld;
+  g.ldc2 = (int32_t)c_ld;
+}
+void set_in(GemmClass &g, char *ws, size_t cbuf, int64_t c_rows, int64_t c_ld) {
+  g.cin = ws + cbuf;
+  g.scin = c_rows * c_ld;
+  g.ldcin = (int32_t)c_ld;
+}
+
+#define HIP_TRY(expr)                                                                      \
+  do {                                                                                     \
+    hipError_t e_ = (expr);                                                                \
+    if (e_ != hipSuccess) return fail(MUON_ERR_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+// Output of the NS schedule: which buffer holds O and its storage scale.
+struct NsResult {
+  int cur;          // index into X / XT ping-pong
+  double scale;     // storage scale of O
+};
+
+muon_status run_direct(const Plan &plan, char *ws, Tracer &st, double sx0, NsResult &res) {
+  const size_t es = (size_t)elem_size(plan.set.ns_dtype);
+  const Scaler S{plan.set.ns_dtype == kF16};
+  const double d = plan.set.divisor;
+  double sigma = 1.0 / std::sqrt(d);
+  double sX = sx0;
+  int cur = 0;
+  for (int k = 1; k <= plan.K; ++k) {
+    const double a = plan.set.coeffs[3 * (k - 1)], b = plan.set.coeffs[3 * (k - 1) + 1], c = plan.set.coeffs[3 * (k - 1) + 2];
+    const double rs = restart_due(k, plan.set.restart_every) ? 1.0 / std::sqrt(d) : 1.0;
+    sigma *= rs;
+    const bool cubic = (c == 0.0);
+    const double sA = S.pick(sigma * sigma);
+    const double sB = S.pick(sup_poly(0.0, b, c, sigma, 2));
+    // A = X X^T (or B = b X X^T directly when c == 0)
+    {
+      StageBuilder sb(plan, ws, st);
+      for (size_t ci = 0; ci < plan.classes.size(); ++ci) {
+        const ClassInfo &cl = plan.classes[ci];
+        GemmClass g = make_gemm(cl, es, ws, cl.X[cur], cl.Sp, cl.Lp, cl.X[cur], cl.Sp, cl.Lp, cl.Lp, true);
+        if (cubic) {
+          set_out(g, ws, cl.sq[1], cl.Sp, cl.Sp, true);
+          g.alpha = (float)(sB * b * rs * rs / (sX * sX));
+        } else {
+          set_out(g, ws, cl.sq[0], cl.Sp, cl.Sp, true);
+          g.alpha = (float)(sA * rs * rs / (sX * sX));
+        }
+        sb.per_class[ci] = g;
+        sb.per_flops[ci] = half_flops(cl, cl.l);
+      }
+      HIP_TRY(sb.launch());
+    }
+    // B = b A + c A^2
+    if (!cubic) {
+      StageBuilder sb(plan, ws, st);
+      for (size_t ci = 0; ci < plan.classes.size(); ++ci) {
+        const ClassInfo &cl = plan.classes[ci];
+        GemmClass g = make_gemm(cl, es, ws, cl.sq[0], cl.Sp, cl.Sp, cl.sq[0], cl.Sp, cl.Sp, cl.Sp, true);
+        set_out(g, ws, cl.sq[1], cl.Sp, cl.Sp, true);
+        set_in(g, ws, cl.sq[0], cl.Sp, cl.Sp);
+        g.alpha = (float)(c * sB / (sA * sA));
+        g.beta = (float)(b * sB / sA);
+        sb.per_class[ci] = g;
+        sb.per_flops[ci] = half_flops(cl, cl.s);
+      }
+      HIP_TRY(sb.launch());
+    }
+    // X^T <- a X^T + X^T B, also written transposed into X
+    const double sigma_new = sup_poly(a, b, c, sigma, 0);
+    const double sXn = S.pick(sigma_new);
+    {
+      StageBuilder sb(plan, ws, st);
+      for (size_t ci = 0; ci < plan.classes.size(); ++ci) {
+        const ClassInfo &cl = plan.classes[ci];
+        GemmClass g = make_gemm(cl, es, ws, cl.XT[cur], cl.Lp, cl.Sp, cl.sq[1], cl.Sp, cl.Sp, cl.Sp, false);
+        set_out(g, ws, cl.XT[1 - cur], cl.Lp, cl.Sp, true);
+        set_out2(g, ws, cl.X[1 - cur], cl.Sp, cl.Lp);
+        set_in(g, ws, cl.XT[cur], cl.Lp, cl.Sp);
+        g.alpha = (float)(sXn * rs / (sX * sB));
+        g.beta = (float)(a * rs * sXn / sX);
+        sb.per_class[ci] = g;
+        sb.per_flops[ci] = full_flops(cl);
+      }
+      HIP_TRY(sb.launch());
+    }
+    cur = 1 - cur;
+    sigma = sigma_new;
+    sX = sXn;
+  }
+  res.cur = cur;
+  res.scale = sX;
+  return MUON_OK;
+}
+
+muon_status run_gram(const Plan &plan, char *ws, Tracer &st, double sx0, NsResult &res) {
+  const size_t es = (size_t)elem_size(plan.set.ns_dtype);
+  const Scaler S{plan.set.ns_dtype == kF16};
+  const double d = plan.set.divisor;
+  const int r = plan.set.restart_every;
+  double sigma = 1.0 / std::sqrt(d);
+  double sY = sx0;
+  int cur = 0;
+  // square-buffer roles (indices into ClassInfo::sq), rotated on the host
+  const int iR = 0, iT = 1;
+  int iP = 2, iQ = 3, iQs = 4;
+  double sR = 1.0, sQ = 1.0, qbound = 1.0;
+  bool q_is_identity = true;
+
+  auto form_gram = [&]() -> muon_status {
+    sR = S.pick(sigma * sigma);
+    StageBuilder sb(plan, ws, st);
+    for (size_t ci = 0; ci < plan.classes.size(); ++ci) {
+      const ClassInfo &cl = plan.classes[ci];
+      GemmClass g = make_gemm(cl, es, ws, cl.X[cur], cl.Sp, cl.Lp, cl.X[cur], cl.Sp, cl.Lp, cl.Lp, true);
+      set_out(g, ws, cl.sq[iR], cl.Sp, cl.Sp, true);
+      g.alpha = (float)(sR / (sY * sY));
+      sb.per_class[ci] = g;
+      sb.per_flops[ci] = half_flops(cl, cl.l);
+    }
+    HIP_TRY(sb.launch());
+    return MUON_OK;
+  };
+  // Y_new = alpha * Y Q, written as Y (tall) and X = Y^T (wide)
+  auto apply_q = [&](double extra, double out_scale) -> muon_status {
+    StageBuilder sb(plan, ws, st);
+    for (size_t ci = 0; ci < plan.classes.size(); ++ci) {
+      const ClassInfo &cl = plan.classes[ci];
+      GemmClass g = make_gemm(cl, es, ws, cl.XT[cur], cl.Lp, cl.Sp, cl.sq[iQ], cl.Sp, cl.Sp, cl.Sp, false);
+      set_out(g, ws, cl.XT[1 - cur], cl.Lp, cl.Sp, true);
+      set_out2(g, ws, cl.X[1 - cur], cl.Sp, cl.Lp);
+      g.alpha = (float)(extra * out_scale / (sY * sQ));
+      sb.per_class[ci] = g;
+      sb.per_flops[ci] = full_flops(cl);
+    }
+    HIP_TRY(sb.launch());
+    return MUON_OK;
+  };
+  // C = alpha * L Rt^T for square s x s operands (half product)
+  auto square_product = [&](int il, int ir, int iout, double alpha) -> muon_status {
+    StageBuilder sb(plan, ws, st);
+    for (size_t ci = 0; ci < plan.classes.size(); ++ci) {
+      const ClassInfo &cl = plan.classes[ci];
+      GemmClass g = make_gemm(cl, es, ws, cl.sq[il], cl.Sp, cl.Sp, cl.sq[ir], cl.Sp, cl.Sp, cl.Sp, true);
+      set_out(g, ws, cl.sq[iout], cl.Sp, cl.Sp, true);
+      g.alpha = (float)alpha;
+      sb.per_class[ci] = g;
+      sb.per_flops[ci] = half_flops(cl, cl.s);
+    }
+    HIP_TRY(sb.launch());
+    return MUON_OK;
+  };
+
+  muon_status stt = form_gram();
+  if (stt != MUON_OK) return stt;
+  for (int k = 1; k <= plan.K; ++k) {
+    const double a = plan.set.coeffs[3 * (k - 1)], b = plan.set.coeffs[3 * (k - 1) + 1], c = plan.set.coeffs[3 * (k - 1) + 2];
+    if (restart_due(k, r)) {
+      const double sigma_new = sigma / std::sqrt(d);
+      const double sYn = S.pick(sigma_new);
+      stt = apply_q(1.0 / std::sqrt(d), sYn);
+      if (stt != MUON_OK) return stt;
+      cur = 1 - cur;
+      sigma = sigma_new;
+      sY = sYn;
+      stt = form_gram();
+      if (stt != MUON_OK) return stt;
+      q_is_identity = true;
+      qbound = 1.0;
+    }
+    // P = a I + b R + c R^2   (K = 0 product when c == 0: epilogue only)
+    const double pbound = sup_poly(a, b, c, sigma, 1);
+    const double sP = S.pick(pbound);
+    {
+      StageBuilder sb(plan, ws, st);
+      for (size_t ci = 0; ci < plan.classes.size(); ++ci) {
+        const ClassInfo &cl = plan.classes[ci];
+        GemmClass g = make_gemm(cl, es, ws, cl.sq[iR], cl.Sp, cl.Sp, cl.sq[iR], cl.Sp, cl.Sp, c != 0.0 ? cl.Sp : 0, true);
+        set_out(g, ws, cl.sq[iP], cl.Sp, cl.Sp, true);
+        set_in(g, ws, cl.sq[iR], cl.Sp, cl.Sp);
+        g.alpha = (float)(c * sP / (sR * sR));
+        g.beta = (float)(b * sP / sR);
+        g.diag = (float)(a * sP);
+        sb.per_class[ci] = g;
+        sb.per_flops[ci] = c != 0.0 ? half_flops(cl, cl.s) : 0.0;
+      }
+      HIP_TRY(sb.launch());
+    }
+    // Q <- Q P.  P's buffer stays valid for the R update below; when Q was
+    // the identity, P's buffer becomes Q and the old Q buffer takes the next P.
+    const int pb = iP;
+    if (q_is_identity) {
+      std::swap(iQ, iP);
+      sQ = sP;
+      qbound = pbound;
+      q_is_identity = false;
+    } else {
+      qbound *= pbound;
+      const double sQn = S.pick(qbound);
+      stt = square_product(iQ, pb, iQs, sQn / (sQ * sP));
+      if (stt != MUON_OK) return stt;
+      std::swap(iQ, iQs);
+      sQ = sQn;
+    }
+    const double sigma_new = sup_poly(a, b, c, sigma, 0);
+    // R <- (R P) P, unless this is the last step before a restart or the end
+    const bool need_r = k < plan.K && !restart_due(k + 1, r);
+    if (need_r) {
+      const double sT = S.pick(sup_poly(a, b, c, sigma, 3));
+      stt = square_product(iR, pb, iT, sT / (sR * sP));
+      if (stt != MUON_OK) return stt;
+      const double sRn = S.pick(sigma_new * sigma_new);
+      stt = square_product(iT, pb, iR, sRn / (sT * sP));
+      if (stt != MUON_OK) return stt;
+      sR = sRn;
+    }
+    sigma = sigma_new;
+  }
+  if (plan.K > 0) {
+    // O = Y Q in both orientations
+    const double sO = S.pick(sigma);
+    stt = apply_q(1.0, sO);
+    if (stt != MUON_OK) return stt;
+    cur = 1 - cur;
+    sY = sO;
+  }
+  res.cur = cur;
+  res.scale = sY;
+  return MUON_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+void muon_options_init(muon_options *o) {
+  if (!o) return;
+  o->grad_dtype = MUON_F32;
+  o->ns_dtype = MUON_F32;
+  o->coeffs = nullptr;
+  o->divisor = 1.0f;
+  o->restart_every = 0;
+  o->step = 0;
+}
+
+size_t muon_workspace_size(const muon_param *params, int n, int ns_steps, muon_variant variant,
+                           const muon_options *opts) {
+  Plan plan;
+  if (build_plan(params, n, ns_steps, variant, opts, plan) != MUON_OK) return 0;
+  g_last_error.clear();
+  return plan.total;
+}
+
+muon_status muon_step(const muon_param *params, int n, float lr, float mu, float beta_a, float alpha, float lambda,
+                      int ns_steps, muon_variant variant, const muon_options *opts, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+  if (!is_finite(lr) || !is_finite(mu) || !is_finite(beta_a) || !is_finite(alpha) || !is_finite(lambda))
+    return fail(MUON_ERR_INVALID_ARG, "lr, mu, beta_a, alpha and lambda must be finite");
+  Plan plan;
+  muon_status st = build_plan(params, n, ns_steps, variant, opts, plan);
+  if (st != MUON_OK) return st;
+  if (n == 0) {
+    g_last_error.clear();
+    return MUON_OK;
+  }
+  if (!workspace) return fail(MUON_ERR_INVALID_ARG, "workspace is NULL");
+  if (((uintptr_t)workspace & 255) != 0) return fail(MUON_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (workspace_bytes < plan.total)
+    return fail(MUON_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes, plan.total);
+  hipStream_t hs = (hipStream_t)stream;
+  char *ws = (char *)workspace;
+  muon_trace *trace = opts ? opts->trace : nullptr;
+  if (trace) {
+    if (trace->capacity > 0 && (!trace->events || !trace->stages || !trace->work))
+      return fail(MUON_ERR_INVALID_ARG, "trace arrays are NULL");
+    trace->count = 0;
+  }
+  Tracer tr{trace, hs};
+  const Settings &set = plan.set;
+  double *partials = (double *)(ws + plan.off_partials);
+  float *scales = (float *)(ws + plan.off_scales);
+
+  // ---- E1, launched separately for plain and MONA matrices
+  for (int mona = 0; mona < 2; ++mona) {
+    E1Args a;
+    std::memset(&a, 0, sizeof(a));
+    a.grad_dtype = set.grad_dtype;
+    a.first_step = set.step == 0 ? 1 : 0;
+    a.mu = mu;
+    a.beta_a = beta_a;
+    a.alpha = alpha;
+    a.partials = partials;
+    int blocks = 0;
+    double bytes = 0.0;
+    auto flush = [&]() -> muon_status {
+      if (a.nmat == 0) return MUON_OK;
+      HIP_TRY(tr.run(MUON_STAGE_E1, bytes, [&]() { return launch_e1(a, blocks, hs); }));
+      a.nmat = 0;
+      blocks = 0;
+      bytes = 0.0;
+      return MUON_OK;
+    };
+    for (int i = 0; i < n; ++i) {
+      if ((params[i].accel != nullptr) != (mona == 1)) continue;
+      if (a.nmat == kE1MaxMats) {
+        st = flush();
+        if (st != MUON_OK) return st;
+      }
+      E1Mat &m = a.mats[a.nmat++];
+      m.grad = params[i].grad;
+      m.mom = params[i].momentum;
+      m.accel = params[i].accel;
+      m.prev = params[i].prev_grad;
+      m.numel = params[i].rows * params[i].cols;
+      m.block_begin = blocks;
+      m.partial_off = plan.partial_off[i];
+      blocks += plan.e1_blocks[i];
+      {
+        // G read, M read+write; MONA: A read+write, G_prev written (and read after step 0)
+        const double gs = (double)elem_size(set.grad_dtype);
+        double per = gs + 8.0;
+        if (mona) per += 8.0 + gs + (set.step == 0 ? 0.0 : gs);
+        bytes += per * (double)m.numel;
+      }
+    }
+    st = flush();
+    if (st != MUON_OK) return st;
+  }
+
+  // ---- norm finalize
+  const Scaler S{set.ns_dtype == kF16};
+  const double sx0 = S.pick(1.0 / std::sqrt(set.divisor));
+  {
+    NormArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.inv_sqrt_d = (float)(1.0 / std::sqrt(set.divisor));
+    a.store_scale = (float)sx0;
+    a.partials = partials;
+    a.scales = scales;
+    for (int i = 0; i < n; ++i) {
+      if (a.nmat == kNormMaxMats) {
+        HIP_TRY(tr.run(MUON_STAGE_NORM, 0.0, [&]() { return launch_norm(a, hs); }));
+        a.nmat = 0;
+      }
+      NormMat &m = a.mats[a.nmat++];
+      m.partial_off = plan.partial_off[i];
+      m.nparts = plan.e1_blocks[i];
+      m.scale_idx = i;
+    }
+    if (a.nmat) HIP_TRY(tr.run(MUON_STAGE_NORM, 0.0, [&]() { return launch_norm(a, hs); }));
+  }
+
+  // ---- E2: X0 into X[0] / XT[0]
+  const size_t es = (size_t)elem_size(set.ns_dtype);
+  {
+    E2Args a;
+    std::memset(&a, 0, sizeof(a));
+    a.ns_dtype = set.ns_dtype;
+    a.scales = scales;
+    int blocks = 0;
+    double bytes = 0.0;
+    for (int i = 0; i < n; ++i) {
+      if (a.nmat == kE2MaxMats) {
+        HIP_TRY(tr.run(MUON_STAGE_E2, bytes, [&]() { return launch_e2(a, blocks, hs); }));
+        a.nmat = 0;
+        blocks = 0;
+        bytes = 0.0;
+      }
+      const ClassInfo &cl = plan.classes[plan.cls_of[i]];
+      const size_t j = (size_t)plan.idx_in_cls[i];
+      const bool wide = params[i].rows <= params[i].cols;
+      const size_t rect = (size_t)cl.Sp * (size_t)cl.Lp * es;
+      E2Mat &m = a.mats[a.nmat++];
+      m.mom = params[i].momentum;
+      m.nat = ws + (wide ? cl.X[0] : cl.XT[0]) + j * rect;
+      m.trn = ws + (wide ? cl.XT[0] : cl.X[0]) + j * rect;
+      m.rows = (int32_t)params[i].rows;
+      m.cols = (int32_t)params[i].cols;
+      const int64_t prow = wide ? cl.Sp : cl.Lp, pcol = wide ? cl.Lp : cl.Sp;
+      m.ld_nat = (int32_t)pcol;
+      m.ld_trn = (int32_t)prow;
+      m.tiles_c = (int32_t)(pcol / kE2Tile);
+      m.tile_begin = blocks;
+      m.scale_idx = i;
+      blocks += (int)((prow / kE2Tile) * (pcol / kE2Tile));
+      // M read (fp32), X0 written in both orientations
+      bytes += (4.0 + 2.0 * (double)es) * (double)(params[i].rows * params[i].cols);
+    }
+    if (a.nmat) HIP_TRY(tr.run(MUON_STAGE_E2, bytes, [&]() { return launch_e2(a, blocks, hs); }));
+  }
+
+  // ---- Newton-Schulz
+  NsResult res{0, sx0};
+  if (plan.K > 0) {
+    st = (variant == MUON_NS_DIRECT) ? run_direct(plan, ws, tr, sx0, res) : run_gram(plan, ws, tr, sx0, res);
+    if (st != MUON_OK) return st;
+  }
+
+  // ---- E3
+  {
+    E3Args a;
+    std::memset(&a, 0, sizeof(a));
+    a.ns_dtype = set.ns_dtype;
+    a.lr = lr;
+    a.wd = lambda;
+    int blocks = 0;
+    double bytes = 0.0;
+    for (int i = 0; i < n; ++i) {
+      if (a.nmat == kE3MaxMats) {
+        HIP_TRY(tr.run(MUON_STAGE_E3, bytes, [&]() { return launch_e3(a, blocks, hs); }));
+        a.nmat = 0;
+        blocks = 0;
+        bytes = 0.0;
+      }
+      const ClassInfo &cl = plan.classes[plan.cls_of[i]];
+      const size_t j = (size_t)plan.idx_in_cls[i];
+      const bool wide = params[i].rows <= params[i].cols;
+      const size_t rect = (size_t)cl.Sp * (size_t)cl.Lp * es;
+      E3Mat &m = a.mats[a.nmat++];
+      m.weight = params[i].weight;
+      m.o = ws + (wide ? cl.X[res.cur] : cl.XT[res.cur]) + j * rect;
+      m.ortho_out = params[i].ortho_out;
+      m.numel = params[i].rows * params[i].cols;
+      m.cols = (int32_t)params[i].cols;
+      m.ld_o = (int32_t)(wide ? cl.Lp : cl.Sp);
+      m.gamma = params[i].gamma;
+      m.inv_o_scale = (float)(1.0 / res.scale);
+      m.block_begin = blocks;
+      m.vec_ok = ((params[i].cols & 3) == 0) && ((((uintptr_t)params[i].weight) | ((uintptr_t)params[i].ortho_out)) & 15) == 0;
+      blocks += (int)((m.numel + kE3BlockElems - 1) / kE3BlockElems);
+      // W read+write, O read (and the optional fp32 copy written)
+      bytes += (8.0 + (double)es + (m.ortho_out ? 4.0 : 0.0)) * (double)m.numel;
+    }
+    if (a.nmat) HIP_TRY(tr.run(MUON_STAGE_E3, bytes, [&]() { return launch_e3(a, blocks, hs); }));
+  }
+  g_last_error.clear();
+  return MUON_OK;
+}
+
+const char *muon_status_string(muon_status s) {
+  switch (s) {
+    case MUON_OK: return "ok";
+    case MUON_ERR_INVALID_ARG: return "invalid argument";
+    case MUON_ERR_UNSUPPORTED: return "unsupported";
+    case MUON_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MUON_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char *muon_last_error(void) { return g_last_error.c_str(); }
+
+const char *muon_version(void) { return "libmuon 0.1.0 gfx950"; }
+
+}  // extern "C"

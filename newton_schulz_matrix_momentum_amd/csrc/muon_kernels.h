@@ -1,0 +1,145 @@
+// Kernel argument blocks and launchers of libmuon (internal).
+//
+// Every kernel takes its per-matrix table by value as a kernel argument
+// (at most ~3 KB per launch), in the manner of a multi-tensor apply: a step
+// needs no host-to-device table copy, no staging memory and no stream
+// synchronisation, and the whole step can be captured in a HIP graph.  Host
+// code splits long matrix lists into several launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace muon {
+
+enum DType : int32_t { kF32 = 0, kF16 = 1, kBF16 = 2 };
+
+// ------------------------------------------------------------------ E1
+// MONA difference + EMA, momentum, per-block partial sums of M^2.
+constexpr int kE1Threads = 256;
+constexpr int kE1ElemsPerThread = 32;                      // 8 groups of 4
+constexpr int kE1BlockElems = kE1Threads * kE1ElemsPerThread;  // 8192
+constexpr int kE1MaxMats = 48;
+
+struct E1Mat {
+  const void *grad;
+  float *mom;
+  float *accel;     // nullptr => plain Muon
+  void *prev;       // previous gradient (grad dtype); nullptr iff accel == nullptr
+  int64_t numel;
+  int32_t block_begin;   // first block of this matrix within the launch
+  int32_t partial_off;   // index of this matrix's first partial in the workspace
+};
+
+struct E1Args {
+  int32_t nmat;
+  int32_t grad_dtype;
+  int32_t first_step;    // MONA: D = 0
+  int32_t vec_ok_mask_unused;
+  float mu, beta_a, alpha, pad;
+  double *partials;      // workspace
+  E1Mat mats[kE1MaxMats];
+};
+
+// ------------------------------------------------------------------ norm
+constexpr int kNormMaxMats = 128;
+struct NormMat {
+  int32_t partial_off;
+  int32_t nparts;
+  int32_t scale_idx;
+  int32_t pad;
+};
+struct NormArgs {
+  int32_t nmat;
+  float inv_sqrt_d;       // 1/sqrt(divisor)
+  float store_scale;      // power-of-two storage scale of X0
+  int32_t pad;
+  const double *partials;
+  float *scales;
+  NormMat mats[kNormMaxMats];
+};
+
+// ------------------------------------------------------------------ E2
+// X0 = M * scale, rounded to the NS dtype, written in M's orientation
+// ("natural", zero-padded to pr x pc) and transposed (pc x pr).
+constexpr int kE2Tile = 64;
+constexpr int kE2MaxMats = 48;
+struct E2Mat {
+  const float *mom;
+  void *nat;
+  void *trn;
+  int32_t rows, cols;        // true M shape
+  int32_t ld_nat, ld_trn;    // = padded cols, padded rows
+  int32_t tiles_c;           // padded cols / 64
+  int32_t tile_begin;
+  int32_t scale_idx;
+  int32_t pad;
+};
+struct E2Args {
+  int32_t nmat;
+  int32_t ns_dtype;
+  const float *scales;
+  E2Mat mats[kE2MaxMats];
+};
+
+// ------------------------------------------------------------------ E3
+// W = W - lr * (gamma * O + wd * W), O read from the NS workspace.
+constexpr int kE3Threads = 256;
+constexpr int kE3BlockElems = kE3Threads * 16;
+constexpr int kE3MaxMats = 56;
+struct E3Mat {
+  float *weight;
+  const void *o;         // final iterate in W's orientation, leading dim ld_o
+  float *ortho_out;      // optional fp32 copy of O
+  int64_t numel;
+  int32_t cols;
+  int32_t ld_o;
+  float gamma;
+  float inv_o_scale;     // 1 / storage scale of O
+  int32_t block_begin;
+  int32_t vec_ok;        // 16-byte aligned and cols % 4 == 0
+};
+struct E3Args {
+  int32_t nmat;
+  int32_t ns_dtype;
+  float lr, wd;
+  E3Mat mats[kE3MaxMats];
+};
+
+// ------------------------------------------------------------------ GEMM
+// C = alpha * A B^T + beta * Cin + diag * I   (A: m x k, B: n x k, row-major)
+// over a group of same-shaped matrices per class; "half" computes only
+// upper-triangular tiles of a symmetric result and mirrors them.
+constexpr int kGemmMaxClasses = 8;
+struct GemmClass {
+  const void *a;
+  const void *b;
+  void *c;          // may be null (only C2 written)
+  void *c2;         // transposed copy of the result, or null
+  const void *cin;  // epilogue input (same orientation as C), or null
+  int64_t sa, sb, sc, sc2, scin;   // per-matrix element strides
+  int32_t lda, ldb, ldc, ldc2, ldcin;
+  int32_t K;                       // multiple of the k-stage
+  int32_t tiles_m, tiles_n;
+  int32_t tiles_per_mat;
+  int32_t count;
+  int32_t half;
+  int32_t diag_limit;              // diag term only where row == col < diag_limit
+  int32_t tile_begin;
+  float alpha, beta, diag;
+};
+struct GemmArgs {
+  int32_t nclass;
+  int32_t total_tiles;
+  GemmClass cls[kGemmMaxClasses];
+};
+
+// Launchers (return the launch status).
+hipError_t launch_e1(const E1Args &args, int blocks, hipStream_t s);
+hipError_t launch_norm(const NormArgs &args, hipStream_t s);
+hipError_t launch_e2(const E2Args &args, int blocks, hipStream_t s);
+hipError_t launch_e3(const E3Args &args, int blocks, hipStream_t s);
+// tile = 64 or 128 (square block tile); dtype selects the operand type.
+hipError_t launch_gemm(const GemmArgs &args, int dtype, int tile, hipStream_t s);
+
+}  // namespace muon

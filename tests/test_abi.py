@@ -1,0 +1,193 @@
+"""The C-ABI library without a GPU: it loads, exports every entry point that
+include/muon.h declares, its structs match the header byte for byte, and every
+argument error is reported before anything would be enqueued."""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+from conftest import ROOT
+from newton_schulz_matrix_momentum_amd import _lib
+
+HEADER = os.path.join(ROOT, "include", "muon.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(muon_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTS), names
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], stdout=subprocess.PIPE, text=True).stdout
+    exported = set(re.findall(r"\bT (muon_\w+)", out))
+    for n in names:
+        assert n in exported, n
+        assert hasattr(lib, n)
+
+
+def test_struct_layout_matches_header(tmp_path):
+    src = tmp_path / "layout.c"
+    src.write_text(r'''
+#include <stdio.h>
+#include <stddef.h>
+#include "muon.h"
+int main(void) {
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(muon_param), offsetof(muon_param, grad),
+         offsetof(muon_param, prev_grad), offsetof(muon_param, rows), offsetof(muon_param, gamma),
+         offsetof(muon_param, ortho_out), sizeof(muon_options), offsetof(muon_options, coeffs),
+         offsetof(muon_options, divisor), offsetof(muon_options, step), offsetof(muon_options, trace),
+         sizeof(muon_trace), offsetof(muon_trace, capacity));
+  return 0;
+}
+''')
+    exe = tmp_path / "layout"
+    subprocess.check_call(["gcc", "-std=c99", "-Wall", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)])
+    got = [int(v) for v in subprocess.check_output([str(exe)]).split()]
+    P, O = _lib.MuonParam, _lib.MuonOptions
+    want = [ctypes.sizeof(P), P.grad.offset, P.prev_grad.offset, P.rows.offset, P.gamma.offset, P.ortho_out.offset,
+            ctypes.sizeof(O), O.coeffs.offset, O.divisor.offset, O.step.offset, O.trace.offset,
+            ctypes.sizeof(_lib.MuonTrace), _lib.MuonTrace.capacity.offset]
+    assert got == want
+
+
+def test_header_compiles_as_cxx(tmp_path):
+    src = tmp_path / "h.cpp"
+    src.write_text('#include "muon.h"\nint main() { muon_options o; muon_options_init(&o); return 0; }\n')
+    subprocess.check_call(["g++", "-std=c++11", "-fsyntax-only", "-I", os.path.join(ROOT, "include"), str(src)])
+
+
+def test_version_and_strings(lib):
+    assert b"gfx950" in lib.muon_version()
+    for s in range(5):
+        assert lib.muon_status_string(s)
+    assert lib.muon_status_string(99) == b"unknown status"
+
+
+# ---------------------------------------------------------------- validation
+# Fake device addresses: validation fails before any pointer is touched.
+BASE = 1 << 40
+
+
+def param(i, rows=8, cols=16, mona=False, gamma=1.0):
+    p = _lib.MuonParam()
+    step = 1 << 28
+    p.weight = BASE + i * 8 * step
+    p.grad = BASE + (i * 8 + 1) * step
+    p.momentum = BASE + (i * 8 + 2) * step
+    if mona:
+        p.accel = BASE + (i * 8 + 3) * step
+        p.prev_grad = BASE + (i * 8 + 4) * step
+    p.rows, p.cols, p.gamma = rows, cols, gamma
+    return p
+
+
+def arr(*ps):
+    a = (_lib.MuonParam * max(len(ps), 1))()
+    for i, p in enumerate(ps):
+        a[i] = p
+    return a
+
+
+def opts(lib, **kw):
+    o = _lib.MuonOptions()
+    lib.muon_options_init(ctypes.byref(o))
+    for k, v in kw.items():
+        setattr(o, k, v)
+    return o
+
+
+def step(lib, ps, n=None, o=None, ns_steps=5, variant=0, ws=BASE * 4, ws_bytes=1 << 40, lr=0.02, mu=0.95,
+         beta=0.9, alpha=0.5, wd=0.01):
+    n = len(ps) if n is None else n
+    return lib.muon_step(arr(*ps), n, lr, mu, beta, alpha, wd, ns_steps, variant,
+                         ctypes.byref(o) if o is not None else None, ws, ws_bytes, None)
+
+
+def test_empty_call_is_ok(lib):
+    assert lib.muon_step(None, 0, 0.02, 0.95, 0.9, 0.5, 0.01, 5, 0, None, None, 0, None) == _lib.MUON_OK
+
+
+def test_invalid_arguments(lib):
+    E = _lib.MUON_ERR_INVALID_ARG
+    assert step(lib, [param(0)], n=-1) == E
+    assert lib.muon_step(None, 2, 0.02, 0.95, 0.9, 0.5, 0.01, 5, 0, None, BASE, 1 << 30, None) == E
+    p = param(0, rows=0)
+    assert step(lib, [p]) == E
+    p = param(0)
+    p.weight = None
+    assert step(lib, [p]) == E
+    p = param(0, mona=True)
+    p.prev_grad = None
+    assert step(lib, [p]) == E
+    assert "prev_grad" in _lib.last_error()
+    assert step(lib, [param(0)], ns_steps=-1) == E
+    assert step(lib, [param(0)], ns_steps=65) == E
+    assert step(lib, [param(0)], variant=7) == E
+    assert step(lib, [param(0)], o=opts(lib, divisor=0.5)) == E
+    assert step(lib, [param(0)], o=opts(lib, divisor=float("nan"))) == E
+    assert step(lib, [param(0)], o=opts(lib, restart_every=-1)) == E
+    assert step(lib, [param(0)], o=opts(lib, step=-3)) == E
+    assert step(lib, [param(0)], lr=float("inf")) == E
+    assert step(lib, [param(0)], alpha=float("nan")) == E
+    assert step(lib, [param(0, gamma=float("nan"))]) == E
+    bad = (ctypes.c_float * 15)(*([1.0] * 14 + [math.inf]))
+    assert step(lib, [param(0)], o=opts(lib, coeffs=ctypes.cast(bad, ctypes.POINTER(ctypes.c_float)))) == E
+    assert step(lib, [param(0)], ws=None) == E
+    assert step(lib, [param(0)], ws=BASE * 4 + 8) == E     # unaligned workspace
+
+
+def test_unsupported(lib):
+    U = _lib.MUON_ERR_UNSUPPORTED
+    assert step(lib, [param(0)], o=opts(lib, grad_dtype=9)) == U
+    assert step(lib, [param(0)], o=opts(lib, ns_dtype=-1)) == U
+    assert step(lib, [param(0, rows=1 << 21, cols=2)]) == U
+
+
+def test_overlap_rejected(lib):
+    E = _lib.MUON_ERR_INVALID_ARG
+    p = param(0)
+    p.momentum = p.weight + 4 * 8   # inside weight's 8x16 fp32 range
+    assert step(lib, [p]) == E
+    a, b = param(0), param(1)
+    b.grad = a.grad                  # two params sharing a gradient
+    assert step(lib, [a, b]) == E
+    assert "overlap" in _lib.last_error()
+
+
+def test_workspace_size_and_too_small(lib):
+    ps = [param(0, 100, 300), param(1, 300, 100), param(2, 64, 64)]
+    o = opts(lib, ns_dtype=_lib.MUON_BF16)
+    need = lib.muon_workspace_size(arr(*ps), 3, 5, 0, ctypes.byref(o))
+    assert need > 0 and need % 256 == 0
+    # independent of pointer values
+    moved = [param(i + 5, p.rows, p.cols) for i, p in enumerate(ps)]
+    assert lib.muon_workspace_size(arr(*moved), 3, 5, 0, ctypes.byref(o)) == need
+    gram = lib.muon_workspace_size(arr(*ps), 3, 5, 1, ctypes.byref(o))
+    assert gram > need
+    f32 = lib.muon_workspace_size(arr(*ps), 3, 5, 0, None)
+    assert f32 > need
+    assert step(lib, ps, o=o, ws_bytes=need - 1) == _lib.MUON_ERR_WORKSPACE_TOO_SMALL
+    assert lib.muon_workspace_size(arr(param(0, rows=0)), 1, 5, 0, None) == 0
+    assert lib.muon_workspace_size(None, 0, 5, 0, None) > 0
+
+
+def test_product_path_has_no_oracle_import():
+    """The package never imports the oracle or any CPU fallback."""
+    pkg = os.path.join(ROOT, "newton_schulz_matrix_momentum_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith(".py"):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text, f
+                assert "numpy" not in text, f

@@ -1,0 +1,247 @@
+"""HIP path vs the fp64 oracle, element by element, on seeded inputs.
+
+Sizes span several tiles and ragged tails (64-wide tiles for short sides up to
+256, 128-wide above), both orientations, every dtype combination, both
+Newton-Schulz variants, MONA on and off, and two consecutive steps.
+Tolerances (relative Frobenius per matrix, on O and on dW = W_new - W_old):
+1e-5 with fp32 Newton-Schulz operands, 2e-2 with fp16 / bf16 operands and fp32
+accumulation; momentum and acceleration 1e-6; the stored previous gradient is
+bitwise the gradient.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import (compare, draw_grads, make_params, oracle_step, snapshot, to64, rel_fro, TOL_STATE)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import newton_schulz_matrix_momentum_amd as nsm
+    nsm.load()
+    yield
+
+
+def run_case(shapes, *, grad_dtype, ns_dtype, variant="direct", kind="quintic", ns_steps=5, mona=False, steps=1,
+             divisor=1.0, restart_every=0, lr=0.02, mu=0.95, wd=0.01, beta_a=0.9, alpha=0.5, seed=0,
+             grad_kind="gaussian", gammas=None):
+    import newton_schulz_matrix_momentum_amd as nsm
+    label = "%s %s/%s %s mona=%s" % (shapes[:3], grad_dtype, ns_dtype, variant, mona)
+    print("case:", label, flush=True)
+    params = make_params(shapes, grad_dtype, mona, seed, gammas=gammas)
+    for p in params:
+        p["ortho_out"] = torch.full(p["weight"].shape, float("nan"), dtype=torch.float32, device="cuda")
+    coeffs = oracle.coefficient_table(kind, ns_steps)
+    worst = (0.0, 0.0)
+    for step in range(steps):
+        grads = draw_grads(shapes, grad_dtype, seed * 100 + step, grad_kind)
+        for p, g in zip(params, grads):
+            p["grad"] = g
+        before = snapshot(params)
+        ref = oracle_step(before, grads, lr=lr, mu=mu, wd=wd, coeffs=coeffs, variant=variant, divisor=divisor,
+                          restart_every=restart_every, beta_a=beta_a, alpha=alpha, step=step)
+        nsm.muon_step(params, lr=lr, mu=mu, beta_a=beta_a, alpha=alpha, weight_decay=wd, ns_steps=ns_steps,
+                      variant=variant, ns_dtype=ns_dtype, coeffs=coeffs.tolist(), divisor=divisor,
+                      restart_every=restart_every, step=step)
+        torch.cuda.synchronize()
+        w = compare(params, before, ref, grads, ns_dtype, label + " step %d" % step)
+        worst = (max(worst[0], w[0]), max(worst[1], w[1]))
+    print("  worst O err %.3g, worst dW err %.3g" % worst, flush=True)
+    return worst
+
+
+SMALL = [(64, 256), (100, 300), (300, 100), (130, 130), (1, 77), (77, 1), (5, 3)]
+MEDIUM = [(260, 520), (520, 260), (384, 384), (300, 1000)]
+
+
+# ---------------------------------------------------------------- fp32 path
+
+def test_single_64x256_f32_cubic():
+    """One fp32 64x256 matrix, N(0,1) grad, 5 cubic steps, direct."""
+    run_case([(64, 256)], grad_dtype="f32", ns_dtype="f32", kind="cubic")
+
+
+@pytest.mark.parametrize("variant", ["direct", "gram"])
+def test_f32_small_ragged(variant):
+    run_case(SMALL, grad_dtype="f32", ns_dtype="f32", variant=variant, divisor=1.03, restart_every=2)
+
+
+@pytest.mark.parametrize("variant", ["direct", "gram"])
+def test_f32_medium_tiles128(variant):
+    run_case(MEDIUM, grad_dtype="f32", ns_dtype="f32", variant=variant, grad_kind="spectral")
+
+
+# ---------------------------------------------------------------- 16-bit paths
+
+@pytest.mark.parametrize("grad_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("variant", ["direct", "gram"])
+def test_bf16_ns(grad_dtype, variant):
+    run_case(SMALL + MEDIUM, grad_dtype=grad_dtype, ns_dtype="bf16", variant=variant, grad_kind="spectral",
+             divisor=1.03 if variant == "gram" else 1.0, restart_every=3 if variant == "gram" else 0)
+
+
+@pytest.mark.parametrize("variant", ["direct", "gram"])
+def test_f16_ns(variant):
+    run_case(SMALL + MEDIUM, grad_dtype="f16", ns_dtype="f16", variant=variant, grad_kind="spectral",
+             divisor=1.03, restart_every=3)
+
+
+@pytest.mark.parametrize("variant", ["direct", "gram"])
+def test_mona_two_steps(variant):
+    run_case([(200, 330), (330, 200), (256, 256)], grad_dtype="bf16", ns_dtype="bf16", variant=variant, mona=True,
+             steps=2)
+
+
+def test_mona_two_steps_f32():
+    run_case([(96, 160), (160, 96)], grad_dtype="f32", ns_dtype="f32", mona=True, steps=3)
+
+
+def test_cubic_gram_no_square_term():
+    run_case([(100, 260), (260, 100)], grad_dtype="f32", ns_dtype="f32", variant="gram", kind="cubic",
+             divisor=1.02, restart_every=2)
+
+
+def test_zero_steps_returns_x0():
+    run_case([(70, 90), (90, 70)], grad_dtype="f32", ns_dtype="f32", ns_steps=0)
+
+
+def test_per_matrix_gamma():
+    run_case([(64, 64), (64, 128)], grad_dtype="f32", ns_dtype="f32", gammas=[0.5, 2.0])
+
+
+# ---------------------------------------------------------------- special cases
+
+def test_zero_grad_is_pure_decay():
+    import newton_schulz_matrix_momentum_amd as nsm
+    params = make_params([(64, 96)], "f32", False, 3)
+    params[0]["grad"] = torch.zeros(64, 96, device="cuda")
+    params[0]["ortho_out"] = torch.full((64, 96), 7.0, device="cuda")
+    w0 = params[0]["weight"].clone()
+    nsm.muon_step(params, lr=0.1, mu=0.9, weight_decay=0.01, ns_dtype="bf16")
+    torch.cuda.synchronize()
+    assert torch.all(params[0]["ortho_out"] == 0)
+    expect = w0 - 0.1 * (0.01 * w0)
+    assert torch.allclose(params[0]["weight"], expect, rtol=0, atol=1e-7)
+
+
+def test_nan_is_isolated_per_matrix():
+    import newton_schulz_matrix_momentum_amd as nsm
+    shapes = [(64, 64), (64, 64), (128, 64)]
+    params = make_params(shapes, "bf16", False, 4)
+    grads = draw_grads(shapes, "bf16", 5)
+    grads[1][3, 7] = float("nan")
+    for p, g in zip(params, grads):
+        p["grad"] = g
+    before = snapshot(params)
+    nsm.muon_step(params, lr=0.02, mu=0.95, weight_decay=0.01, ns_dtype="bf16")
+    torch.cuda.synchronize()
+    assert torch.isnan(params[1]["weight"]).any()
+    ref = oracle_step([before[0], before[2]], [grads[0], grads[2]], lr=0.02, mu=0.95, wd=0.01,
+                      coeffs=oracle.coefficient_table("quintic", 5), variant="direct", divisor=1.0,
+                      restart_every=0, beta_a=0.0, alpha=0.0, step=0)
+    compare([params[0], params[2]], [before[0], before[2]], ref, [grads[0], grads[2]], "bf16", "nan-isolation")
+
+
+def test_alpha_zero_equals_plain_muon_bitwise():
+    import newton_schulz_matrix_momentum_amd as nsm
+    shapes = [(96, 200), (200, 96)]
+    pa = make_params(shapes, "bf16", True, 6)
+    pp = make_params(shapes, "bf16", False, 6)
+    for step in range(2):
+        grads = draw_grads(shapes, "bf16", 60 + step)
+        for a, p, g in zip(pa, pp, grads):
+            a["grad"] = g
+            p["grad"] = g
+        nsm.muon_step(pa, lr=0.02, mu=0.95, beta_a=0.9, alpha=0.0, weight_decay=0.01, ns_dtype="bf16", step=step)
+        nsm.muon_step(pp, lr=0.02, mu=0.95, weight_decay=0.01, ns_dtype="bf16", step=step)
+    torch.cuda.synchronize()
+    for a, p in zip(pa, pp):
+        assert torch.equal(a["weight"], p["weight"])
+        assert torch.equal(a["momentum"], p["momentum"])
+
+
+def test_deterministic_bitwise():
+    import newton_schulz_matrix_momentum_amd as nsm
+    shapes = [(300, 700), (700, 300), (192, 192)]
+    outs = []
+    for _ in range(2):
+        params = make_params(shapes, "bf16", True, 8)
+        for p, g in zip(params, draw_grads(shapes, "bf16", 9)):
+            p["grad"] = g
+        nsm.muon_step(params, lr=0.02, mu=0.95, beta_a=0.9, alpha=0.5, weight_decay=0.01, ns_dtype="bf16",
+                      variant="gram", divisor=1.03, restart_every=3, step=1)
+        torch.cuda.synchronize()
+        outs.append([p["weight"].clone() for p in params])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+def test_resume_equals_continuous():
+    """Two steps == one step + state copy + one step (bitwise)."""
+    import newton_schulz_matrix_momentum_amd as nsm
+    shapes = [(128, 320), (320, 128)]
+    hp = dict(lr=0.02, mu=0.95, beta_a=0.9, alpha=0.5, weight_decay=0.01, ns_dtype="bf16")
+    grads = [draw_grads(shapes, "bf16", 70 + s) for s in range(2)]
+    cont = make_params(shapes, "bf16", True, 10)
+    for s in range(2):
+        for p, g in zip(cont, grads[s]):
+            p["grad"] = g
+        nsm.muon_step(cont, step=s, **hp)
+    res = make_params(shapes, "bf16", True, 10)
+    for p, g in zip(res, grads[0]):
+        p["grad"] = g
+    nsm.muon_step(res, step=0, **hp)
+    torch.cuda.synchronize()
+    saved = [{k: v.detach().cpu().clone() for k, v in p.items() if isinstance(v, torch.Tensor)} for p in res]
+    restored = [{k: v.cuda() for k, v in s.items()} for s in saved]
+    for p, g in zip(restored, grads[1]):
+        p["grad"] = g
+        p["gamma"] = 1.0
+    nsm.muon_step(restored, step=1, **hp)
+    torch.cuda.synchronize()
+    for a, b in zip(cont, restored):
+        for k in ("weight", "momentum", "accel", "prev_grad"):
+            assert torch.equal(a[k], b[k]), k
+
+
+def test_empty_list_is_noop():
+    import newton_schulz_matrix_momentum_amd as nsm
+    nsm.muon_step([], lr=0.02, mu=0.95)
+
+
+def test_stream_ordering_no_hidden_sync():
+    """The call enqueues on the current stream and returns; results are right
+    after a later synchronize."""
+    import newton_schulz_matrix_momentum_amd as nsm
+    s = torch.cuda.Stream()
+    shapes = [(256, 1024)] * 4
+    params = make_params(shapes, "bf16", False, 11)
+    grads = draw_grads(shapes, "bf16", 12)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        for p, g in zip(params, grads):
+            p["grad"] = g
+        before = snapshot(params)
+        nsm.muon_step(params, lr=0.02, mu=0.95, weight_decay=0.01, ns_dtype="bf16")
+    s.synchronize()
+    ref = oracle_step(before, grads, lr=0.02, mu=0.95, wd=0.01, coeffs=oracle.coefficient_table("quintic", 5),
+                      variant="direct", divisor=1.0, restart_every=0, beta_a=0.0, alpha=0.0, step=0)
+    compare(params, before, ref, grads, "bf16", "side-stream")
+
+
+def test_symmetric_input_gram_f32():
+    """A symmetric gradient through the Gram variant with fp32 operands."""
+    import newton_schulz_matrix_momentum_amd as nsm
+    g = torch.randn(200, 200, dtype=torch.float64, generator=torch.Generator().manual_seed(13))
+    g = (g + g.T).float().cuda()
+    params = make_params([(200, 200)], "f32", False, 14)
+    params[0]["grad"] = g
+    params[0]["ortho_out"] = torch.empty(200, 200, device="cuda")
+    nsm.muon_step(params, lr=0.02, mu=0.95, weight_decay=0.0, ns_dtype="f32", variant="gram")
+    torch.cuda.synchronize()
+    ref = oracle.newton_schulz_gram(oracle.frobenius_normalize(to64(g)), oracle.coefficient_table("quintic", 5))
+    assert rel_fro(to64(params[0]["ortho_out"]), ref) < 1e-5
