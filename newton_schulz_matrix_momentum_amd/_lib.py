@@ -11,7 +11,8 @@ import ctypes
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libmuon.so")
+# LIBMUON_PATH selects another build of the library (e.g. a tuning variant)
+LIB_PATH = os.environ.get("LIBMUON_PATH") or os.path.join(_PKG, "libmuon.so")
 
 MUON_OK = 0
 MUON_ERR_INVALID_ARG = 1

@@ -37,9 +37,9 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found; libmuon needs ROCm's hipcc to build")
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + HIPCC_FLAGS
+def _compile(src: str, verbose: bool, defines=(), tag: str = "") -> str:
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + tag + ".o")
+    cmd = [hipcc()] + HIPCC_FLAGS + ["-D" + d for d in defines]
     if src.endswith(".cpp"):
         cmd += ["-x", "hip"]
     cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
@@ -54,20 +54,24 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source for gfx950 and link libmuon.so; returns its path."""
+def build(verbose: bool = False, defines=(), out: str = LIB) -> str:
+    """Compile every source for gfx950 and link libmuon.so; returns its path.
+
+    ``defines`` (``NAME=VALUE`` strings) and ``out`` build a tuning variant
+    of the library elsewhere; the defaults build the shipped library."""
     os.makedirs(BUILD, exist_ok=True)
+    tag = "" if out == LIB else "_" + str(abs(hash((tuple(defines), out))))
     with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, verbose, defines, tag), SOURCES))
+    tmp = out + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

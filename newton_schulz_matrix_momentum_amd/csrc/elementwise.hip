@@ -101,6 +101,7 @@ template <int GDT, bool MONA>
 __global__ __launch_bounds__(kE1Threads) void e1_kernel(E1Args args) {
   typedef typename Elem<GDT>::raw graw;
   typedef typename Vec4<GDT>::type gvec;
+  constexpr int G = kE1ElemsPerThread / 4;   // groups of 4 elements per thread
   const int mi = find_mat(args.mats, args.nmat, (int)blockIdx.x);
   const E1Mat &mt = args.mats[mi];
   const int64_t blk = (int64_t)blockIdx.x - mt.block_begin;
@@ -112,21 +113,30 @@ __global__ __launch_bounds__(kE1Threads) void e1_kernel(E1Args args) {
   float *acc = mt.accel;
   const bool vec_ok = ((((uintptr_t)grad) | ((uintptr_t)mom) | ((uintptr_t)acc) | ((uintptr_t)prev)) & 15) == 0 &&
                       (sizeof(graw) == 4 || ((((uintptr_t)grad) | ((uintptr_t)prev)) & 7) == 0);
+  const bool full = vec_ok && base + kE1BlockElems <= numel;
   float sq = 0.0f;
+  if (full) {
+    // every load of the thread is issued before the first use
+    gvec gv[G], pv[G];
+    float4 mv[G], av[G];
 #pragma unroll
-  for (int it = 0; it < kE1ElemsPerThread / 4; ++it) {
-    const int64_t e = base + ((int64_t)it * kE1Threads + threadIdx.x) * 4;
-    if (e >= numel) break;
-    if (vec_ok && e + 4 <= numel) {
-      float g[4], m[4], a[4] = {0, 0, 0, 0}, p[4] = {0, 0, 0, 0};
-      const gvec gv = *(const gvec *)(grad + e);
-      Vec4<GDT>::unpack(gv, g);
-      const float4 mv = *(const float4 *)(mom + e);
-      m[0] = mv.x; m[1] = mv.y; m[2] = mv.z; m[3] = mv.w;
+    for (int it = 0; it < G; ++it) {
+      const int64_t e = base + ((int64_t)it * kE1Threads + threadIdx.x) * 4;
+      gv[it] = *(const gvec *)(grad + e);
+      mv[it] = *(const float4 *)(mom + e);
       if (MONA) {
-        const float4 av = *(const float4 *)(acc + e);
-        a[0] = av.x; a[1] = av.y; a[2] = av.z; a[3] = av.w;
-        if (!args.first_step) Vec4<GDT>::unpack(*(const gvec *)(prev + e), p);
+        av[it] = *(const float4 *)(acc + e);
+        if (!args.first_step) pv[it] = *(const gvec *)(prev + e);
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < G; ++it) {
+      const int64_t e = base + ((int64_t)it * kE1Threads + threadIdx.x) * 4;
+      float g[4], m[4] = {mv[it].x, mv[it].y, mv[it].z, mv[it].w}, a[4] = {0, 0, 0, 0}, p[4] = {0, 0, 0, 0};
+      Vec4<GDT>::unpack(gv[it], g);
+      if (MONA) {
+        a[0] = av[it].x; a[1] = av[it].y; a[2] = av[it].z; a[3] = av[it].w;
+        if (!args.first_step) Vec4<GDT>::unpack(pv[it], p);
       }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -136,26 +146,26 @@ __global__ __launch_bounds__(kE1Threads) void e1_kernel(E1Args args) {
       *(float4 *)(mom + e) = make_float4(m[0], m[1], m[2], m[3]);
       if (MONA) {
         *(float4 *)(acc + e) = make_float4(a[0], a[1], a[2], a[3]);
-        *(gvec *)(prev + e) = gv;  // exact copy of the stored gradient
+        *(gvec *)(prev + e) = gv[it];  // exact copy of the stored gradient
       }
-    } else {
-      const int64_t end = (e + 4 < numel) ? e + 4 : numel;
-      for (int64_t j = e; j < end; ++j) {
-        const graw graw_v = grad[j];
-        const float g = Elem<GDT>::to_f32(graw_v);
-        float m = mom[j];
-        float a = 0.0f, p = 0.0f;
-        if (MONA) {
-          a = acc[j];
-          if (!args.first_step) p = Elem<GDT>::to_f32(prev[j]);
-        }
-        e1_elem<GDT, MONA>(g, m, a, p, args);
-        sq += m * m;
-        mom[j] = m;
-        if (MONA) {
-          acc[j] = a;
-          prev[j] = graw_v;
-        }
+    }
+  } else {
+    // ragged tail or unaligned buffers: element by element
+    for (int64_t j = base + threadIdx.x; j < numel && j < base + kE1BlockElems; j += kE1Threads) {
+      const graw graw_v = grad[j];
+      const float g = Elem<GDT>::to_f32(graw_v);
+      float m = mom[j];
+      float a = 0.0f, p = 0.0f;
+      if (MONA) {
+        a = acc[j];
+        if (!args.first_step) p = Elem<GDT>::to_f32(prev[j]);
+      }
+      e1_elem<GDT, MONA>(g, m, a, p, args);
+      sq += m * m;
+      mom[j] = m;
+      if (MONA) {
+        acc[j] = a;
+        prev[j] = graw_v;
       }
     }
   }
@@ -253,22 +263,30 @@ template <int NDT>
 __global__ __launch_bounds__(kE3Threads) void e3_kernel(E3Args args) {
   typedef typename Elem<NDT>::raw nraw;
   typedef typename Vec4<NDT>::type nvec;
+  constexpr int G = kE3BlockElems / (kE3Threads * 4);
   const int mi = find_mat(args.mats, args.nmat, (int)blockIdx.x);
   const E3Mat &mt = args.mats[mi];
   const int64_t base = ((int64_t)blockIdx.x - mt.block_begin) * kE3BlockElems;
   const nraw *o = (const nraw *)mt.o;
   const float lr = args.lr, wd = args.wd, gamma = mt.gamma, inv = mt.inv_o_scale;
+  if (mt.vec_ok && base + kE3BlockElems <= mt.numel) {
+    // every load of the thread is issued before the first use
+    nvec ovv[G];
+    float4 wvv[G];
 #pragma unroll
-  for (int it = 0; it < kE3BlockElems / (kE3Threads * 4); ++it) {
-    const int64_t e = base + ((int64_t)it * kE3Threads + threadIdx.x) * 4;
-    if (e >= mt.numel) break;
-    if (mt.vec_ok && e + 4 <= mt.numel) {
+    for (int it = 0; it < G; ++it) {
+      const int64_t e = base + ((int64_t)it * kE3Threads + threadIdx.x) * 4;
       const int64_t i = e / mt.cols;
       const int64_t j = e - i * mt.cols;
+      ovv[it] = *(const nvec *)(o + i * mt.ld_o + j);
+      wvv[it] = *(const float4 *)(mt.weight + e);
+    }
+#pragma unroll
+    for (int it = 0; it < G; ++it) {
+      const int64_t e = base + ((int64_t)it * kE3Threads + threadIdx.x) * 4;
       float ov[4];
-      Vec4<NDT>::unpack(*(const nvec *)(o + i * mt.ld_o + j), ov);
-      float4 w = *(const float4 *)(mt.weight + e);
-      float wv[4] = {w.x, w.y, w.z, w.w};
+      Vec4<NDT>::unpack(ovv[it], ov);
+      float wv[4] = {wvv[it].x, wvv[it].y, wvv[it].z, wvv[it].w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         ov[q] *= inv;
@@ -276,16 +294,15 @@ __global__ __launch_bounds__(kE3Threads) void e3_kernel(E3Args args) {
       }
       *(float4 *)(mt.weight + e) = make_float4(wv[0], wv[1], wv[2], wv[3]);
       if (mt.ortho_out) *(float4 *)(mt.ortho_out + e) = make_float4(ov[0], ov[1], ov[2], ov[3]);
-    } else {
-      const int64_t end = (e + 4 < mt.numel) ? e + 4 : mt.numel;
-      for (int64_t x = e; x < end; ++x) {
-        const int64_t i = x / mt.cols;
-        const int64_t j = x - i * mt.cols;
-        const float ov = Elem<NDT>::to_f32(o[i * mt.ld_o + j]) * inv;
-        const float w = mt.weight[x];
-        mt.weight[x] = w - lr * (gamma * ov + wd * w);
-        if (mt.ortho_out) mt.ortho_out[x] = ov;
-      }
+    }
+  } else {
+    for (int64_t x = base + threadIdx.x; x < mt.numel && x < base + kE3BlockElems; x += kE3Threads) {
+      const int64_t i = x / mt.cols;
+      const int64_t j = x - i * mt.cols;
+      const float ov = Elem<NDT>::to_f32(o[i * mt.ld_o + j]) * inv;
+      const float w = mt.weight[x];
+      mt.weight[x] = w - lr * (gamma * ov + wd * w);
+      if (mt.ortho_out) mt.ortho_out[x] = ov;
     }
   }
 }

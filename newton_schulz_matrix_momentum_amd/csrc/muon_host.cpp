@@ -83,6 +83,18 @@ struct Plan {
 
 bool is_finite(double v) { return std::isfinite(v); }
 
+// Largest square block tile whose zero padding of the short side stays under
+// 7% (the padded s x s products grow with its square); small sides use 64.
+int pick_tile(int64_t s, int64_t l, int ns_dtype) {
+  (void)l;
+  for (int t : {256, 128}) {
+    if (t == 256 && ns_dtype == kF32) continue;   // the 256 tile is 16-bit only
+    if (s < 2 * t) continue;
+    if ((double)round_up(s, t) <= 1.07 * (double)s) return t;
+  }
+  return 64;
+}
+
 muon_status read_options(const muon_options *o, int ns_steps, Settings &s) {
   s = Settings();
   muon_options d;
@@ -183,7 +195,7 @@ muon_status build_plan(const muon_param *p, int n, int ns_steps, muon_variant v,
       ClassInfo ci;
       ci.s = s;
       ci.l = l;
-      ci.tile = s <= 256 ? 64 : 128;
+      ci.tile = pick_tile(s, l, plan.set.ns_dtype);
       ci.Sp = round_up(s, ci.tile);
       ci.Lp = round_up(l, ci.tile);
       plan.classes.push_back(ci);
@@ -294,7 +306,7 @@ struct StageBuilder {
     per_flops.assign(p.classes.size(), 0.0);
   }
   hipError_t launch() {
-    for (int tile : {64, 128}) {
+    for (int tile : {64, 128, 256}) {
       GemmArgs args;
       std::memset(&args, 0, sizeof(args));
       double flops = 0.0;

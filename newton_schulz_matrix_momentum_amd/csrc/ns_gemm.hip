@@ -33,6 +33,22 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// s_waitcnt vmcnt(n), leaving expcnt and lgkmcnt alone.  gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].  n >= 32 waits
+// for vmcnt(0) (always safe).
+#define MUON_VMCNT(n) (0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
+#define MUON_VMCASE(n) case n: __builtin_amdgcn_s_waitcnt(MUON_VMCNT(n)); break;
+__device__ __forceinline__ void waitcnt_vm(int n) {
+  switch (n) {
+    MUON_VMCASE(1) MUON_VMCASE(2) MUON_VMCASE(3) MUON_VMCASE(4) MUON_VMCASE(5) MUON_VMCASE(6) MUON_VMCASE(7)
+    MUON_VMCASE(8) MUON_VMCASE(9) MUON_VMCASE(10) MUON_VMCASE(11) MUON_VMCASE(12) MUON_VMCASE(13) MUON_VMCASE(14)
+    MUON_VMCASE(15) MUON_VMCASE(16) MUON_VMCASE(17) MUON_VMCASE(18) MUON_VMCASE(19) MUON_VMCASE(20) MUON_VMCASE(21)
+    MUON_VMCASE(22) MUON_VMCASE(23) MUON_VMCASE(24) MUON_VMCASE(25) MUON_VMCASE(26) MUON_VMCASE(27) MUON_VMCASE(28)
+    MUON_VMCASE(29) MUON_VMCASE(30) MUON_VMCASE(31)
+    default: __builtin_amdgcn_s_waitcnt(MUON_VMCNT(0)); break;
+  }
+}
+
 template <typename T> struct Mma;
 template <> struct Mma<__bf16> {
   static __device__ __forceinline__ void run(const u32x4 &a, const u32x4 &b, f32x4 &c) {
@@ -80,6 +96,103 @@ template <typename H> struct Store16 {
 template <> struct Store<__bf16> : Store16<__bf16> {};
 template <> struct Store<_Float16> : Store16<_Float16> {};
 
+
+// Compile-time loop: every index is a template constant, so register arrays
+// indexed by it are never demoted to scratch memory.
+template <int I> struct IntC { static constexpr int value = I; };
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (I < N) {
+    f(IntC<I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+struct TileRef {
+  int ci, mat, tm, tn;
+};
+
+// Locate (class, matrix, tile) of this workgroup; uniform across the block.
+// Workgroups are dealt round-robin to the 8 XCDs (each with its own L2):
+// remap so that each XCD walks a contiguous run of tiles, which share
+// operand panels.
+__device__ __forceinline__ TileRef locate_tile(const GemmArgs &args) {
+  const int nb = (int)gridDim.x;
+  const int b = (int)blockIdx.x;
+  const int per_xcd = nb / 8, rem = nb % 8, xcd = b % 8, slot = b / 8;
+  const int tile = (xcd < rem ? xcd * (per_xcd + 1) : rem * (per_xcd + 1) + (xcd - rem) * per_xcd) + slot;
+  int ci = 0;
+#pragma unroll 1
+  for (int i = 1; i < args.nclass; ++i)
+    if (tile >= args.cls[i].tile_begin) ci = i;
+  const GemmClass &cl = args.cls[ci];
+  const int local = tile - cl.tile_begin;
+  TileRef r;
+  r.ci = ci;
+  r.mat = local / cl.tiles_per_mat;
+  int t = local - r.mat * cl.tiles_per_mat;
+  if (cl.half) {
+    int tm = 0, rowlen = cl.tiles_n;
+#pragma unroll 1
+    while (t >= rowlen) { t -= rowlen; ++tm; --rowlen; }
+    r.tm = tm;
+    r.tn = tm + t;
+  } else {
+    r.tm = t / cl.tiles_n;
+    r.tn = t - r.tm * cl.tiles_n;
+  }
+  return r;
+}
+
+// Epilogue for one wave's FM x FN grid of 16x16 accumulator blocks whose
+// top-left corner is (row0, col0).  MFMA 16x16 output layout: lane holds
+// rows 4*(lane/16) + r, column lane%16, r = 0..3.
+template <typename T, int FM, int FN>
+__device__ __forceinline__ void epilogue(const GemmClass &cl, int mat, bool diag_tile, int row0, int col0,
+                                         const f32x4 (&acc)[FM][FN]) {
+  constexpr int ES = sizeof(T);
+  const int lane = threadIdx.x & 63;
+  const float alpha = cl.alpha, beta = cl.beta, diag = cl.diag;
+  void *C = cl.c ? (void *)((char *)cl.c + (int64_t)mat * cl.sc * ES) : nullptr;
+  void *C2 = cl.c2 ? (void *)((char *)cl.c2 + (int64_t)mat * cl.sc2 * ES) : nullptr;
+  const void *Cin = cl.cin ? (const void *)((const char *)cl.cin + (int64_t)mat * cl.scin * ES) : nullptr;
+  const int row_base = row0 + 4 * (lane >> 4);
+  const int col_base = col0 + (lane & 15);
+  static_for<0, FM>([&](auto ic) {
+    static_for<0, FN>([&](auto jc) {
+      constexpr int i = decltype(ic)::value, j = decltype(jc)::value;
+      const int r0 = row_base + i * 16;
+      const int col = col_base + j * 16;
+      float v[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        v[r] = alpha * acc[i][j][r];
+        if (Cin) v[r] += beta * Store<T>::load(Cin, (int64_t)(r0 + r) * cl.ldcin + col);
+        if (diag != 0.0f && r0 + r == col && col < cl.diag_limit) v[r] += diag;
+      }
+      if (C) {
+        if (!cl.half) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) Store<T>::store(C, (int64_t)(r0 + r) * cl.ldc + col, v[r]);
+        } else if (!diag_tile) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) Store<T>::store(C, (int64_t)(r0 + r) * cl.ldc + col, v[r]);
+          Store<T>::store4(C, (int64_t)col * cl.ldc + r0, v);   // mirror
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            if (col >= r0 + r) {
+              Store<T>::store(C, (int64_t)(r0 + r) * cl.ldc + col, v[r]);
+              Store<T>::store(C, (int64_t)col * cl.ldc + r0 + r, v[r]);
+            }
+          }
+        }
+      }
+      if (C2) Store<T>::store4(C2, (int64_t)col * cl.ldc2 + r0, v);
+    });
+  });
+}
+
 constexpr int kThreads = 256;
 constexpr int kStageBytes = 128;               // k bytes per LDS stage per row
 constexpr int kPitch = kStageBytes + 16;       // padded LDS row
@@ -95,27 +208,9 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(GemmArgs args) {
   static_assert(A_LD >= 1 && B_LD >= 1, "tile too small for the block");
   __shared__ __attribute__((aligned(16))) char lds[2][(BM + BN) * kPitch];
 
-  // ---- locate (class, matrix, tile); uniform across the block
-  const int tile = blockIdx.x;
-  int ci = 0;
-#pragma unroll 1
-  for (int i = 1; i < args.nclass; ++i)
-    if (tile >= args.cls[i].tile_begin) ci = i;
-  const GemmClass &cl = args.cls[ci];
-  const int local = tile - cl.tile_begin;
-  const int mat = local / cl.tiles_per_mat;
-  int t = local - mat * cl.tiles_per_mat;
-  int tm, tn;
-  if (cl.half) {
-    tm = 0;
-    int rowlen = cl.tiles_n;
-#pragma unroll 1
-    while (t >= rowlen) { t -= rowlen; ++tm; --rowlen; }
-    tn = tm + t;
-  } else {
-    tm = t / cl.tiles_n;
-    tn = t - tm * cl.tiles_n;
-  }
+  const TileRef tr = locate_tile(args);
+  const GemmClass &cl = args.cls[tr.ci];
+  const int mat = tr.mat, tm = tr.tm, tn = tr.tn;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -203,56 +298,282 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(GemmArgs args) {
     }
   }
 
-  // ---- epilogue.  MFMA 16x16 output layout: lane holds rows 4*(lane/16)+r,
-  // column lane%16, r = 0..3.
-  const float alpha = cl.alpha, beta = cl.beta, diag = cl.diag;
-  void *C = cl.c ? (void *)((char *)cl.c + (int64_t)mat * cl.sc * ES) : nullptr;
-  void *C2 = cl.c2 ? (void *)((char *)cl.c2 + (int64_t)mat * cl.sc2 * ES) : nullptr;
-  const void *Cin = cl.cin ? (const void *)((const char *)cl.cin + (int64_t)mat * cl.scin * ES) : nullptr;
-  const bool diag_tile = cl.half && tm == tn;
-  const int row_base = tm * BM + wm * WM + 4 * (lane >> 4);
-  const int col_base = tn * BN + wn * WN + (lane & 15);
+  epilogue<T, FM, FN>(cl, mat, cl.half && tm == tn, tm * BM + wm * WM, tn * BN + wn * WN, acc);
+}
+
+
+// ---------------------------------------------------------------------------
+// 256 x 256 block tile for fp16 / bf16: four waves of 128 x 128 each, which
+// halves LDS traffic per MFMA relative to 64 x 64 wave tiles.
+//
+// Operands move global -> LDS with global_load_lds_dwordx4 (no register
+// staging).  A stage is 32 k (64 bytes per row) of the 256-row A and B
+// panels, 32 KB in all; stages live in a 4-deep LDS ring (128 KB) and are
+// fetched three stages ahead.  One DMA instruction deposits 1 KB = 16 rows x
+// 64 bytes.  LDS rows are not padded: 16-byte chunk c of row r is stored at
+// chunk c ^ ((r >> 1) & 3), so the 16-byte fragment reads of any 8
+// consecutive rows touch 8 distinct bank groups.
+//
+// Iteration kb (one barrier): wait until stage kb+1 has landed, barrier,
+// issue the DMA of stage kb+3 into the slot stage kb-1 used, then run the 64
+// MFMAs of stage kb while streaming its A fragments one ahead and reading the
+// B fragments (and first A fragment) of stage kb+1.
+constexpr int kBigTile = 256;
+constexpr int kBigRowBytes = 64;                                    // 32 x 16-bit k per stage
+constexpr int kBigStage = (kBigTile + kBigTile) * kBigRowBytes;     // 32 KB
+#ifndef MUON_BIG_RING
+#define MUON_BIG_RING 4
+#endif
+#ifndef MUON_A_AHEAD
+#define MUON_A_AHEAD 3
+#endif
+constexpr int kBigRing = MUON_BIG_RING;   // LDS ring depth (stages); DMA runs kBigRing-1 ahead
+constexpr int kAAhead = MUON_A_AHEAD;     // A fragments read this many 16-row blocks ahead
+
+// WN_WAVES = 2: four waves (one per SIMD), 128 x 128 each.
+// WN_WAVES = 4: eight waves (two per SIMD), 128 x 64 each; the second wave
+// on each SIMD issues MFMAs while the first waits at a barrier or on LDS.
+template <typename T, int WN_WAVES>
+__global__ __launch_bounds__(2 * WN_WAVES * 64, 1) void ns_gemm_big_kernel(GemmArgs args) {
+  static_assert(sizeof(T) == 2, "16-bit operands only");
+  static_assert(8 % (kAAhead + 1) == 0, "A fragment ring must divide the 8 row blocks");
+  constexpr int NWAVES = 2 * WN_WAVES;
+  constexpr int WTN = kBigTile / WN_WAVES;       // wave tile columns
+  constexpr int FM = 8, FN = WTN / 16;           // 128 x WTN per wave
+  constexpr int DMA_PER_WAVE = 16 / NWAVES;      // 1 KB DMA instructions per operand per stage
+  __shared__ __attribute__((aligned(1024))) char lds[kBigRing * kBigStage];
+
+  const TileRef tr = locate_tile(args);
+  const GemmClass &cl = args.cls[tr.ci];
+  const int mat = tr.mat, tm = tr.tm, tn = tr.tn;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave / WN_WAVES, wn = wave % WN_WAVES;
+  constexpr int PER_STAGE = 2 * DMA_PER_WAVE;   // DMA instructions per stage and wave
+
+  const char *A = (const char *)cl.a + ((int64_t)mat * cl.sa + (int64_t)tm * kBigTile * cl.lda) * 2;
+  const char *B = (const char *)cl.b + ((int64_t)mat * cl.sb + (int64_t)tn * kBigTile * cl.ldb) * 2;
+  const int64_t lda_b = (int64_t)cl.lda * 2, ldb_b = (int64_t)cl.ldb * 2;
+
+  // DMA: wave w moves rows [16 DMA_PER_WAVE w, +16 DMA_PER_WAVE) of A and of
+  // B, 16 rows per instruction; lane L covers row L / 4 of the group and
+  // physical chunk L % 4, which holds logical chunk (L % 4) ^ ((L / 4 >> 1) & 3).
+  const int dma_row = lane >> 2;
+  const int dma_chunk = (lane & 3) ^ ((dma_row >> 1) & 3);
+  const uint32_t a_lane = (uint32_t)(dma_row * lda_b) + (uint32_t)(dma_chunk * 16);
+  const uint32_t b_lane = (uint32_t)(dma_row * ldb_b) + (uint32_t)(dma_chunk * 16);
+  const char *a_src = A + (int64_t)(wave * 16 * DMA_PER_WAVE) * lda_b;
+  const char *b_src = B + (int64_t)(wave * 16 * DMA_PER_WAVE) * ldb_b;
+
+  // fragment reads: row (16-row block) + lane % 16, logical chunk lane / 16
+  const int fr_row = lane & 15;
+  const int fr_chunk = ((lane >> 4) ^ ((fr_row >> 1) & 3)) * 16;
+  const int a_frag = (wm * 128 + fr_row) * kBigRowBytes + fr_chunk;
+  const int b_frag = (kBigTile + wn * WTN + fr_row) * kBigRowBytes + fr_chunk;
+
+  f32x4 acc[FM][FN];
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int r0 = row_base + i * 16;
-      const int col = col_base + j * 16;
-      float v[4];
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = cl.K / (kBigRowBytes / 2);
+  if (nk > 0) {
+    auto dma = [&](int kb) {
+      char *dst = lds + (kb % kBigRing) * kBigStage + wave * DMA_PER_WAVE * 1024;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        v[r] = alpha * acc[i][j][r];
-        if (Cin) v[r] += beta * Store<T>::load(Cin, (int64_t)(r0 + r) * cl.ldcin + col);
-        if (diag != 0.0f && r0 + r == col && col < cl.diag_limit) v[r] += diag;
+      for (int j = 0; j < DMA_PER_WAVE; ++j) {
+        const char *base = a_src + (int64_t)j * 16 * lda_b + (int64_t)kb * kBigRowBytes;
+        __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)(base + a_lane),
+                                         (void __attribute__((address_space(3))) *)(dst + j * 1024), 16, 0, 0);
       }
-      if (C) {
-        if (!cl.half) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) Store<T>::store(C, (int64_t)(r0 + r) * cl.ldc + col, v[r]);
-        } else if (!diag_tile) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) Store<T>::store(C, (int64_t)(r0 + r) * cl.ldc + col, v[r]);
-          Store<T>::store4(C, (int64_t)col * cl.ldc + r0, v);   // mirror
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            if (col >= r0 + r) {
-              Store<T>::store(C, (int64_t)(r0 + r) * cl.ldc + col, v[r]);
-              Store<T>::store(C, (int64_t)col * cl.ldc + r0 + r, v[r]);
-            }
-          }
-        }
+      for (int j = 0; j < DMA_PER_WAVE; ++j) {
+        const char *base = b_src + (int64_t)j * 16 * ldb_b + (int64_t)kb * kBigRowBytes;
+        __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)(base + b_lane),
+                                         (void __attribute__((address_space(3))) *)(dst + kBigTile * kBigRowBytes + j * 1024),
+                                         16, 0, 0);
       }
-      if (C2) Store<T>::store4(C2, (int64_t)col * cl.ldc2 + r0, v);
+    };
+    auto rd = [&](int kb, int off) -> u32x4 {
+      return *(const u32x4 *)(lds + (kb % kBigRing) * kBigStage + off);
+    };
+    // prologue: stages 0 .. kBigRing-2 in flight; wait for stage 0 (DMA
+    // completes in issue order, PER_STAGE instructions per stage and wave)
+    static_for<0, kBigRing - 1>([&](auto sc) {
+      constexpr int st = decltype(sc)::value;
+      if (st < nk) dma(st);
+    });
+    {
+      const int inflight = min(nk, kBigRing - 1) - 1;   // stages issued after stage 0
+      waitcnt_vm(inflight * PER_STAGE);
+    }
+    __syncthreads();
+    u32x4 bx[FN], by[FN], a_q[kAAhead + 1];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) bx[j] = rd(0, b_frag + j * 16 * kBigRowBytes);
+#pragma unroll
+    for (int q = 0; q < kAAhead; ++q) a_q[q] = rd(0, a_frag + q * 16 * kBigRowBytes);
+
+    // one stage: MFMAs on (a_cur stream, bc), reading bn and the next a_cur
+    auto stage = [&](int kb, u32x4 (&bc)[FN], u32x4 (&bn)[FN]) {
+      // Stage kb+1 must be visible before its fragments are read below: this
+      // wave's DMA of kb+1 is done once at most one stage is outstanding; the
+      // barrier covers the other waves.  The barrier is raw (no fence) so the
+      // DMA of stage kb+2 stays in flight; the memory clobber keeps the
+      // compiler from moving LDS reads across it.
+      // DMAs issued so far cover stages up to kb + kBigRing - 2; all but the
+      // ones after kb+1 must have landed
+      waitcnt_vm(max(0, min(nk - (kb + 2), kBigRing - 3)) * PER_STAGE);
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_barrier" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      if (kb + kBigRing - 1 < nk) dma(kb + kBigRing - 1);
+      // After the last stage the look-ahead reads fetch a stale ring slot
+      // (inside the LDS allocation) and are never used: no branch, so the
+      // accumulators keep one register assignment around the loop.
+      static_for<0, FM>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        constexpr int ia = i + kAAhead;            // A block read in this group
+        a_q[(i + kAAhead) % (kAAhead + 1)] =
+            (ia < FM) ? rd(kb, a_frag + ia * 16 * kBigRowBytes) : rd(kb + 1, a_frag + (ia - FM) * 16 * kBigRowBytes);
+        if constexpr (i < FN) bn[i] = rd(kb + 1, b_frag + i * 16 * kBigRowBytes);
+        __builtin_amdgcn_sched_barrier(0);   // reads issue before the MFMAs that hide them
+#pragma unroll
+        for (int j = 0; j < FN; ++j) Mma<T>::run(a_q[i % (kAAhead + 1)], bc[j], acc[i][j]);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    };
+    // K is a multiple of the 256 tile, so nk is a multiple of 8: stages
+    // come in pairs and the B fragment sets alternate without copies.
+#pragma unroll 1
+    for (int kb = 0; kb < nk; kb += 2) {
+      stage(kb, bx, by);
+      stage(kb + 1, by, bx);
     }
   }
+  epilogue<T, FM, FN>(cl, mat, cl.half && tm == tn, tm * kBigTile + wm * 128, tn * kBigTile + wn * WTN, acc);
+}
+
+// ---------------------------------------------------------------------------
+// 64 x 64 block tile for fp16 / bf16 at small sizes, where a step is a chain
+// of memory latencies rather than MFMA work.  Four waves of 32 x 32.  The
+// same swizzled, unpadded 64-byte-row LDS stages as the 256 tile (32 k per
+// stage, 8 KB for A and B), in a ring of RING stages that is filled up front:
+// a K <= 32 RING panel costs one memory round trip.  Stages are consumed in
+// groups of 4 with one barrier per group; after the barrier the slots of the
+// previous group are refilled with the stages RING ahead.
+constexpr int kSmallTile = 64;
+constexpr int kSmallStage = 2 * kSmallTile * kBigRowBytes;   // 8 KB
+constexpr int kSmallGroup = 4;
+
+template <typename T, int RING>
+__global__ __launch_bounds__(kThreads) void ns_gemm_small_kernel(GemmArgs args) {
+  static_assert(sizeof(T) == 2, "16-bit operands only");
+  static_assert(RING % kSmallGroup == 0, "ring holds whole groups");
+  constexpr int FM = 2, FN = 2;
+  __shared__ __attribute__((aligned(1024))) char lds[RING * kSmallStage];
+
+  const TileRef tr = locate_tile(args);
+  const GemmClass &cl = args.cls[tr.ci];
+  const int mat = tr.mat, tm = tr.tm, tn = tr.tn;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  const char *A = (const char *)cl.a + ((int64_t)mat * cl.sa + (int64_t)tm * kSmallTile * cl.lda) * 2;
+  const char *B = (const char *)cl.b + ((int64_t)mat * cl.sb + (int64_t)tn * kSmallTile * cl.ldb) * 2;
+  const int64_t lda_b = (int64_t)cl.lda * 2, ldb_b = (int64_t)cl.ldb * 2;
+
+  // DMA: wave w moves rows [16 w, 16 w + 16) of A and of B (one instruction
+  // each per stage); lane L covers row L / 4 and physical chunk L % 4.
+  const int dma_row = lane >> 2;
+  const int dma_chunk = (lane & 3) ^ ((dma_row >> 1) & 3);
+  const char *a_src = A + (int64_t)(wave * 16 + dma_row) * lda_b + dma_chunk * 16;
+  const char *b_src = B + (int64_t)(wave * 16 + dma_row) * ldb_b + dma_chunk * 16;
+
+  const int fr_row = lane & 15;
+  const int fr_chunk = ((lane >> 4) ^ ((fr_row >> 1) & 3)) * 16;
+  const int a_frag = (wm * 32 + fr_row) * kBigRowBytes + fr_chunk;
+  const int b_frag = (kSmallTile + wn * 32 + fr_row) * kBigRowBytes + fr_chunk;
+
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = cl.K / (kBigRowBytes / 2);
+  if (nk > 0) {
+    auto dma = [&](int kb) {
+      char *dst = lds + (kb % RING) * kSmallStage + wave * 1024;
+      __builtin_amdgcn_global_load_lds((const void *)(a_src + (int64_t)kb * kBigRowBytes),
+                                       (void __attribute__((address_space(3))) *)dst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void *)(b_src + (int64_t)kb * kBigRowBytes),
+                                       (void __attribute__((address_space(3))) *)(dst + kSmallTile * kBigRowBytes),
+                                       16, 0, 0);
+    };
+    const int first = min(nk, RING);
+#pragma unroll 1
+    for (int kb = 0; kb < first; ++kb) dma(kb);
+    int issued = first;   // stages [0, issued) have been requested
+    const int ngroups = (nk + kSmallGroup - 1) / kSmallGroup;
+#pragma unroll 1
+    for (int g = 0; g < ngroups; ++g) {
+      const int s0 = g * kSmallGroup, s1 = min(nk, s0 + kSmallGroup);
+      // stages after this group may stay in flight (2 DMA per stage and wave)
+      waitcnt_vm(2 * (issued - s1));
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_barrier" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      // every wave is past group g-1: refill its slots with the stages RING ahead
+      if (g > 0) {
+        const int r1 = min(nk, s0 - kSmallGroup + RING + kSmallGroup);
+#pragma unroll 1
+        for (; issued < r1; ++issued) dma(issued);
+      }
+#pragma unroll 1
+      for (int kb = s0; kb < s1; ++kb) {
+        const char *st = lds + (kb % RING) * kSmallStage;
+        u32x4 fa[FM], fb[FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) fa[i] = *(const u32x4 *)(st + a_frag + i * 16 * kBigRowBytes);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) fb[j] = *(const u32x4 *)(st + b_frag + j * 16 * kBigRowBytes);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) Mma<T>::run(fa[i], fb[j], acc[i][j]);
+      }
+    }
+  }
+  epilogue<T, FM, FN>(cl, mat, cl.half && tm == tn, tm * kSmallTile + wm * 32, tn * kSmallTile + wn * 32, acc);
 }
 
 template <typename T>
 hipError_t launch_t(const GemmArgs &args, int tile, hipStream_t s) {
   switch (tile) {
-    case 64: hipLaunchKernelGGL((ns_gemm_kernel<T, 64, 64>), dim3(args.total_tiles), dim3(kThreads), 0, s, args); break;
+    case 64:
+      if constexpr (sizeof(T) == 2) {
+        // ring just deep enough for the longest K of the launch (max 16 stages)
+        int kmax = 0;
+        for (int c = 0; c < args.nclass; ++c) kmax = max(kmax, args.cls[c].K);
+        const int nk = kmax / (kBigRowBytes / 2);
+        if (nk <= 4) hipLaunchKernelGGL((ns_gemm_small_kernel<T, 4>), dim3(args.total_tiles), dim3(kThreads), 0, s, args);
+        else if (nk <= 8) hipLaunchKernelGGL((ns_gemm_small_kernel<T, 8>), dim3(args.total_tiles), dim3(kThreads), 0, s, args);
+        else hipLaunchKernelGGL((ns_gemm_small_kernel<T, 16>), dim3(args.total_tiles), dim3(kThreads), 0, s, args);
+      } else {
+        hipLaunchKernelGGL((ns_gemm_kernel<T, 64, 64>), dim3(args.total_tiles), dim3(kThreads), 0, s, args);
+      }
+      break;
     case 128: hipLaunchKernelGGL((ns_gemm_kernel<T, 128, 128>), dim3(args.total_tiles), dim3(kThreads), 0, s, args); break;
+    case 256:
+      if constexpr (sizeof(T) == 2) {
+        hipLaunchKernelGGL((ns_gemm_big_kernel<T, 4>), dim3(args.total_tiles), dim3(512), 0, s, args);
+        break;
+      } else {
+        return hipErrorInvalidValue;
+      }
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

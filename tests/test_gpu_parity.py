@@ -55,7 +55,7 @@ def run_case(shapes, *, grad_dtype, ns_dtype, variant="direct", kind="quintic", 
 
 
 SMALL = [(64, 256), (100, 300), (300, 100), (130, 130), (1, 77), (77, 1), (5, 3)]
-MEDIUM = [(260, 520), (520, 260), (384, 384), (300, 1000)]
+MEDIUM = [(260, 520), (520, 260), (384, 384), (300, 1000), (600, 900), (1000, 1500), (1500, 1000)]
 
 
 # ---------------------------------------------------------------- fp32 path
