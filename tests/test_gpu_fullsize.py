@@ -1,0 +1,126 @@
+"""Full-size parity: every synthetic workload at its real size, stepped exactly
+as bench.py steps it (all matrices in one call), checked against the fp64
+oracle on one sampled matrix per shape class (every stage: momentum,
+acceleration, previous gradient, O and dW), plus finiteness of every matrix.
+
+The oracle computes full products in fp64 on the host, so only sampled
+matrices are re-derived; the elementwise state of every other matrix is
+checked on sampled elements.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import rel_fro, to64, tol_for, TOL_STATE
+from workloads import WORKLOADS, make_grads, make_state
+
+pytestmark = pytest.mark.gpu
+
+
+def _setup(w, device):
+    gen_dev = device if w.name.startswith("gram_tall") else "cpu"
+    state = make_state(w, device=gen_dev)
+    params = []
+    for st in state:
+        params.append({k: v.to(device) for k, v in st.items()})
+    return params, gen_dev
+
+
+def _sample_indices(w):
+    """First matrix of every shape class."""
+    seen, idx = set(), []
+    for i, s in enumerate(w.shapes):
+        if s not in seen:
+            seen.add(s)
+            idx.append(i)
+    return idx
+
+
+def _run_workload(name, variant):
+    import newton_schulz_matrix_momentum_amd as nsm
+    w = WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    print("workload %s variant %s: %d matrices" % (name, variant, len(w.shapes)), flush=True)
+    params, gen_dev = _setup(w, dev)
+    sample = _sample_indices(w)
+    for i in sample:
+        params[i]["ortho_out"] = torch.empty_like(params[i]["weight"])
+    divisor, restart = w.settings_for(variant)
+    coeffs = oracle.coefficient_table(w.coeffs, w.ns_steps)
+    tol = tol_for(w.ns_dtype)
+    snaps = {i: {k: to64(v) for k, v in params[i].items() if k != "ortho_out"} for i in sample}
+    rng = np.random.default_rng(7)
+    for step in range(w.steps):
+        grads = make_grads(w, step, device=gen_dev)
+        for p, g in zip(params, grads):
+            p["grad"] = g.to(dev)
+        # elementwise spot checks on a few elements of every matrix
+        probes = []
+        for i, p in enumerate(params):
+            n = p["weight"].numel()
+            pos = torch.from_numpy(rng.integers(0, n, 16)).to(dev)
+            probes.append((i, pos, {k: p[k].flatten()[pos].double().cpu().numpy()
+                                    for k in ("grad", "momentum", "accel", "prev_grad") if k in p}))
+        w_gpu_before = {i: to64(params[i]["weight"]) for i in sample}
+        nsm.muon_step(params, lr=w.lr, mu=w.mu, beta_a=w.beta_a, alpha=w.alpha, weight_decay=w.weight_decay,
+                      ns_steps=w.ns_steps, variant=variant, ns_dtype=w.ns_dtype, coeffs=coeffs.tolist(),
+                      divisor=divisor, restart_every=restart, step=step)
+        torch.cuda.synchronize()
+        for i, pos, before in probes:
+            p = params[i]
+            m_ref = w.mu * before["momentum"]
+            if "accel" in before:
+                d = np.zeros_like(before["grad"]) if step == 0 else before["grad"] - before["prev_grad"]
+                a_ref = w.beta_a * before["accel"] + (1 - w.beta_a) * d
+                m_ref = m_ref + before["grad"] + w.alpha * a_ref
+                np.testing.assert_allclose(p["accel"].flatten()[pos].double().cpu().numpy(), a_ref,
+                                           rtol=1e-5, atol=1e-7)
+                assert torch.equal(p["prev_grad"].flatten()[pos], p["grad"].flatten()[pos])
+            else:
+                m_ref = m_ref + before["grad"]
+            np.testing.assert_allclose(p["momentum"].flatten()[pos].double().cpu().numpy(), m_ref,
+                                       rtol=1e-5, atol=1e-6)
+            assert torch.isfinite(p["weight"]).all(), "matrix %d has non-finite weights" % i
+        for i in sample:
+            s = snaps[i]
+            g = to64(params[i]["grad"])
+            ref = oracle.muon_step_matrix(s["weight"], g, s["momentum"], lr=w.lr, mu=w.mu,
+                                          weight_decay=w.weight_decay, coeffs=coeffs, variant=variant,
+                                          divisor=divisor, restart_every=restart, accel=s.get("accel"),
+                                          prev_grad=s.get("prev_grad"), beta_a=w.beta_a, alpha=w.alpha, step=step)
+            p = params[i]
+            assert rel_fro(to64(p["momentum"]), ref["momentum"]) <= TOL_STATE
+            if "accel" in p:
+                assert rel_fro(to64(p["accel"]), ref["accel"]) <= TOL_STATE
+            o_err = rel_fro(to64(p["ortho_out"]), ref["ortho"])
+            dw_err = rel_fro(to64(p["weight"]) - w_gpu_before[i], ref["weight"] - s["weight"])
+            print("  step %d matrix %d %s: O err %.3g, dW err %.3g (tol %.0e)"
+                  % (step, i, w.shapes[i], o_err, dw_err, tol), flush=True)
+            assert o_err <= tol and dw_err <= tol
+            # carry the oracle's own state forward (never the GPU's)
+            s["weight"], s["momentum"] = ref["weight"], ref["momentum"]
+            if "accel" in ref:
+                s["accel"], s["prev_grad"] = ref["accel"], ref["prev_grad"]
+
+
+def test_full_single_64x256_f32():
+    _run_workload("single_64x256_f32", "direct")
+
+
+def test_full_nanochat_6l_d192():
+    _run_workload("nanochat_6l_d192", "direct")
+
+
+def test_full_llama430m_24l_d1024():
+    _run_workload("llama430m_24l_d1024", "direct")
+
+
+@pytest.mark.parametrize("variant", ["direct", "gram"])
+def test_full_moe_64e_d2048(variant):
+    _run_workload("moe_64e_d2048", variant)
+
+
+@pytest.mark.timeout(600)
+def test_full_gram_tall_32x4096x16384():
+    _run_workload("gram_tall_32x4096x16384", "gram")
