@@ -37,7 +37,52 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--trace-steps", type=int, default=None, help="steps timed per launch (default: --steps)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB --steps times (counter calibration)")
     return ap.parse_args()
+
+
+def kernel_source_hash():
+    """sha256 of the NS GEMM kernel source: HBM-traffic figures in profiles/
+    apply only to the kernel they were measured on."""
+    import hashlib
+    path = os.path.join(ROOT, "newton_schulz_matrix_momentum_amd", "csrc", "ns_gemm.hip")
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def recorded_traffic(workload):
+    """HBM bytes per NS GEMM launch measured with rocprofv3 FETCH_SIZE and
+    WRITE_SIZE (scaled by a plain copy's readings), from
+    profiles/<workload>_ns_gemm_traffic.md, or None when that file is absent
+    or was measured on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", "%s_ns_gemm_traffic.md" % workload)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and line.startswith("- "):
+                k, v = line[2:].split(":", 1)
+                vals[k.strip()] = v.strip().strip("`")
+    if vals.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_probe(args):
+    import torch
+    n = args.copy_probe << 20
+    x = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "launches": args.steps}), flush=True)
 
 
 class HipEvents:
@@ -223,6 +268,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_probe:
+        copy_probe(args)
+        return
     w = WORKLOADS[args.workload]
     variant = args.variant or w.variants[0]
     print("bench: workload %s variant %s, %d matrices, %d warmup + %d timed steps" %
@@ -242,9 +290,10 @@ def main():
     if dom == "gemm":
         per_launch_work = gemm["work"] / gemm["launches"]
         per_launch_ms = gemm["ms"] / gemm["launches"]
-        roof = {"kernel": "ns_gemm_kernel (%s)" % w.ns_dtype, "bound": "mfma",
+        roof = {"kernel": "ns_gemm (all Newton-Schulz product launches, %s)" % w.ns_dtype, "bound": "mfma",
                 "achieved": per_launch_work / (per_launch_ms * 1e-3) / 1e12, "peak": peak, "unit": "TFLOP/s",
-                "avg_launch_us": per_launch_ms * 1e3, "work_per_launch": per_launch_work, "traffic": None}
+                "avg_launch_us": per_launch_ms * 1e3, "work_per_launch": per_launch_work,
+                "traffic": recorded_traffic(w.name)}
     else:
         d = per_stage[dom]
         per_launch_work = d["work"] / d["launches"]
