@@ -75,15 +75,14 @@ __device__ __forceinline__ double wave_sum(double v) {
   return v;
 }
 
-// Find the matrix owning block `b` (block_begin is ascending).
-template <typename M>
-__device__ __forceinline__ int find_mat(const M *mats, int n, int b) {
-  int lo = 0, hi = n - 1;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (mats[mid].block_begin <= b) lo = mid; else hi = mid - 1;
-  }
-  return lo;
+// Matrix owning block `b`: begin[] is ascending with INT32_MAX past the
+// last matrix, so the owner's index is the number of later entries <= b.
+template <int N>
+__device__ __forceinline__ int find_mat(const int32_t (&begin)[N], int b) {
+  int mi = 0;
+#pragma unroll
+  for (int i = 1; i < N; ++i) mi += (begin[i] <= b) ? 1 : 0;
+  return mi;
 }
 
 // ------------------------------------------------------------------ E1
@@ -102,10 +101,20 @@ __global__ __launch_bounds__(kE1Threads) void e1_kernel(E1Args args) {
   typedef typename Elem<GDT>::raw graw;
   typedef typename Vec4<GDT>::type gvec;
   constexpr int G = kE1ElemsPerThread / 4;   // groups of 4 elements per thread
-  const int mi = find_mat(args.mats, args.nmat, (int)blockIdx.x);
+  const int mi = find_mat(args.begin, (int)blockIdx.x);
   const E1Mat &mt = args.mats[mi];
-  const int64_t blk = (int64_t)blockIdx.x - mt.block_begin;
+  const int64_t blk = (int64_t)blockIdx.x - args.begin[mi];
   const int64_t base = blk * kE1BlockElems;
+  if (blk == 0 && threadIdx.x == 0 && mt.desc_idx >= 0) {
+    FinalDesc d;
+    d.weight = mt.weight;
+    d.ortho_out = mt.ortho_out;
+    d.rows = mt.rows;
+    d.cols = mt.cols;
+    d.gamma = mt.gamma;
+    d.wide = mt.rows <= mt.cols ? 1 : 0;
+    args.desc[mt.desc_idx] = d;
+  }
   const int64_t numel = mt.numel;
   const graw *grad = (const graw *)mt.grad;
   graw *prev = (graw *)mt.prev;
@@ -113,44 +122,65 @@ __global__ __launch_bounds__(kE1Threads) void e1_kernel(E1Args args) {
   float *acc = mt.accel;
   const bool vec_ok = ((((uintptr_t)grad) | ((uintptr_t)mom) | ((uintptr_t)acc) | ((uintptr_t)prev)) & 15) == 0 &&
                       (sizeof(graw) == 4 || ((((uintptr_t)grad) | ((uintptr_t)prev)) & 7) == 0);
-  const bool full = vec_ok && base + kE1BlockElems <= numel;
   float sq = 0.0f;
-  if (full) {
-    // every load of the thread is issued before the first use
+  if (vec_ok) {
+    // Groups of 4 elements, predicated on lying inside the matrix; every load
+    // of the thread is issued before the first use (no serial tail loop).
     gvec gv[G], pv[G];
     float4 mv[G], av[G];
 #pragma unroll
     for (int it = 0; it < G; ++it) {
       const int64_t e = base + ((int64_t)it * kE1Threads + threadIdx.x) * 4;
-      gv[it] = *(const gvec *)(grad + e);
-      mv[it] = *(const float4 *)(mom + e);
-      if (MONA) {
-        av[it] = *(const float4 *)(acc + e);
-        if (!args.first_step) pv[it] = *(const gvec *)(prev + e);
+      if (e + 4 <= numel) {
+        gv[it] = *(const gvec *)(grad + e);
+        mv[it] = *(const float4 *)(mom + e);
+        if (MONA) {
+          av[it] = *(const float4 *)(acc + e);
+          if (!args.first_step) pv[it] = *(const gvec *)(prev + e);
+        }
       }
     }
 #pragma unroll
     for (int it = 0; it < G; ++it) {
       const int64_t e = base + ((int64_t)it * kE1Threads + threadIdx.x) * 4;
-      float g[4], m[4] = {mv[it].x, mv[it].y, mv[it].z, mv[it].w}, a[4] = {0, 0, 0, 0}, p[4] = {0, 0, 0, 0};
-      Vec4<GDT>::unpack(gv[it], g);
-      if (MONA) {
-        a[0] = av[it].x; a[1] = av[it].y; a[2] = av[it].z; a[3] = av[it].w;
-        if (!args.first_step) Vec4<GDT>::unpack(pv[it], p);
-      }
+      if (e + 4 <= numel) {
+        float g[4], m[4] = {mv[it].x, mv[it].y, mv[it].z, mv[it].w}, a[4] = {0, 0, 0, 0}, p[4] = {0, 0, 0, 0};
+        Vec4<GDT>::unpack(gv[it], g);
+        if (MONA) {
+          a[0] = av[it].x; a[1] = av[it].y; a[2] = av[it].z; a[3] = av[it].w;
+          if (!args.first_step) Vec4<GDT>::unpack(pv[it], p);
+        }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        e1_elem<GDT, MONA>(g[q], m[q], a[q], p[q], args);
-        sq += m[q] * m[q];
-      }
-      *(float4 *)(mom + e) = make_float4(m[0], m[1], m[2], m[3]);
-      if (MONA) {
-        *(float4 *)(acc + e) = make_float4(a[0], a[1], a[2], a[3]);
-        *(gvec *)(prev + e) = gv[it];  // exact copy of the stored gradient
+        for (int q = 0; q < 4; ++q) {
+          e1_elem<GDT, MONA>(g[q], m[q], a[q], p[q], args);
+          sq += m[q] * m[q];
+        }
+        *(float4 *)(mom + e) = make_float4(m[0], m[1], m[2], m[3]);
+        if (MONA) {
+          *(float4 *)(acc + e) = make_float4(a[0], a[1], a[2], a[3]);
+          *(gvec *)(prev + e) = gv[it];  // exact copy of the stored gradient
+        }
+      } else if (e < numel) {
+        // the matrix's last numel % 4 elements
+        for (int64_t j = e; j < numel; ++j) {
+          const graw graw_v = grad[j];
+          float m = mom[j], a = 0.0f, pp = 0.0f;
+          if (MONA) {
+            a = acc[j];
+            if (!args.first_step) pp = Elem<GDT>::to_f32(prev[j]);
+          }
+          e1_elem<GDT, MONA>(Elem<GDT>::to_f32(graw_v), m, a, pp, args);
+          sq += m * m;
+          mom[j] = m;
+          if (MONA) {
+            acc[j] = a;
+            prev[j] = graw_v;
+          }
+        }
       }
     }
   } else {
-    // ragged tail or unaligned buffers: element by element
+    // unaligned buffers: element by element
     for (int64_t j = base + threadIdx.x; j < numel && j < base + kE1BlockElems; j += kE1Threads) {
       const graw graw_v = grad[j];
       const float g = Elem<GDT>::to_f32(graw_v);
@@ -205,44 +235,65 @@ __global__ __launch_bounds__(256) void e2_kernel(E2Args args) {
   typedef typename Elem<NDT>::raw nraw;
   typedef typename Vec4<NDT>::type nvec;
   __shared__ float tile[kE2Tile][kE2Tile + 1];
-  // matrices are found by tile_begin (stored in the block_begin slot's place)
-  int lo = 0, hi = args.nmat - 1;
   const int b = blockIdx.x;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (args.mats[mid].tile_begin <= b) lo = mid; else hi = mid - 1;
-  }
-  const E2Mat &mt = args.mats[lo];
-  const int t = b - mt.tile_begin;
+  const int mi = find_mat(args.begin, b);
+  const E2Mat &mt = args.mats[mi];
+  const int t = b - args.begin[mi];
   const int tr = t / mt.tiles_c, tc = t - tr * mt.tiles_c;
   const int r0 = tr * kE2Tile, c0 = tc * kE2Tile;
-  const float scale = args.scales[mt.scale_idx];
+  // M loads first: their latency overlaps the scale reduction below
   const int cg = (threadIdx.x & 15) * 4;   // column group within the tile
   const int rr = threadIdx.x >> 4;         // 0..15
-  nraw *nat = (nraw *)mt.nat;
-  nraw *trn = (nraw *)mt.trn;
   const bool vec_ok = ((mt.cols & 3) == 0) && ((((uintptr_t)mt.mom) & 15) == 0);
+  float v[4][4];
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
     const int r = r0 + rr + 16 * it;
     const int c = c0 + cg;
-    float v[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[it][q] = 0.f;
     if (r < mt.rows) {
       const float *src = mt.mom + (int64_t)r * mt.cols;
       if (vec_ok && c + 4 <= mt.cols) {
         const float4 x = *(const float4 *)(src + c);
-        v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+        v[it][0] = x.x; v[it][1] = x.y; v[it][2] = x.z; v[it][3] = x.w;
       } else {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          if (c + q < mt.cols) v[q] = src[c + q];
+          if (c + q < mt.cols) v[it][q] = src[c + q];
       }
     }
+  }
+  float scale;
+  if (mt.nparts > 0) {
+    // few partials: reduce them here, in the same fixed order in every block
+    // of the matrix (one partial per lane, fp64 butterfly)
+    __shared__ float sh_scale;
+    if (threadIdx.x < 64) {
+      double p = ((int)threadIdx.x < mt.nparts) ? args.partials[mt.partial_off + threadIdx.x] : 0.0;
+      p = wave_sum(p);
+      if (threadIdx.x == 0) {
+        // zero matrix => X0 = 0 (no epsilon); Inf/NaN propagate
+        const double sc = (p == 0.0) ? 0.0 : (double)args.inv_sqrt_d / sqrt(p);
+        sh_scale = (float)(sc * (double)args.store_scale);
+      }
+    }
+    __syncthreads();
+    scale = sh_scale;
+  } else {
+    scale = args.scales[mt.scale_idx];
+  }
+  nraw *nat = (nraw *)mt.nat;
+  nraw *trn = (nraw *)mt.trn;
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int r = r0 + rr + 16 * it;
+    const int c = c0 + cg;
     float o[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       // round once to the storage dtype; the LDS copy holds the rounded value
-      o[q] = Elem<NDT>::to_f32(Elem<NDT>::from_f32(v[q] * scale));
+      o[q] = Elem<NDT>::to_f32(Elem<NDT>::from_f32(v[it][q] * scale));
       tile[rr + 16 * it][cg + q] = o[q];
     }
     *(nvec *)(nat + (int64_t)r * mt.ld_nat + c) = Vec4<NDT>::pack(o);
@@ -264,26 +315,30 @@ __global__ __launch_bounds__(kE3Threads) void e3_kernel(E3Args args) {
   typedef typename Elem<NDT>::raw nraw;
   typedef typename Vec4<NDT>::type nvec;
   constexpr int G = kE3BlockElems / (kE3Threads * 4);
-  const int mi = find_mat(args.mats, args.nmat, (int)blockIdx.x);
+  const int mi = find_mat(args.begin, (int)blockIdx.x);
   const E3Mat &mt = args.mats[mi];
-  const int64_t base = ((int64_t)blockIdx.x - mt.block_begin) * kE3BlockElems;
+  const int64_t base = ((int64_t)blockIdx.x - args.begin[mi]) * kE3BlockElems;
   const nraw *o = (const nraw *)mt.o;
   const float lr = args.lr, wd = args.wd, gamma = mt.gamma, inv = mt.inv_o_scale;
-  if (mt.vec_ok && base + kE3BlockElems <= mt.numel) {
-    // every load of the thread is issued before the first use
+  if (mt.vec_ok) {
+    // cols % 4 == 0, so groups of 4 never straddle a row; every load of the
+    // thread is issued before the first use
     nvec ovv[G];
     float4 wvv[G];
 #pragma unroll
     for (int it = 0; it < G; ++it) {
       const int64_t e = base + ((int64_t)it * kE3Threads + threadIdx.x) * 4;
-      const int64_t i = e / mt.cols;
-      const int64_t j = e - i * mt.cols;
-      ovv[it] = *(const nvec *)(o + i * mt.ld_o + j);
-      wvv[it] = *(const float4 *)(mt.weight + e);
+      if (e < mt.numel) {
+        const int64_t i = e / mt.cols;
+        const int64_t j = e - i * mt.cols;
+        ovv[it] = *(const nvec *)(o + i * mt.ld_o + j);
+        wvv[it] = *(const float4 *)(mt.weight + e);
+      }
     }
 #pragma unroll
     for (int it = 0; it < G; ++it) {
       const int64_t e = base + ((int64_t)it * kE3Threads + threadIdx.x) * 4;
+      if (e >= mt.numel) continue;
       float ov[4];
       Vec4<NDT>::unpack(ovv[it], ov);
       float wv[4] = {wvv[it].x, wvv[it].y, wvv[it].z, wvv[it].w};

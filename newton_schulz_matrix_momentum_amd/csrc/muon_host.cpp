@@ -65,6 +65,7 @@ struct ClassInfo {
   int64_t s = 0, l = 0;
   int tile = 64;
   int64_t Sp = 0, Lp = 0;
+  int desc_base = 0;               // first FinalDesc slot of the class
   std::vector<int> members;
   size_t X[2] = {0, 0}, XT[2] = {0, 0};
   size_t sq[5] = {0, 0, 0, 0, 0};   // direct: A, B ; gram: R, T, P, Q, Qspare
@@ -78,7 +79,7 @@ struct Plan {
   std::vector<ClassInfo> classes;
   std::vector<int> cls_of, idx_in_cls;
   std::vector<int> e1_blocks, partial_off;
-  size_t off_partials = 0, off_scales = 0, total = 0;
+  size_t off_partials = 0, off_scales = 0, off_desc = 0, total = 0;
 };
 
 bool is_finite(double v) { return std::isfinite(v); }
@@ -214,6 +215,15 @@ muon_status build_plan(const muon_param *p, int n, int ns_steps, muon_variant v,
   off = align256(off + (size_t)parts * sizeof(double));
   plan.off_scales = off;
   off = align256(off + (size_t)std::max(n, 1) * sizeof(float));
+  plan.off_desc = off;
+  off = align256(off + (size_t)std::max(n, 1) * sizeof(FinalDesc));
+  {
+    int base = 0;
+    for (ClassInfo &c : plan.classes) {
+      c.desc_base = base;
+      base += (int)c.members.size();
+    }
+  }
   const size_t es = (size_t)elem_size(plan.set.ns_dtype);
   for (ClassInfo &c : plan.classes) {
     const size_t cnt = c.members.size();
@@ -308,7 +318,11 @@ struct StageBuilder {
   hipError_t launch() {
     for (int tile : {64, 128, 256}) {
       GemmArgs args;
-      std::memset(&args, 0, sizeof(args));
+      auto reset = [&]() {
+        std::memset(&args, 0, sizeof(args));
+        for (int i = 0; i < kGemmMaxClasses; ++i) args.tile_begin[i] = INT32_MAX;
+      };
+      reset();
       double flops = 0.0;
       auto go = [&]() -> hipError_t {
         const GemmArgs a = args;
@@ -321,10 +335,10 @@ struct StageBuilder {
         if (args.nclass == kGemmMaxClasses) {
           hipError_t e = go();
           if (e != hipSuccess) return e;
-          std::memset(&args, 0, sizeof(args));
+          reset();
           flops = 0.0;
         }
-        g.tile_begin = args.total_tiles;
+        args.tile_begin[args.nclass] = args.total_tiles;
         args.cls[args.nclass++] = g;
         args.total_tiles += g.tiles_per_mat * g.count;
         flops += per_flops[c] * (double)g.count;
@@ -384,6 +398,17 @@ void set_in(GemmClass &g, char *ws, size_t cbuf, int64_t c_rows, int64_t c_ld) {
   g.ldcin = (int32_t)c_ld;
 }
 
+// Turn the iteration's last product into the fused decoupled update.
+void set_final(GemmClass &g, const Plan &plan, const ClassInfo &cl, char *ws, float lr, float wd) {
+  g.c = nullptr;
+  g.c2 = nullptr;
+  g.final_mode = 1;
+  g.desc_base = cl.desc_base;
+  g.desc = (const FinalDesc *)(ws + plan.off_desc);
+  g.lr = lr;
+  g.wd = wd;
+}
+
 #define HIP_TRY(expr)                                                                      \
   do {                                                                                     \
     hipError_t e_ = (expr);                                                                \
@@ -396,7 +421,7 @@ struct NsResult {
   double scale;     // storage scale of O
 };
 
-muon_status run_direct(const Plan &plan, char *ws, Tracer &st, double sx0, NsResult &res) {
+muon_status run_direct(const Plan &plan, char *ws, Tracer &st, double sx0, float lr, float wd, NsResult &res) {
   const size_t es = (size_t)elem_size(plan.set.ns_dtype);
   const Scaler S{plan.set.ns_dtype == kF16};
   const double d = plan.set.divisor;
@@ -454,8 +479,15 @@ muon_status run_direct(const Plan &plan, char *ws, Tracer &st, double sx0, NsRes
         set_out(g, ws, cl.XT[1 - cur], cl.Lp, cl.Sp, true);
         set_out2(g, ws, cl.X[1 - cur], cl.Sp, cl.Lp);
         set_in(g, ws, cl.XT[cur], cl.Lp, cl.Sp);
-        g.alpha = (float)(sXn * rs / (sX * sB));
-        g.beta = (float)(a * rs * sXn / sX);
+        if (k == plan.K) {
+          // last step: O in true scale goes straight into the weight update
+          set_final(g, plan, cl, ws, lr, wd);
+          g.alpha = (float)(rs / (sX * sB));
+          g.beta = (float)(a * rs / sX);
+        } else {
+          g.alpha = (float)(sXn * rs / (sX * sB));
+          g.beta = (float)(a * rs * sXn / sX);
+        }
         sb.per_class[ci] = g;
         sb.per_flops[ci] = full_flops(cl);
       }
@@ -470,7 +502,7 @@ muon_status run_direct(const Plan &plan, char *ws, Tracer &st, double sx0, NsRes
   return MUON_OK;
 }
 
-muon_status run_gram(const Plan &plan, char *ws, Tracer &st, double sx0, NsResult &res) {
+muon_status run_gram(const Plan &plan, char *ws, Tracer &st, double sx0, float lr, float wd, NsResult &res) {
   const size_t es = (size_t)elem_size(plan.set.ns_dtype);
   const Scaler S{plan.set.ns_dtype == kF16};
   const double d = plan.set.divisor;
@@ -498,14 +530,16 @@ muon_status run_gram(const Plan &plan, char *ws, Tracer &st, double sx0, NsResul
     HIP_TRY(sb.launch());
     return MUON_OK;
   };
-  // Y_new = alpha * Y Q, written as Y (tall) and X = Y^T (wide)
-  auto apply_q = [&](double extra, double out_scale) -> muon_status {
+  // Y_new = alpha * Y Q, written as Y (tall) and X = Y^T (wide); the final
+  // O = Y Q goes straight into the weight update instead
+  auto apply_q = [&](double extra, double out_scale, bool final_product = false) -> muon_status {
     StageBuilder sb(plan, ws, st);
     for (size_t ci = 0; ci < plan.classes.size(); ++ci) {
       const ClassInfo &cl = plan.classes[ci];
       GemmClass g = make_gemm(cl, es, ws, cl.XT[cur], cl.Lp, cl.Sp, cl.sq[iQ], cl.Sp, cl.Sp, cl.Sp, false);
       set_out(g, ws, cl.XT[1 - cur], cl.Lp, cl.Sp, true);
       set_out2(g, ws, cl.X[1 - cur], cl.Sp, cl.Lp);
+      if (final_product) set_final(g, plan, cl, ws, lr, wd);
       g.alpha = (float)(extra * out_scale / (sY * sQ));
       sb.per_class[ci] = g;
       sb.per_flops[ci] = full_flops(cl);
@@ -594,12 +628,11 @@ muon_status run_gram(const Plan &plan, char *ws, Tracer &st, double sx0, NsResul
     sigma = sigma_new;
   }
   if (plan.K > 0) {
-    // O = Y Q in both orientations
-    const double sO = S.pick(sigma);
-    stt = apply_q(1.0, sO);
+    // O = Y Q, fused with the weight update (true scale)
+    stt = apply_q(1.0, 1.0, true);
     if (stt != MUON_OK) return stt;
     cur = 1 - cur;
-    sY = sO;
+    sY = 1.0;
   }
   res.cur = cur;
   res.scale = sY;
@@ -661,18 +694,21 @@ muon_status muon_step(const muon_param *params, int n, float lr, float mu, float
   for (int mona = 0; mona < 2; ++mona) {
     E1Args a;
     std::memset(&a, 0, sizeof(a));
+    for (int j = 0; j < kE1MaxMats; ++j) a.begin[j] = INT32_MAX;
     a.grad_dtype = set.grad_dtype;
     a.first_step = set.step == 0 ? 1 : 0;
     a.mu = mu;
     a.beta_a = beta_a;
     a.alpha = alpha;
     a.partials = partials;
+    a.desc = (FinalDesc *)(ws + plan.off_desc);
     int blocks = 0;
     double bytes = 0.0;
     auto flush = [&]() -> muon_status {
       if (a.nmat == 0) return MUON_OK;
       HIP_TRY(tr.run(MUON_STAGE_E1, bytes, [&]() { return launch_e1(a, blocks, hs); }));
       a.nmat = 0;
+      for (int j = 0; j < kE1MaxMats; ++j) a.begin[j] = INT32_MAX;
       blocks = 0;
       bytes = 0.0;
       return MUON_OK;
@@ -689,8 +725,14 @@ muon_status muon_step(const muon_param *params, int n, float lr, float mu, float
       m.accel = params[i].accel;
       m.prev = params[i].prev_grad;
       m.numel = params[i].rows * params[i].cols;
-      m.block_begin = blocks;
+      a.begin[a.nmat - 1] = blocks;
       m.partial_off = plan.partial_off[i];
+      m.weight = params[i].weight;
+      m.ortho_out = params[i].ortho_out;
+      m.rows = (int32_t)params[i].rows;
+      m.cols = (int32_t)params[i].cols;
+      m.gamma = params[i].gamma;
+      m.desc_idx = plan.K > 0 ? plan.classes[plan.cls_of[i]].desc_base + plan.idx_in_cls[i] : -1;
       blocks += plan.e1_blocks[i];
       {
         // G read, M read+write; MONA: A read+write, G_prev written (and read after step 0)
@@ -715,6 +757,7 @@ muon_status muon_step(const muon_param *params, int n, float lr, float mu, float
     a.partials = partials;
     a.scales = scales;
     for (int i = 0; i < n; ++i) {
+      if (plan.e1_blocks[i] <= kE2InlineParts) continue;   // reduced inside E2
       if (a.nmat == kNormMaxMats) {
         HIP_TRY(tr.run(MUON_STAGE_NORM, 0.0, [&]() { return launch_norm(a, hs); }));
         a.nmat = 0;
@@ -732,8 +775,12 @@ muon_status muon_step(const muon_param *params, int n, float lr, float mu, float
   {
     E2Args a;
     std::memset(&a, 0, sizeof(a));
+    for (int j = 0; j < kE2MaxMats; ++j) a.begin[j] = INT32_MAX;
     a.ns_dtype = set.ns_dtype;
     a.scales = scales;
+    a.partials = partials;
+    a.inv_sqrt_d = (float)(1.0 / std::sqrt(set.divisor));
+    a.store_scale = (float)sx0;
     int blocks = 0;
     double bytes = 0.0;
     for (int i = 0; i < n; ++i) {
@@ -742,6 +789,7 @@ muon_status muon_step(const muon_param *params, int n, float lr, float mu, float
         a.nmat = 0;
         blocks = 0;
         bytes = 0.0;
+        for (int j = 0; j < kE2MaxMats; ++j) a.begin[j] = INT32_MAX;
       }
       const ClassInfo &cl = plan.classes[plan.cls_of[i]];
       const size_t j = (size_t)plan.idx_in_cls[i];
@@ -757,8 +805,12 @@ muon_status muon_step(const muon_param *params, int n, float lr, float mu, float
       m.ld_nat = (int32_t)pcol;
       m.ld_trn = (int32_t)prow;
       m.tiles_c = (int32_t)(pcol / kE2Tile);
-      m.tile_begin = blocks;
+      a.begin[a.nmat - 1] = blocks;
       m.scale_idx = i;
+      if (plan.e1_blocks[i] <= kE2InlineParts) {
+        m.partial_off = plan.partial_off[i];
+        m.nparts = plan.e1_blocks[i];
+      }
       blocks += (int)((prow / kE2Tile) * (pcol / kE2Tile));
       // M read (fp32), X0 written in both orientations
       bytes += (4.0 + 2.0 * (double)es) * (double)(params[i].rows * params[i].cols);
@@ -769,14 +821,17 @@ muon_status muon_step(const muon_param *params, int n, float lr, float mu, float
   // ---- Newton-Schulz
   NsResult res{0, sx0};
   if (plan.K > 0) {
-    st = (variant == MUON_NS_DIRECT) ? run_direct(plan, ws, tr, sx0, res) : run_gram(plan, ws, tr, sx0, res);
+    st = (variant == MUON_NS_DIRECT) ? run_direct(plan, ws, tr, sx0, lr, lambda, res)
+                                     : run_gram(plan, ws, tr, sx0, lr, lambda, res);
     if (st != MUON_OK) return st;
   }
 
-  // ---- E3
-  {
+  // ---- E3: only without Newton-Schulz steps (O = X0); otherwise the last
+  // product applied the update in its epilogue
+  if (plan.K == 0) {
     E3Args a;
     std::memset(&a, 0, sizeof(a));
+    for (int j = 0; j < kE3MaxMats; ++j) a.begin[j] = INT32_MAX;
     a.ns_dtype = set.ns_dtype;
     a.lr = lr;
     a.wd = lambda;
@@ -788,6 +843,7 @@ muon_status muon_step(const muon_param *params, int n, float lr, float mu, float
         a.nmat = 0;
         blocks = 0;
         bytes = 0.0;
+        for (int j = 0; j < kE3MaxMats; ++j) a.begin[j] = INT32_MAX;
       }
       const ClassInfo &cl = plan.classes[plan.cls_of[i]];
       const size_t j = (size_t)plan.idx_in_cls[i];
@@ -802,7 +858,7 @@ muon_status muon_step(const muon_param *params, int n, float lr, float mu, float
       m.ld_o = (int32_t)(wide ? cl.Lp : cl.Sp);
       m.gamma = params[i].gamma;
       m.inv_o_scale = (float)(1.0 / res.scale);
-      m.block_begin = blocks;
+      a.begin[a.nmat - 1] = blocks;
       m.vec_ok = ((params[i].cols & 3) == 0) && ((((uintptr_t)params[i].weight) | ((uintptr_t)params[i].ortho_out)) & 15) == 0;
       blocks += (int)((m.numel + kE3BlockElems - 1) / kE3BlockElems);
       // W read+write, O read (and the optional fp32 copy written)

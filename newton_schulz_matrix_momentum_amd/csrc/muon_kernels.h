@@ -10,6 +10,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <climits>
+
 namespace muon {
 
 enum DType : int32_t { kF32 = 0, kF16 = 1, kBF16 = 2 };
@@ -19,25 +21,36 @@ enum DType : int32_t { kF32 = 0, kF16 = 1, kBF16 = 2 };
 constexpr int kE1Threads = 256;
 constexpr int kE1ElemsPerThread = 32;                      // 8 groups of 4
 constexpr int kE1BlockElems = kE1Threads * kE1ElemsPerThread;  // 8192
-constexpr int kE1MaxMats = 48;
+constexpr int kE1MaxMats = 40;
 
+struct FinalDesc;
 struct E1Mat {
   const void *grad;
   float *mom;
   float *accel;     // nullptr => plain Muon
   void *prev;       // previous gradient (grad dtype); nullptr iff accel == nullptr
+  float *weight;    // for the FinalDesc written by the matrix's block 0
+  float *ortho_out;
   int64_t numel;
-  int32_t block_begin;   // first block of this matrix within the launch
   int32_t partial_off;   // index of this matrix's first partial in the workspace
+  int32_t desc_idx;      // FinalDesc slot, or -1
+  int32_t rows, cols;
+  float gamma;
+  int32_t pad;
 };
 
+// begin[i] = first block of matrix i within the launch, ascending; unused
+// entries hold INT32_MAX.  A block finds its matrix by counting entries <= its
+// index: independent scalar loads, one memory round trip.
 struct E1Args {
   int32_t nmat;
   int32_t grad_dtype;
   int32_t first_step;    // MONA: D = 0
-  int32_t vec_ok_mask_unused;
-  float mu, beta_a, alpha, pad;
+  int32_t pad0;
+  float mu, beta_a, alpha, pad1;
   double *partials;      // workspace
+  FinalDesc *desc;       // workspace
+  int32_t begin[kE1MaxMats];
   E1Mat mats[kE1MaxMats];
 };
 
@@ -59,11 +72,26 @@ struct NormArgs {
   NormMat mats[kNormMaxMats];
 };
 
+// What the last Newton-Schulz product needs to apply W <- W - lr (gamma O + wd W);
+// written by E1 (block 0 of each matrix) into the workspace.
+struct FinalDesc {
+  float *weight;
+  float *ortho_out;     // optional fp32 copy of O
+  int32_t rows, cols;
+  float gamma;
+  int32_t wide;         // rows <= cols: O is the transpose of the tall tile
+};
+
 // ------------------------------------------------------------------ E2
 // X0 = M * scale, rounded to the NS dtype, written in M's orientation
-// ("natural", zero-padded to pr x pc) and transposed (pc x pr).
+// ("natural", zero-padded to pr x pc) and transposed (pc x pr).  A matrix
+// with at most kE2InlineParts norm partials has its scale reduced inside E2
+// (every block of the matrix computes the same fixed-order sum); others read
+// the scale written by norm_kernel.
 constexpr int kE2Tile = 64;
 constexpr int kE2MaxMats = 48;
+constexpr int kE2InlineParts = 64;
+
 struct E2Mat {
   const float *mom;
   void *nat;
@@ -71,14 +99,18 @@ struct E2Mat {
   int32_t rows, cols;        // true M shape
   int32_t ld_nat, ld_trn;    // = padded cols, padded rows
   int32_t tiles_c;           // padded cols / 64
-  int32_t tile_begin;
   int32_t scale_idx;
-  int32_t pad;
+  int32_t partial_off;       // inline norm: first partial
+  int32_t nparts;            // inline norm when 0 < nparts <= kE2InlineParts
 };
 struct E2Args {
   int32_t nmat;
   int32_t ns_dtype;
+  float inv_sqrt_d;          // inline norm: 1/sqrt(divisor)
+  float store_scale;         // inline norm: storage scale of X0
   const float *scales;
+  const double *partials;
+  int32_t begin[kE2MaxMats];   // first tile of each matrix (see E1Args)
   E2Mat mats[kE2MaxMats];
 };
 
@@ -96,13 +128,14 @@ struct E3Mat {
   int32_t ld_o;
   float gamma;
   float inv_o_scale;     // 1 / storage scale of O
-  int32_t block_begin;
   int32_t vec_ok;        // 16-byte aligned and cols % 4 == 0
+  int32_t pad;
 };
 struct E3Args {
   int32_t nmat;
   int32_t ns_dtype;
   float lr, wd;
+  int32_t begin[kE3MaxMats];   // first block of each matrix (see E1Args)
   E3Mat mats[kE3MaxMats];
 };
 
@@ -125,12 +158,19 @@ struct GemmClass {
   int32_t count;
   int32_t half;
   int32_t diag_limit;              // diag term only where row == col < diag_limit
-  int32_t tile_begin;
   float alpha, beta, diag;
+  // Final product of the iteration: instead of storing C / C2, apply
+  // W <- W - lr (gamma O + wd W) through desc[desc_base + matrix]; the tile
+  // is in the tall orientation (rows index the long side).
+  int32_t final_mode;
+  int32_t desc_base;
+  const FinalDesc *desc;
+  float lr, wd;
 };
 struct GemmArgs {
   int32_t nclass;
   int32_t total_tiles;
+  int32_t tile_begin[kGemmMaxClasses];   // first tile of each class; unused = INT32_MAX
   GemmClass cls[kGemmMaxClasses];
 };
 

@@ -121,12 +121,13 @@ __device__ __forceinline__ TileRef locate_tile(const GemmArgs &args) {
   const int b = (int)blockIdx.x;
   const int per_xcd = nb / 8, rem = nb % 8, xcd = b % 8, slot = b / 8;
   const int tile = (xcd < rem ? xcd * (per_xcd + 1) : rem * (per_xcd + 1) + (xcd - rem) * per_xcd) + slot;
+  // tile_begin[] is ascending with INT32_MAX past the last class: the class
+  // index is the count of later entries <= tile (independent scalar loads)
   int ci = 0;
-#pragma unroll 1
-  for (int i = 1; i < args.nclass; ++i)
-    if (tile >= args.cls[i].tile_begin) ci = i;
+#pragma unroll
+  for (int i = 1; i < kGemmMaxClasses; ++i) ci += (args.tile_begin[i] <= tile) ? 1 : 0;
   const GemmClass &cl = args.cls[ci];
-  const int local = tile - cl.tile_begin;
+  const int local = tile - args.tile_begin[ci];
   TileRef r;
   r.ci = ci;
   r.mat = local / cl.tiles_per_mat;
@@ -147,9 +148,29 @@ __device__ __forceinline__ TileRef locate_tile(const GemmArgs &args) {
 // Epilogue for one wave's FM x FN grid of 16x16 accumulator blocks whose
 // top-left corner is (row0, col0).  MFMA 16x16 output layout: lane holds
 // rows 4*(lane/16) + r, column lane%16, r = 0..3.
+// Load the epilogue input Cin for one wave's FM x FN accumulator grid (same
+// layout as the accumulators), so its latency can overlap the main loop.
 template <typename T, int FM, int FN>
+__device__ __forceinline__ void load_cin(const GemmClass &cl, int mat, int row0, int col0, float (&cin)[FM][FN][4]) {
+  constexpr int ES = sizeof(T);
+  const int lane = threadIdx.x & 63;
+  if (!cl.cin) return;
+  const void *Cin = (const void *)((const char *)cl.cin + (int64_t)mat * cl.scin * ES);
+  const int row_base = row0 + 4 * (lane >> 4);
+  const int col_base = col0 + (lane & 15);
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        cin[i][j][r] = Store<T>::load(Cin, (int64_t)(row_base + i * 16 + r) * cl.ldcin + col_base + j * 16);
+}
+
+// PRE: Cin was prefetched into cin_pre by load_cin (else it is loaded here).
+template <typename T, int FM, int FN, bool PRE = false>
 __device__ __forceinline__ void epilogue(const GemmClass &cl, int mat, bool diag_tile, int row0, int col0,
-                                         const f32x4 (&acc)[FM][FN]) {
+                                         const f32x4 (&acc)[FM][FN], const float (&cin_pre)[FM][FN][4]) {
   constexpr int ES = sizeof(T);
   const int lane = threadIdx.x & 63;
   const float alpha = cl.alpha, beta = cl.beta, diag = cl.diag;
@@ -158,6 +179,12 @@ __device__ __forceinline__ void epilogue(const GemmClass &cl, int mat, bool diag
   const void *Cin = cl.cin ? (const void *)((const char *)cl.cin + (int64_t)mat * cl.scin * ES) : nullptr;
   const int row_base = row0 + 4 * (lane >> 4);
   const int col_base = col0 + (lane & 15);
+  FinalDesc fd{};
+  bool fvec = false;
+  if (cl.final_mode) {
+    fd = cl.desc[cl.desc_base + mat];
+    fvec = (fd.cols & 3) == 0 && ((((uintptr_t)fd.weight) | ((uintptr_t)fd.ortho_out)) & 15) == 0;
+  }
   static_for<0, FM>([&](auto ic) {
     static_for<0, FN>([&](auto jc) {
       constexpr int i = decltype(ic)::value, j = decltype(jc)::value;
@@ -167,8 +194,49 @@ __device__ __forceinline__ void epilogue(const GemmClass &cl, int mat, bool diag
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         v[r] = alpha * acc[i][j][r];
-        if (Cin) v[r] += beta * Store<T>::load(Cin, (int64_t)(r0 + r) * cl.ldcin + col);
+        if (Cin) {
+          if constexpr (PRE) v[r] += beta * cin_pre[i][j][r];
+          else v[r] += beta * Store<T>::load(Cin, (int64_t)(r0 + r) * cl.ldcin + col);
+        }
         if (diag != 0.0f && r0 + r == col && col < cl.diag_limit) v[r] += diag;
+      }
+      if (cl.final_mode) {
+        // fused decoupled update: the tile is tall (rows = long side)
+        const float lr = cl.lr, wd = cl.wd, gm = fd.gamma;
+        if (!fd.wide) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = r0 + r;
+            if (i < fd.rows && col < fd.cols) {
+              const int64_t x = (int64_t)i * fd.cols + col;
+              const float w = fd.weight[x];
+              fd.weight[x] = w - lr * (gm * v[r] + wd * w);
+              if (fd.ortho_out) fd.ortho_out[x] = v[r];
+            }
+          }
+        } else if (col < fd.rows) {
+          // W row `col`, columns r0 .. r0+3 (r0 is a multiple of 4)
+          const int64_t x = (int64_t)col * fd.cols + r0;
+          if (fvec && r0 + 4 <= fd.cols) {
+            float4 w = *(const float4 *)(fd.weight + x);
+            w.x = w.x - lr * (gm * v[0] + wd * w.x);
+            w.y = w.y - lr * (gm * v[1] + wd * w.y);
+            w.z = w.z - lr * (gm * v[2] + wd * w.z);
+            w.w = w.w - lr * (gm * v[3] + wd * w.w);
+            *(float4 *)(fd.weight + x) = w;
+            if (fd.ortho_out) *(float4 *)(fd.ortho_out + x) = make_float4(v[0], v[1], v[2], v[3]);
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              if (r0 + r < fd.cols) {
+                const float w = fd.weight[x + r];
+                fd.weight[x + r] = w - lr * (gm * v[r] + wd * w);
+                if (fd.ortho_out) fd.ortho_out[x + r] = v[r];
+              }
+            }
+          }
+        }
+        return;
       }
       if (C) {
         if (!cl.half) {
@@ -298,7 +366,8 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(GemmArgs args) {
     }
   }
 
-  epilogue<T, FM, FN>(cl, mat, cl.half && tm == tn, tm * BM + wm * WM, tn * BN + wn * WN, acc);
+  const float no_cin[FM][FN][4] = {};
+  epilogue<T, FM, FN>(cl, mat, cl.half && tm == tn, tm * BM + wm * WM, tn * BN + wn * WN, acc, no_cin);
 }
 
 
@@ -452,7 +521,8 @@ __global__ __launch_bounds__(2 * WN_WAVES * 64, 1) void ns_gemm_big_kernel(GemmA
       stage(kb + 1, by, bx);
     }
   }
-  epilogue<T, FM, FN>(cl, mat, cl.half && tm == tn, tm * kBigTile + wm * 128, tn * kBigTile + wn * WTN, acc);
+  const float no_cin[FM][FN][4] = {};
+  epilogue<T, FM, FN>(cl, mat, cl.half && tm == tn, tm * kBigTile + wm * 128, tn * kBigTile + wn * WTN, acc, no_cin);
 }
 
 // ---------------------------------------------------------------------------
@@ -467,10 +537,12 @@ constexpr int kSmallTile = 64;
 constexpr int kSmallStage = 2 * kSmallTile * kBigRowBytes;   // 8 KB
 constexpr int kSmallGroup = 4;
 
+// RING < 16 is launched only when the whole K fits in the ring (no refill);
+// RING == 16 refills and keeps at least two groups of look-ahead.
 template <typename T, int RING>
 __global__ __launch_bounds__(kThreads) void ns_gemm_small_kernel(GemmArgs args) {
   static_assert(sizeof(T) == 2, "16-bit operands only");
-  static_assert(RING % kSmallGroup == 0, "ring holds whole groups");
+  static_assert(RING < 16 || RING >= 2 * kSmallGroup, "refilling ring needs two groups of look-ahead");
   constexpr int FM = 2, FN = 2;
   __shared__ __attribute__((aligned(1024))) char lds[RING * kSmallStage];
 
@@ -502,6 +574,8 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_small_kernel(GemmArgs args) 
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float cin[FM][FN][4];
+  load_cin<T, FM, FN>(cl, mat, tm * kSmallTile + wm * 32, tn * kSmallTile + wn * 32, cin);
 
   const int nk = cl.K / (kBigRowBytes / 2);
   if (nk > 0) {
@@ -527,10 +601,12 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_small_kernel(GemmArgs args) 
       asm volatile("s_barrier" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
       // every wave is past group g-1: refill its slots with the stages RING ahead
-      if (g > 0) {
-        const int r1 = min(nk, s0 - kSmallGroup + RING + kSmallGroup);
+      if constexpr (RING >= 16) {
+        if (g > 0) {
+          const int r1 = min(nk, s0 + RING);
 #pragma unroll 1
-        for (; issued < r1; ++issued) dma(issued);
+          for (; issued < r1; ++issued) dma(issued);
+        }
       }
 #pragma unroll 1
       for (int kb = s0; kb < s1; ++kb) {
@@ -547,7 +623,8 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_small_kernel(GemmArgs args) 
       }
     }
   }
-  epilogue<T, FM, FN>(cl, mat, cl.half && tm == tn, tm * kSmallTile + wm * 32, tn * kSmallTile + wn * 32, acc);
+  epilogue<T, FM, FN, true>(cl, mat, cl.half && tm == tn, tm * kSmallTile + wm * 32, tn * kSmallTile + wn * 32, acc,
+                            cin);
 }
 
 template <typename T>
@@ -559,9 +636,14 @@ hipError_t launch_t(const GemmArgs &args, int tile, hipStream_t s) {
         int kmax = 0;
         for (int c = 0; c < args.nclass; ++c) kmax = max(kmax, args.cls[c].K);
         const int nk = kmax / (kBigRowBytes / 2);
-        if (nk <= 4) hipLaunchKernelGGL((ns_gemm_small_kernel<T, 4>), dim3(args.total_tiles), dim3(kThreads), 0, s, args);
-        else if (nk <= 8) hipLaunchKernelGGL((ns_gemm_small_kernel<T, 8>), dim3(args.total_tiles), dim3(kThreads), 0, s, args);
-        else hipLaunchKernelGGL((ns_gemm_small_kernel<T, 16>), dim3(args.total_tiles), dim3(kThreads), 0, s, args);
+        const dim3 g(args.total_tiles), b(kThreads);
+        // the ring is as small as the longest K allows, so more blocks fit per CU
+        if (nk <= 2) hipLaunchKernelGGL((ns_gemm_small_kernel<T, 2>), g, b, 0, s, args);
+        else if (nk <= 4) hipLaunchKernelGGL((ns_gemm_small_kernel<T, 4>), g, b, 0, s, args);
+        else if (nk <= 6) hipLaunchKernelGGL((ns_gemm_small_kernel<T, 6>), g, b, 0, s, args);
+        else if (nk <= 8) hipLaunchKernelGGL((ns_gemm_small_kernel<T, 8>), g, b, 0, s, args);
+        else if (nk <= 12) hipLaunchKernelGGL((ns_gemm_small_kernel<T, 12>), g, b, 0, s, args);
+        else hipLaunchKernelGGL((ns_gemm_small_kernel<T, 16>), g, b, 0, s, args);
       } else {
         hipLaunchKernelGGL((ns_gemm_kernel<T, 64, 64>), dim3(args.total_tiles), dim3(kThreads), 0, s, args);
       }
