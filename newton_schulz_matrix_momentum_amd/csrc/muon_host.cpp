@@ -45,6 +45,9 @@ muon_status fail(muon_status s, const char *fmt, ...) {
 }
 
 constexpr int kMaxSteps = 64;
+static_assert(sizeof(GemmArgs) <= 4096 && sizeof(E1Args) <= 4096 && sizeof(E2Args) <= 4096 &&
+                  sizeof(E3Args) <= 4096 && sizeof(NormArgs) <= 4096,
+              "kernel arguments must stay within 4 KB");
 constexpr int64_t kMaxDim = int64_t(1) << 20;
 constexpr int64_t kMaxNumel = (int64_t(1) << 31) - 1;
 
@@ -421,56 +424,84 @@ struct NsResult {
   double scale;     // storage scale of O
 };
 
-muon_status run_direct(const Plan &plan, char *ws, Tracer &st, double sx0, float lr, float wd, NsResult &res) {
-  const size_t es = (size_t)elem_size(plan.set.ns_dtype);
+// Scalars of the direct iteration's products, step by step, with the
+// storage scales of fp16 buffers and the restart factors folded in.  The
+// last update yields O in true scale.
+struct DirectStep {
+  double syrk_alpha;          // A = syrk_alpha X X^T   (B itself when cubic)
+  double sq_alpha, sq_beta;   // B = sq_alpha A A + sq_beta A
+  double upd_alpha, upd_beta; // X'^T = upd_alpha X^T B + upd_beta X^T
+  bool cubic;
+};
+
+std::vector<DirectStep> direct_steps(const Plan &plan, double sx0) {
   const Scaler S{plan.set.ns_dtype == kF16};
   const double d = plan.set.divisor;
   double sigma = 1.0 / std::sqrt(d);
   double sX = sx0;
-  int cur = 0;
+  std::vector<DirectStep> out;
   for (int k = 1; k <= plan.K; ++k) {
     const double a = plan.set.coeffs[3 * (k - 1)], b = plan.set.coeffs[3 * (k - 1) + 1], c = plan.set.coeffs[3 * (k - 1) + 2];
     const double rs = restart_due(k, plan.set.restart_every) ? 1.0 / std::sqrt(d) : 1.0;
     sigma *= rs;
-    const bool cubic = (c == 0.0);
+    DirectStep st{};
+    st.cubic = (c == 0.0);
     const double sA = S.pick(sigma * sigma);
     const double sB = S.pick(sup_poly(0.0, b, c, sigma, 2));
+    if (st.cubic) {
+      st.syrk_alpha = sB * b * rs * rs / (sX * sX);
+    } else {
+      st.syrk_alpha = sA * rs * rs / (sX * sX);
+      st.sq_alpha = c * sB / (sA * sA);
+      st.sq_beta = b * sB / sA;
+    }
+    const double sigma_new = sup_poly(a, b, c, sigma, 0);
+    const double sXn = (k == plan.K) ? 1.0 : S.pick(sigma_new);
+    st.upd_alpha = sXn * rs / (sX * sB);
+    st.upd_beta = a * rs * sXn / sX;
+    out.push_back(st);
+    sigma = sigma_new;
+    sX = sXn;
+  }
+  return out;
+}
+
+muon_status run_direct(const Plan &plan, char *ws, Tracer &st, double sx0, float lr, float wd, NsResult &res) {
+  const size_t es = (size_t)elem_size(plan.set.ns_dtype);
+  const std::vector<DirectStep> steps = direct_steps(plan, sx0);
+  int cur = 0;
+  for (int k = 1; k <= plan.K; ++k) {
+    const DirectStep &ds = steps[k - 1];
     // A = X X^T (or B = b X X^T directly when c == 0)
     {
       StageBuilder sb(plan, ws, st);
       for (size_t ci = 0; ci < plan.classes.size(); ++ci) {
         const ClassInfo &cl = plan.classes[ci];
         GemmClass g = make_gemm(cl, es, ws, cl.X[cur], cl.Sp, cl.Lp, cl.X[cur], cl.Sp, cl.Lp, cl.Lp, true);
-        if (cubic) {
-          set_out(g, ws, cl.sq[1], cl.Sp, cl.Sp, true);
-          g.alpha = (float)(sB * b * rs * rs / (sX * sX));
-        } else {
-          set_out(g, ws, cl.sq[0], cl.Sp, cl.Sp, true);
-          g.alpha = (float)(sA * rs * rs / (sX * sX));
-        }
+        set_out(g, ws, ds.cubic ? cl.sq[1] : cl.sq[0], cl.Sp, cl.Sp, true);
+        g.alpha = (float)ds.syrk_alpha;
         sb.per_class[ci] = g;
         sb.per_flops[ci] = half_flops(cl, cl.l);
       }
       HIP_TRY(sb.launch());
     }
     // B = b A + c A^2
-    if (!cubic) {
+    if (!ds.cubic) {
       StageBuilder sb(plan, ws, st);
       for (size_t ci = 0; ci < plan.classes.size(); ++ci) {
         const ClassInfo &cl = plan.classes[ci];
         GemmClass g = make_gemm(cl, es, ws, cl.sq[0], cl.Sp, cl.Sp, cl.sq[0], cl.Sp, cl.Sp, cl.Sp, true);
         set_out(g, ws, cl.sq[1], cl.Sp, cl.Sp, true);
         set_in(g, ws, cl.sq[0], cl.Sp, cl.Sp);
-        g.alpha = (float)(c * sB / (sA * sA));
-        g.beta = (float)(b * sB / sA);
+        g.alpha = (float)ds.sq_alpha;
+        g.beta = (float)ds.sq_beta;
         sb.per_class[ci] = g;
         sb.per_flops[ci] = half_flops(cl, cl.s);
       }
       HIP_TRY(sb.launch());
     }
-    // X^T <- a X^T + X^T B, also written transposed into X
-    const double sigma_new = sup_poly(a, b, c, sigma, 0);
-    const double sXn = S.pick(sigma_new);
+    // X^T <- a X^T + X^T B, also written transposed into X; the last step's
+    // O (true scale) goes straight into the weight update
     {
       StageBuilder sb(plan, ws, st);
       for (size_t ci = 0; ci < plan.classes.size(); ++ci) {
@@ -479,26 +510,18 @@ muon_status run_direct(const Plan &plan, char *ws, Tracer &st, double sx0, float
         set_out(g, ws, cl.XT[1 - cur], cl.Lp, cl.Sp, true);
         set_out2(g, ws, cl.X[1 - cur], cl.Sp, cl.Lp);
         set_in(g, ws, cl.XT[cur], cl.Lp, cl.Sp);
-        if (k == plan.K) {
-          // last step: O in true scale goes straight into the weight update
-          set_final(g, plan, cl, ws, lr, wd);
-          g.alpha = (float)(rs / (sX * sB));
-          g.beta = (float)(a * rs / sX);
-        } else {
-          g.alpha = (float)(sXn * rs / (sX * sB));
-          g.beta = (float)(a * rs * sXn / sX);
-        }
+        if (k == plan.K) set_final(g, plan, cl, ws, lr, wd);
+        g.alpha = (float)ds.upd_alpha;
+        g.beta = (float)ds.upd_beta;
         sb.per_class[ci] = g;
         sb.per_flops[ci] = full_flops(cl);
       }
       HIP_TRY(sb.launch());
     }
     cur = 1 - cur;
-    sigma = sigma_new;
-    sX = sXn;
   }
   res.cur = cur;
-  res.scale = sX;
+  res.scale = 1.0;
   return MUON_OK;
 }
 
@@ -651,6 +674,7 @@ void muon_options_init(muon_options *o) {
   o->divisor = 1.0f;
   o->restart_every = 0;
   o->step = 0;
+  o->trace = nullptr;
 }
 
 size_t muon_workspace_size(const muon_param *params, int n, int ns_steps, muon_variant variant,

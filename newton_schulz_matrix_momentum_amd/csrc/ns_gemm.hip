@@ -145,9 +145,6 @@ __device__ __forceinline__ TileRef locate_tile(const GemmArgs &args) {
   return r;
 }
 
-// Epilogue for one wave's FM x FN grid of 16x16 accumulator blocks whose
-// top-left corner is (row0, col0).  MFMA 16x16 output layout: lane holds
-// rows 4*(lane/16) + r, column lane%16, r = 0..3.
 // Load the epilogue input Cin for one wave's FM x FN accumulator grid (same
 // layout as the accumulators), so its latency can overlap the main loop.
 template <typename T, int FM, int FN>
@@ -167,6 +164,10 @@ __device__ __forceinline__ void load_cin(const GemmClass &cl, int mat, int row0,
         cin[i][j][r] = Store<T>::load(Cin, (int64_t)(row_base + i * 16 + r) * cl.ldcin + col_base + j * 16);
 }
 
+// Direct epilogue for latency-bound small tiles: each lane stores its own
+// accumulator values (MFMA 16x16 layout: rows 4 (lane / 16) + r, column
+// lane % 16) straight to global memory, with no LDS hand-off.  Same results
+// as epilogue_lds.  Top-left corner of the wave's grid: (row0, col0).
 // PRE: Cin was prefetched into cin_pre by load_cin (else it is loaded here).
 template <typename T, int FM, int FN, bool PRE = false>
 __device__ __forceinline__ void epilogue(const GemmClass &cl, int mat, bool diag_tile, int row0, int col0,
@@ -259,6 +260,207 @@ __device__ __forceinline__ void epilogue(const GemmClass &cl, int mat, bool diag
       if (C2) Store<T>::store4(C2, (int64_t)col * cl.ldc2 + r0, v);
     });
   });
+}
+
+// s_waitcnt lgkmcnt(0) (LDS and scalar memory), vmcnt and expcnt untouched.
+#define MUON_LGKM0 (0xF | (0x7 << 4) | (0x3 << 14))
+
+// Barrier for LDS hand-offs inside the epilogue: this wave's LDS accesses
+// have completed, then s_barrier.  No memory fence, so global stores already
+// issued stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(MUON_LGKM0);
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Floats of LDS the epilogue of a BM x BN block tile needs (bands of HB
+// rows, stored row-major and transposed, rows padded by 4 floats).
+template <int HB, int BN>
+constexpr int epilogue_lds_floats() {
+  return HB * (BN + 4) + BN * (HB + 4);
+}
+
+// One 16-byte chunk of the result read from an LDS band (16-byte aligned)
+// and stored to global memory as T.
+template <typename T> struct Pack;
+template <> struct Pack<float> {
+  static __device__ __forceinline__ void copy(float *dst, const float *src) {
+    *(float4 *)dst = *(const float4 *)src;
+  }
+};
+template <typename H> struct Pack16 {
+  static __device__ __forceinline__ uint32_t pair(float a, float b) {
+    return (uint32_t)Store16<H>::bits(a) | ((uint32_t)Store16<H>::bits(b) << 16);
+  }
+  static __device__ __forceinline__ void copy(H *dst, const float *src) {
+    const float4 a = *(const float4 *)src, b = *(const float4 *)(src + 4);
+    u32x4 u;
+    u.x = pair(a.x, a.y);
+    u.y = pair(a.z, a.w);
+    u.z = pair(b.x, b.y);
+    u.w = pair(b.z, b.w);
+    *(u32x4 *)dst = u;
+  }
+};
+template <> struct Pack<__bf16> : Pack16<__bf16> {};
+template <> struct Pack<_Float16> : Pack16<_Float16> {};
+
+// Epilogue of one BM x BN block tile (NT threads; wave tiles of FM x FN
+// 16 x 16 accumulator blocks with block-local origin (wrow, wcol)):
+//   v = alpha * acc + beta * Cin + diag * [row == col < diag_limit]
+// computed in the MFMA layout (lane holds rows 4 (lane / 16) + r, column
+// lane % 16), then handed through LDS in bands of HB rows, each written
+// row-major and transposed, so that every global store is a 16-byte vector
+// along a row of its destination: C, the mirrored tile of a symmetric
+// product (upper-triangular tiles only; a diagonal tile keeps its upper
+// triangle and mirrors it), the transposed copy C2, or in final mode the fp32
+// decoupled update of W (row-major for tall W, transposed for wide W).
+// PRE: Cin was prefetched into cin_pre by load_cin (else it is loaded here).
+// On entry every wave must be done reading LDS for the main loop.
+template <typename T, int BM, int BN, int HB, int NT, int FM, int FN, bool PRE>
+__device__ __forceinline__ void epilogue_lds(const GemmClass &cl, int mat, int tm, int tn, int wrow, int wcol,
+                                             f32x4 (&acc)[FM][FN], const float (&cin_pre)[FM][FN][4], float *lds) {
+  static_assert(BM % HB == 0 && HB % 16 == 0, "bands hold whole 16-row blocks");
+  constexpr int ES = sizeof(T);
+  constexpr int CE = 16 / ES;                 // elements per 16-byte store
+  constexpr int PR = BN + 4, PT = HB + 4;     // pitches (floats) of the two copies
+  float *lr = lds;                            // HB x PR, row-major band
+  float *lt = lds + HB * PR;                  // BN x PT, transposed band
+  const int lane = threadIdx.x & 63;
+  const int tid = threadIdx.x;
+  const int row0 = tm * BM, col0 = tn * BN;   // block tile origin in the result
+  const float alpha = cl.alpha, beta = cl.beta, diag = cl.diag;
+  const void *Cin = cl.cin ? (const void *)((const char *)cl.cin + (int64_t)mat * cl.scin * ES) : nullptr;
+  // v in place of the accumulators
+  {
+    const int rb = row0 + wrow + 4 * (lane >> 4);
+    const int cb = col0 + wcol + (lane & 15);
+    static_for<0, FM>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int col = cb + j * 16;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = rb + i * 16 + r;
+          float v = alpha * acc[i][j][r];
+          if (Cin) {
+            if constexpr (PRE) v += beta * cin_pre[i][j][r];
+            else v += beta * Store<T>::load(Cin, (int64_t)row * cl.ldcin + col);
+          }
+          if (diag != 0.0f && row == col && col < cl.diag_limit) v += diag;
+          acc[i][j][r] = v;
+        }
+      }
+    });
+  }
+  const bool diag_tile = cl.half && tm == tn;
+  FinalDesc fd{};
+  bool fvec = false;
+  if (cl.final_mode) {
+    fd = cl.desc[cl.desc_base + mat];
+    fvec = (fd.cols & 3) == 0 && ((((uintptr_t)fd.weight) | ((uintptr_t)fd.ortho_out)) & 15) == 0;
+  }
+  const bool need_r = cl.final_mode ? !fd.wide : (cl.c != nullptr);
+  const bool need_t = cl.final_mode ? (fd.wide != 0) : (cl.half ? cl.c != nullptr : cl.c2 != nullptr);
+  T *C = cl.c ? (T *)((char *)cl.c + (int64_t)mat * cl.sc * ES) : nullptr;
+  T *C2 = cl.c2 ? (T *)((char *)cl.c2 + (int64_t)mat * cl.sc2 * ES) : nullptr;
+
+#pragma unroll 1
+  for (int p = 0; p < BM / HB; ++p) {
+    lds_barrier();   // previous band (or the main loop) is done with LDS
+    static_for<0, FM>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      const int rloc = wrow + i * 16 - p * HB;   // band-local first row of block i
+      if (rloc >= 0 && rloc < HB) {
+        const int rr = rloc + 4 * (lane >> 4);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int c = wcol + j * 16 + (lane & 15);
+          if (need_r) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) lr[(rr + r) * PR + c] = acc[i][j][r];
+          }
+          if (need_t) *(float4 *)&lt[c * PT + rr] = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+        }
+      }
+    });
+    lds_barrier();
+    const int brow = p * HB;   // block-local first row of the band
+    if (cl.final_mode) {
+      const float lrate = cl.lr, wd = cl.wd, gm = fd.gamma;
+      // tall: W rows are block rows; wide: W rows are block columns
+      const int n_inner = fd.wide ? HB / 4 : BN / 4;
+#pragma unroll 1
+      for (int q = tid; q < HB * BN / 4; q += NT) {
+        const int outer = q / n_inner, inner = (q - outer * n_inner) * 4;
+        const float *src = fd.wide ? &lt[outer * PT + inner] : &lr[outer * PR + inner];
+        const int wr = fd.wide ? col0 + outer : row0 + brow + outer;
+        const int wc = fd.wide ? row0 + brow + inner : col0 + inner;
+        if (wr >= fd.rows || wc >= fd.cols) continue;
+        const float4 o = *(const float4 *)src;
+        const int64_t x = (int64_t)wr * fd.cols + wc;
+        if (fvec) {   // cols % 4 == 0, so wc + 4 <= cols
+          float4 w = *(const float4 *)(fd.weight + x);
+          w.x = w.x - lrate * (gm * o.x + wd * w.x);
+          w.y = w.y - lrate * (gm * o.y + wd * w.y);
+          w.z = w.z - lrate * (gm * o.z + wd * w.z);
+          w.w = w.w - lrate * (gm * o.w + wd * w.w);
+          *(float4 *)(fd.weight + x) = w;
+          if (fd.ortho_out) *(float4 *)(fd.ortho_out + x) = o;
+        } else {
+          const float ov[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (wc + e < fd.cols) {
+              const float w = fd.weight[x + e];
+              fd.weight[x + e] = w - lrate * (gm * ov[e] + wd * w);
+              if (fd.ortho_out) fd.ortho_out[x + e] = ov[e];
+            }
+          }
+        }
+      }
+      continue;
+    }
+    // row-major copy -> C rows
+    if (C) {
+#pragma unroll 1
+      for (int q = tid; q < HB * BN / CE; q += NT) {
+        const int r = q / (BN / CE), c = (q - r * (BN / CE)) * CE;
+        const float *src = &lr[r * PR + c];
+        T *dst = C + (int64_t)(row0 + brow + r) * cl.ldc + col0 + c;
+        const int R = brow + r;   // block-local row
+        if (!diag_tile || c >= R) {
+          Pack<T>::copy(dst, src);
+        } else if (c + CE > R) {   // the chunk crossing the diagonal: upper part only
+#pragma unroll
+          for (int e = 0; e < CE; ++e)
+            if (c + e >= R) Store<T>::store(dst, e, src[e]);
+        }
+      }
+    }
+    // transposed copy -> mirror of a symmetric tile, or C2
+    T *Ct = cl.half ? C : C2;
+    const int ldt = cl.half ? cl.ldc : cl.ldc2;
+    if (Ct) {
+#pragma unroll 1
+      for (int q = tid; q < BN * HB / CE; q += NT) {
+        const int c = q / (HB / CE), rr = (q - c * (HB / CE)) * CE;
+        const float *src = &lt[c * PT + rr];
+        T *dst = Ct + (int64_t)(col0 + c) * ldt + row0 + brow + rr;
+        const int R0 = brow + rr;   // block-local row of the chunk's first element
+        if (!diag_tile || c >= R0 + CE - 1) {
+          Pack<T>::copy(dst, src);
+        } else if (c >= R0) {       // mirror only the upper-triangular sources
+#pragma unroll
+          for (int e = 0; e < CE; ++e)
+            if (c >= R0 + e) Store<T>::store(dst, e, src[e]);
+        }
+      }
+    }
+  }
 }
 
 constexpr int kThreads = 256;
@@ -366,8 +568,13 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(GemmArgs args) {
     }
   }
 
+  static_assert(epilogue_lds_floats<64, BN>() * 4 <= (int)sizeof(lds), "epilogue bands must fit the LDS stages");
   const float no_cin[FM][FN][4] = {};
-  epilogue<T, FM, FN>(cl, mat, cl.half && tm == tn, tm * BM + wm * WM, tn * BN + wn * WN, acc, no_cin);
+  if constexpr (BM == 64)   // latency-bound small tiles: no LDS hand-off
+    epilogue<T, FM, FN>(cl, mat, cl.half && tm == tn, tm * BM + wm * WM, tn * BN + wn * WN, acc, no_cin);
+  else
+    epilogue_lds<T, BM, BN, 64, kThreads, FM, FN, false>(cl, mat, tm, tn, wm * WM, wn * WN, acc, no_cin,
+                                                         (float *)&lds[0][0]);
 }
 
 
@@ -410,7 +617,9 @@ __global__ __launch_bounds__(2 * WN_WAVES * 64, 1) void ns_gemm_big_kernel(GemmA
   constexpr int WTN = kBigTile / WN_WAVES;       // wave tile columns
   constexpr int FM = 8, FN = WTN / 16;           // 128 x WTN per wave
   constexpr int DMA_PER_WAVE = 16 / NWAVES;      // 1 KB DMA instructions per operand per stage
-  __shared__ __attribute__((aligned(1024))) char lds[kBigRing * kBigStage];
+  constexpr int kLdsBytes = kBigRing * kBigStage > epilogue_lds_floats<64, kBigTile>() * 4
+                                ? kBigRing * kBigStage : epilogue_lds_floats<64, kBigTile>() * 4;
+  __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
 
   const TileRef tr = locate_tile(args);
   const GemmClass &cl = args.cls[tr.ci];
@@ -522,7 +731,8 @@ __global__ __launch_bounds__(2 * WN_WAVES * 64, 1) void ns_gemm_big_kernel(GemmA
     }
   }
   const float no_cin[FM][FN][4] = {};
-  epilogue<T, FM, FN>(cl, mat, cl.half && tm == tn, tm * kBigTile + wm * 128, tn * kBigTile + wn * WTN, acc, no_cin);
+  epilogue_lds<T, kBigTile, kBigTile, 64, NWAVES * 64, FM, FN, false>(cl, mat, tm, tn, wm * 128, wn * WTN, acc, no_cin,
+                                                                     (float *)lds);
 }
 
 // ---------------------------------------------------------------------------
