@@ -275,65 +275,83 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Floats of LDS the epilogue of a BM x BN block tile needs (bands of HB
-// rows, stored row-major and transposed, rows padded by 4 floats).
+// Floats of LDS the epilogue of a BM x BN block tile needs: a band of HB
+// rows stored row-major (rows padded by 4 floats) and transposed.
 template <int HB, int BN>
 constexpr int epilogue_lds_floats() {
-  return HB * (BN + 4) + BN * (HB + 4);
+  return HB * (BN + 4) + BN * HB;
 }
 
-// One 16-byte chunk of the result read from an LDS band (16-byte aligned)
-// and stored to global memory as T.
+// One 16-byte chunk of the result, from 16-byte aligned floats, stored to
+// global memory as T.
 template <typename T> struct Pack;
 template <> struct Pack<float> {
-  static __device__ __forceinline__ void copy(float *dst, const float *src) {
-    *(float4 *)dst = *(const float4 *)src;
-  }
+  static __device__ __forceinline__ void copy(float *dst, const float4 *src) { *(float4 *)dst = src[0]; }
 };
 template <typename H> struct Pack16 {
   static __device__ __forceinline__ uint32_t pair(float a, float b) {
     return (uint32_t)Store16<H>::bits(a) | ((uint32_t)Store16<H>::bits(b) << 16);
   }
-  static __device__ __forceinline__ void copy(H *dst, const float *src) {
-    const float4 a = *(const float4 *)src, b = *(const float4 *)(src + 4);
+  static __device__ __forceinline__ void copy(H *dst, const float4 *src) {
     u32x4 u;
-    u.x = pair(a.x, a.y);
-    u.y = pair(a.z, a.w);
-    u.z = pair(b.x, b.y);
-    u.w = pair(b.z, b.w);
+    u.x = pair(src[0].x, src[0].y);
+    u.y = pair(src[0].z, src[0].w);
+    u.z = pair(src[1].x, src[1].y);
+    u.w = pair(src[1].z, src[1].w);
     *(u32x4 *)dst = u;
   }
 };
 template <> struct Pack<__bf16> : Pack16<__bf16> {};
 template <> struct Pack<_Float16> : Pack16<_Float16> {};
 
+__device__ __forceinline__ float elem(const float4 *v, int e) {
+  const float4 x = v[e >> 2];
+  return (e & 3) == 0 ? x.x : (e & 3) == 1 ? x.y : (e & 3) == 2 ? x.z : x.w;
+}
+
+// Offset of (column c, band row r) in the transposed band: rows are stored
+// in groups of 4 (one float4), and the groups of column c are permuted by
+// (c / 8) % 8 so that float4 accesses of 8 consecutive 8-column chunks at one
+// row group fall into distinct banks.
+template <int HB>
+__device__ __forceinline__ int tpos(int c, int r) {
+  return c * HB + 4 * ((r >> 2) ^ ((c >> 3) & 7)) + (r & 3);
+}
+
 // Epilogue of one BM x BN block tile (NT threads; wave tiles of FM x FN
 // 16 x 16 accumulator blocks with block-local origin (wrow, wcol)):
 //   v = alpha * acc + beta * Cin + diag * [row == col < diag_limit]
-// computed in the MFMA layout (lane holds rows 4 (lane / 16) + r, column
-// lane % 16), then handed through LDS in bands of HB rows, each written
-// row-major and transposed, so that every global store is a 16-byte vector
-// along a row of its destination: C, the mirrored tile of a symmetric
-// product (upper-triangular tiles only; a diagonal tile keeps its upper
-// triangle and mirrors it), the transposed copy C2, or in final mode the fp32
-// decoupled update of W (row-major for tall W, transposed for wide W).
-// PRE: Cin was prefetched into cin_pre by load_cin (else it is loaded here).
-// On entry every wave must be done reading LDS for the main loop.
-template <typename T, int BM, int BN, int HB, int NT, int FM, int FN, bool PRE>
+// handed through LDS in bands of HB rows so that every global access is a
+// 16-byte vector along a row.  Per band: the waves write alpha * acc (+ diag)
+// from the MFMA layout (lane holds rows 4 (lane / 16) + r, column lane % 16)
+// into a row-major copy; a row-major sweep, in units of 4 rows x 16 bytes,
+// adds beta * Cin (read as 16-byte chunks in C's orientation), stores C rows
+// and fills the transposed copy; a transposed sweep stores the mirrored tile
+// of a symmetric product (upper-triangular tiles only; a diagonal tile keeps
+// its upper triangle and mirrors it) or the transposed copy C2.  In final
+// mode the sweeps apply the fp32 decoupled update of W instead: row-major for
+// tall W, transposed for wide W.  On entry every wave must be done reading
+// LDS for the main loop.
+template <typename T, int BM, int BN, int HB, int NT, int FM, int FN>
 __device__ __forceinline__ void epilogue_lds(const GemmClass &cl, int mat, int tm, int tn, int wrow, int wcol,
-                                             f32x4 (&acc)[FM][FN], const float (&cin_pre)[FM][FN][4], float *lds) {
-  static_assert(BM % HB == 0 && HB % 16 == 0, "bands hold whole 16-row blocks");
+                                             f32x4 (&acc)[FM][FN], float *lds) {
+  static_assert(BM % HB == 0 && HB % 16 == 0 && HB >= 32 && HB <= 64, "bands hold whole 16-row blocks");
   constexpr int ES = sizeof(T);
-  constexpr int CE = 16 / ES;                 // elements per 16-byte store
-  constexpr int PR = BN + 4, PT = HB + 4;     // pitches (floats) of the two copies
+  constexpr int CE = 16 / ES;                 // elements per 16-byte chunk
+  constexpr int CQ = CE / 4;                  // float4 per chunk
+  constexpr int PR = BN + 4;                  // row-major pitch (floats)
+  constexpr int CPR = BN / CE;                // chunks per row
+  constexpr int UNITS = (HB / 4) * CPR;       // 4-row units per band
+  static_assert(UNITS % NT == 0, "every thread takes the same number of units");
+  constexpr int NU = UNITS / NT;
   float *lr = lds;                            // HB x PR, row-major band
-  float *lt = lds + HB * PR;                  // BN x PT, transposed band
+  float *lt = lds + HB * PR;                  // BN x HB, transposed band (tpos)
   const int lane = threadIdx.x & 63;
   const int tid = threadIdx.x;
   const int row0 = tm * BM, col0 = tn * BN;   // block tile origin in the result
   const float alpha = cl.alpha, beta = cl.beta, diag = cl.diag;
-  const void *Cin = cl.cin ? (const void *)((const char *)cl.cin + (int64_t)mat * cl.scin * ES) : nullptr;
-  // v in place of the accumulators
+  const T *Cin = cl.cin ? (const T *)((const char *)cl.cin + (int64_t)mat * cl.scin * ES) : nullptr;
+  // alpha * acc + diag in place
   {
     const int rb = row0 + wrow + 4 * (lane >> 4);
     const int cb = col0 + wcol + (lane & 15);
@@ -344,13 +362,8 @@ __device__ __forceinline__ void epilogue_lds(const GemmClass &cl, int mat, int t
         const int col = cb + j * 16;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int row = rb + i * 16 + r;
           float v = alpha * acc[i][j][r];
-          if (Cin) {
-            if constexpr (PRE) v += beta * cin_pre[i][j][r];
-            else v += beta * Store<T>::load(Cin, (int64_t)row * cl.ldcin + col);
-          }
-          if (diag != 0.0f && row == col && col < cl.diag_limit) v += diag;
+          if (diag != 0.0f && rb + i * 16 + r == col && col < cl.diag_limit) v += diag;
           acc[i][j][r] = v;
         }
       }
@@ -363,101 +376,153 @@ __device__ __forceinline__ void epilogue_lds(const GemmClass &cl, int mat, int t
     fd = cl.desc[cl.desc_base + mat];
     fvec = (fd.cols & 3) == 0 && ((((uintptr_t)fd.weight) | ((uintptr_t)fd.ortho_out)) & 15) == 0;
   }
-  const bool need_r = cl.final_mode ? !fd.wide : (cl.c != nullptr);
-  const bool need_t = cl.final_mode ? (fd.wide != 0) : (cl.half ? cl.c != nullptr : cl.c2 != nullptr);
   T *C = cl.c ? (T *)((char *)cl.c + (int64_t)mat * cl.sc * ES) : nullptr;
   T *C2 = cl.c2 ? (T *)((char *)cl.c2 + (int64_t)mat * cl.sc2 * ES) : nullptr;
+  T *Ct = cl.half ? C : C2;                   // destination of the transposed sweep
+  const int ldt = cl.half ? cl.ldc : cl.ldc2;
+  const bool out_r = cl.final_mode ? !fd.wide : (C != nullptr);    // row-major sweep stores
+  const bool out_t = cl.final_mode ? (fd.wide != 0) : (Ct != nullptr);
+  // the MFMA layout fills the transposed copy directly unless beta * Cin must
+  // be added first (then the row-major sweep fills it)
+  const bool direct_t = out_t && !Cin;
+  const float lrate = cl.lr, wd = cl.wd, gm = fd.gamma;
+
+  // W <- W - lr (gamma o + wd W) for 4 consecutive elements of W's row wr
+  auto update_w = [&](int wr, int wc, const float4 o4) {
+    if (wr >= fd.rows || wc >= fd.cols) return;
+    const float o[4] = {o4.x, o4.y, o4.z, o4.w};
+    const int64_t x = (int64_t)wr * fd.cols + wc;
+    if (fvec) {   // cols % 4 == 0, so wc + 4 <= cols
+      float4 w = *(const float4 *)(fd.weight + x);
+      w.x = w.x - lrate * (gm * o[0] + wd * w.x);
+      w.y = w.y - lrate * (gm * o[1] + wd * w.y);
+      w.z = w.z - lrate * (gm * o[2] + wd * w.z);
+      w.w = w.w - lrate * (gm * o[3] + wd * w.w);
+      *(float4 *)(fd.weight + x) = w;
+      if (fd.ortho_out) *(float4 *)(fd.ortho_out + x) = o4;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (wc + e < fd.cols) {
+          const float w = fd.weight[x + e];
+          fd.weight[x + e] = w - lrate * (gm * o[e] + wd * w);
+          if (fd.ortho_out) fd.ortho_out[x + e] = o[e];
+        }
+      }
+    }
+  };
 
 #pragma unroll 1
   for (int p = 0; p < BM / HB; ++p) {
+    const int brow = p * HB;   // block-local first row of the band
+    // this thread's Cin chunks for the band, issued before the LDS hand-off
+    u32x4 cinv[NU][4];
+    if (Cin) {
+#pragma unroll
+      for (int k = 0; k < NU; ++k) {
+        const int u = tid + k * NT;
+        const int rg = u / CPR, c = (u - rg * CPR) * CE;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          cinv[k][i] = *(const u32x4 *)(Cin + (int64_t)(row0 + brow + 4 * rg + i) * cl.ldcin + col0 + c);
+      }
+    }
     lds_barrier();   // previous band (or the main loop) is done with LDS
     static_for<0, FM>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
-      const int rloc = wrow + i * 16 - p * HB;   // band-local first row of block i
+      const int rloc = wrow + i * 16 - brow;   // band-local first row of block i
       if (rloc >= 0 && rloc < HB) {
         const int rr = rloc + 4 * (lane >> 4);
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           const int c = wcol + j * 16 + (lane & 15);
-          if (need_r) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) lr[(rr + r) * PR + c] = acc[i][j][r];
-          }
-          if (need_t) *(float4 *)&lt[c * PT + rr] = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+          for (int r = 0; r < 4; ++r) lr[(rr + r) * PR + c] = acc[i][j][r];
+          if (direct_t) *(float4 *)&lt[tpos<HB>(c, rr)] = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
         }
       }
     });
     lds_barrier();
-    const int brow = p * HB;   // block-local first row of the band
-    if (cl.final_mode) {
-      const float lrate = cl.lr, wd = cl.wd, gm = fd.gamma;
-      // tall: W rows are block rows; wide: W rows are block columns
-      const int n_inner = fd.wide ? HB / 4 : BN / 4;
-#pragma unroll 1
-      for (int q = tid; q < HB * BN / 4; q += NT) {
-        const int outer = q / n_inner, inner = (q - outer * n_inner) * 4;
-        const float *src = fd.wide ? &lt[outer * PT + inner] : &lr[outer * PR + inner];
-        const int wr = fd.wide ? col0 + outer : row0 + brow + outer;
-        const int wc = fd.wide ? row0 + brow + inner : col0 + inner;
-        if (wr >= fd.rows || wc >= fd.cols) continue;
-        const float4 o = *(const float4 *)src;
-        const int64_t x = (int64_t)wr * fd.cols + wc;
-        if (fvec) {   // cols % 4 == 0, so wc + 4 <= cols
-          float4 w = *(const float4 *)(fd.weight + x);
-          w.x = w.x - lrate * (gm * o.x + wd * w.x);
-          w.y = w.y - lrate * (gm * o.y + wd * w.y);
-          w.z = w.z - lrate * (gm * o.z + wd * w.z);
-          w.w = w.w - lrate * (gm * o.w + wd * w.w);
-          *(float4 *)(fd.weight + x) = w;
-          if (fd.ortho_out) *(float4 *)(fd.ortho_out + x) = o;
-        } else {
-          const float ov[4] = {o.x, o.y, o.z, o.w};
+    // row-major sweep: units of 4 rows x one 16-byte chunk
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if (wc + e < fd.cols) {
-              const float w = fd.weight[x + e];
-              fd.weight[x + e] = w - lrate * (gm * ov[e] + wd * w);
-              if (fd.ortho_out) fd.ortho_out[x + e] = ov[e];
-            }
+    for (int k = 0; k < NU; ++k) {
+      const int u = tid + k * NT;
+      const int rg = u / CPR, c = (u - rg * CPR) * CE;
+      float4 v[4][CQ];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int h = 0; h < CQ; ++h) v[i][h] = *(const float4 *)&lr[(4 * rg + i) * PR + c + 4 * h];
+      if (Cin) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const u32x4 w = cinv[k][i];
+          if constexpr (ES == 4) {
+            v[i][0].x += beta * __uint_as_float(w.x);
+            v[i][0].y += beta * __uint_as_float(w.y);
+            v[i][0].z += beta * __uint_as_float(w.z);
+            v[i][0].w += beta * __uint_as_float(w.w);
+          } else {
+            auto lo = [](uint32_t x) { return (float)__builtin_bit_cast(T, (uint16_t)(x & 0xFFFFu)); };
+            auto hi = [](uint32_t x) { return (float)__builtin_bit_cast(T, (uint16_t)(x >> 16)); };
+            v[i][0].x += beta * lo(w.x);
+            v[i][0].y += beta * hi(w.x);
+            v[i][0].z += beta * lo(w.y);
+            v[i][0].w += beta * hi(w.y);
+            v[i][1].x += beta * lo(w.z);
+            v[i][1].y += beta * hi(w.z);
+            v[i][1].z += beta * lo(w.w);
+            v[i][1].w += beta * hi(w.w);
           }
         }
+        if (out_t) {   // column c + e, rows 4 rg .. 4 rg + 3
+#pragma unroll
+          for (int e = 0; e < CE; ++e)
+            *(float4 *)&lt[tpos<HB>(c + e, 4 * rg)] =
+                make_float4(elem(v[0], e), elem(v[1], e), elem(v[2], e), elem(v[3], e));
+        }
       }
-      continue;
-    }
-    // row-major copy -> C rows
-    if (C) {
-#pragma unroll 1
-      for (int q = tid; q < HB * BN / CE; q += NT) {
-        const int r = q / (BN / CE), c = (q - r * (BN / CE)) * CE;
-        const float *src = &lr[r * PR + c];
-        T *dst = C + (int64_t)(row0 + brow + r) * cl.ldc + col0 + c;
-        const int R = brow + r;   // block-local row
+      if (!out_r) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int R = brow + 4 * rg + i;   // block-local row
+        if (cl.final_mode) {
+#pragma unroll
+          for (int h = 0; h < CQ; ++h) update_w(row0 + R, col0 + c + 4 * h, v[i][h]);
+          continue;
+        }
+        T *dst = C + (int64_t)(row0 + R) * cl.ldc + col0 + c;
         if (!diag_tile || c >= R) {
-          Pack<T>::copy(dst, src);
+          Pack<T>::copy(dst, v[i]);
         } else if (c + CE > R) {   // the chunk crossing the diagonal: upper part only
 #pragma unroll
           for (int e = 0; e < CE; ++e)
-            if (c + e >= R) Store<T>::store(dst, e, src[e]);
+            if (c + e >= R) Store<T>::store(dst, e, elem(v[i], e));
         }
       }
     }
-    // transposed copy -> mirror of a symmetric tile, or C2
-    T *Ct = cl.half ? C : C2;
-    const int ldt = cl.half ? cl.ldc : cl.ldc2;
-    if (Ct) {
+    if (!out_t) continue;
+    if (!direct_t) lds_barrier();   // the transposed copy was filled by the sweep above
+    // transposed sweep: chunks of CE band rows of one column
 #pragma unroll 1
-      for (int q = tid; q < BN * HB / CE; q += NT) {
-        const int c = q / (HB / CE), rr = (q - c * (HB / CE)) * CE;
-        const float *src = &lt[c * PT + rr];
-        T *dst = Ct + (int64_t)(col0 + c) * ldt + row0 + brow + rr;
-        const int R0 = brow + rr;   // block-local row of the chunk's first element
-        if (!diag_tile || c >= R0 + CE - 1) {
-          Pack<T>::copy(dst, src);
-        } else if (c >= R0) {       // mirror only the upper-triangular sources
+    for (int q = tid; q < BN * HB / CE; q += NT) {
+      const int c = q / (HB / CE), rr = (q - c * (HB / CE)) * CE;
+      float4 src[CQ];
 #pragma unroll
-          for (int e = 0; e < CE; ++e)
-            if (c >= R0 + e) Store<T>::store(dst, e, src[e]);
-        }
+      for (int h = 0; h < CQ; ++h) src[h] = *(const float4 *)&lt[tpos<HB>(c, rr + 4 * h)];
+      if (cl.final_mode) {
+#pragma unroll
+        for (int h = 0; h < CQ; ++h) update_w(col0 + c, row0 + brow + rr + 4 * h, src[h]);
+        continue;
+      }
+      T *dst = Ct + (int64_t)(col0 + c) * ldt + row0 + brow + rr;
+      const int R0 = brow + rr;   // block-local row of the chunk's first element
+      if (!diag_tile || c >= R0 + CE - 1) {
+        Pack<T>::copy(dst, src);
+      } else if (c >= R0) {       // mirror only the upper-triangular sources
+#pragma unroll
+        for (int e = 0; e < CE; ++e)
+          if (c >= R0 + e) Store<T>::store(dst, e, elem(src, e));
       }
     }
   }
@@ -573,8 +638,7 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(GemmArgs args) {
   if constexpr (BM == 64)   // latency-bound small tiles: no LDS hand-off
     epilogue<T, FM, FN>(cl, mat, cl.half && tm == tn, tm * BM + wm * WM, tn * BN + wn * WN, acc, no_cin);
   else
-    epilogue_lds<T, BM, BN, 64, kThreads, FM, FN, false>(cl, mat, tm, tn, wm * WM, wn * WN, acc, no_cin,
-                                                         (float *)&lds[0][0]);
+    epilogue_lds<T, BM, BN, 64, kThreads, FM, FN>(cl, mat, tm, tn, wm * WM, wn * WN, acc, (float *)&lds[0][0]);
 }
 
 
@@ -730,9 +794,7 @@ __global__ __launch_bounds__(2 * WN_WAVES * 64, 1) void ns_gemm_big_kernel(GemmA
       stage(kb + 1, by, bx);
     }
   }
-  const float no_cin[FM][FN][4] = {};
-  epilogue_lds<T, kBigTile, kBigTile, 64, NWAVES * 64, FM, FN, false>(cl, mat, tm, tn, wm * 128, wn * WTN, acc, no_cin,
-                                                                     (float *)lds);
+  epilogue_lds<T, kBigTile, kBigTile, 64, NWAVES * 64, FM, FN>(cl, mat, tm, tn, wm * 128, wn * WTN, acc, (float *)lds);
 }
 
 // ---------------------------------------------------------------------------
