@@ -17,12 +17,11 @@
 // X' = a X + B X, plus the storage scale of fp16 buffers.
 //
 // Operands: fp16 / bf16 use v_mfma_f32_16x16x32_{f16,bf16}; fp32 uses
-// v_mfma_f32_16x16x4_f32.  Accumulation is always fp32.  Each 64-lane
-// wavefront owns a (BM/2) x (BN/2) sub-tile; k advances 128 bytes per LDS
-// stage, double-buffered, with one barrier per stage.  LDS rows carry 16 bytes
-// of padding so the 16-byte fragment reads of 8 consecutive rows fall into
-// distinct banks.  All workspace buffers are zero-padded to tile multiples, so
-// the main loop has no bounds checks.
+// v_mfma_f32_16x16x4_f32.  Accumulation is always fp32.  Three block tiles:
+// 64 x 64 (latency-bound small products, 16-bit), 128 x 128 (register-staged
+// loads; also every fp32 product) and 256 x 256 (global -> LDS DMA, 16-bit).
+// All workspace buffers are zero-padded to tile multiples, so the main loops
+// have no bounds checks.
 #include "muon_kernels.h"
 
 namespace muon {
@@ -528,6 +527,11 @@ __device__ __forceinline__ void epilogue_lds(const GemmClass &cl, int mat, int t
   }
 }
 
+// Register-staged BM x BN block tile (64 or 128; every fp32 product and the
+// 16-bit 128 tile): four waves of (BM/2) x (BN/2); k advances 128 bytes per
+// LDS stage, double-buffered through registers, with one barrier per stage.
+// LDS rows carry 16 bytes of padding so the 16-byte fragment reads of 8
+// consecutive rows fall into distinct banks.
 constexpr int kThreads = 256;
 constexpr int kStageBytes = 128;               // k bytes per LDS stage per row
 constexpr int kPitch = kStageBytes + 16;       // padded LDS row
@@ -643,46 +647,45 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(GemmArgs args) {
 
 
 // ---------------------------------------------------------------------------
-// 256 x 256 block tile for fp16 / bf16: four waves of 128 x 128 each, which
-// halves LDS traffic per MFMA relative to 64 x 64 wave tiles.
-//
-// Operands move global -> LDS with global_load_lds_dwordx4 (no register
-// staging).  A stage is 32 k (64 bytes per row) of the 256-row A and B
-// panels, 32 KB in all; stages live in a 4-deep LDS ring (128 KB) and are
-// fetched three stages ahead.  One DMA instruction deposits 1 KB = 16 rows x
-// 64 bytes.  LDS rows are not padded: 16-byte chunk c of row r is stored at
-// chunk c ^ ((r >> 1) & 3), so the 16-byte fragment reads of any 8
-// consecutive rows touch 8 distinct bank groups.
-//
-// Iteration kb (one barrier): wait until stage kb+1 has landed, barrier,
-// issue the DMA of stage kb+3 into the slot stage kb-1 used, then run the 64
-// MFMAs of stage kb while streaming its A fragments one ahead and reading the
-// B fragments (and first A fragment) of stage kb+1.
+// Stage formats shared by the 16-bit DMA kernels.
 constexpr int kBigTile = 256;
-constexpr int kBigRowBytes = 64;                                    // 32 x 16-bit k per stage
-constexpr int kBigStage = (kBigTile + kBigTile) * kBigRowBytes;     // 32 KB
-#ifndef MUON_BIG_RING
-#define MUON_BIG_RING 4
-#endif
+constexpr int kBigRowBytes = 64;   // 32 x 16-bit k per stage row (64 x 64 tile)
 #ifndef MUON_A_AHEAD
 #define MUON_A_AHEAD 3
 #endif
-constexpr int kBigRing = MUON_BIG_RING;   // LDS ring depth (stages); DMA runs kBigRing-1 ahead
 constexpr int kAAhead = MUON_A_AHEAD;     // A fragments read this many 16-row blocks ahead
 
-// WN_WAVES = 2: four waves (one per SIMD), 128 x 128 each.
-// WN_WAVES = 4: eight waves (two per SIMD), 128 x 64 each; the second wave
-// on each SIMD issues MFMAs while the first waits at a barrier or on LDS.
+// ---------------------------------------------------------------------------
+// 256 x 256 block tile for fp16 / bf16: eight waves (two per SIMD) of
+// 128 x 64 each; the second wave on a SIMD issues MFMAs while the first
+// waits at a barrier or on LDS.
+//
+// Operands move global -> LDS with global_load_lds_dwordx4 (no register
+// staging).  A stage holds 64 k = 128 bytes of every row of the 256-row A
+// and B panels (64 KB); each group of 8 lanes of a DMA instruction fetches
+// one whole 128-byte line (8 rows x 128 bytes per instruction), which halves
+// the L1 -> L2 requests per byte relative to 64-byte row segments.  Two
+// stages (128 KB) form the ring; the DMA of stage kb+2 is issued once every
+// wave is done with stage kb, so a stage has one stage of compute to land.
+// LDS rows are not padded: 16-byte chunk c of row r is stored at chunk
+// c ^ (r & 7), so the fragment reads of 8 consecutive rows at one logical
+// chunk cover all 32 banks.  Within a stage the A fragments are streamed
+// kAAhead 16-row blocks ahead and the second k-step's B fragments are read
+// during the first.
+constexpr int kWideRowBytes = 128;                                  // 64 x 16-bit k per stage
+constexpr int kWideStage = (kBigTile + kBigTile) * kWideRowBytes;   // 64 KB
+
 template <typename T, int WN_WAVES>
-__global__ __launch_bounds__(2 * WN_WAVES * 64, 1) void ns_gemm_big_kernel(GemmArgs args) {
+__global__ __launch_bounds__(2 * WN_WAVES * 64, 1) void ns_gemm_wide_kernel(GemmArgs args) {
   static_assert(sizeof(T) == 2, "16-bit operands only");
-  static_assert(8 % (kAAhead + 1) == 0, "A fragment ring must divide the 8 row blocks");
+  static_assert(16 % (kAAhead + 1) == 0, "A fragment ring must divide the 16 fragment groups");
   constexpr int NWAVES = 2 * WN_WAVES;
   constexpr int WTN = kBigTile / WN_WAVES;       // wave tile columns
   constexpr int FM = 8, FN = WTN / 16;           // 128 x WTN per wave
-  constexpr int DMA_PER_WAVE = 16 / NWAVES;      // 1 KB DMA instructions per operand per stage
-  constexpr int kLdsBytes = kBigRing * kBigStage > epilogue_lds_floats<64, kBigTile>() * 4
-                                ? kBigRing * kBigStage : epilogue_lds_floats<64, kBigTile>() * 4;
+  constexpr int DMA_PER_WAVE = 32 / NWAVES;      // 1 KB DMA instructions per operand per stage
+  constexpr int PER_STAGE = 2 * DMA_PER_WAVE;    // DMA instructions per stage and wave
+  constexpr int kLdsBytes = 2 * kWideStage > epilogue_lds_floats<64, kBigTile>() * 4
+                                ? 2 * kWideStage : epilogue_lds_floats<64, kBigTile>() * 4;
   __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
 
   const TileRef tr = locate_tile(args);
@@ -691,27 +694,26 @@ __global__ __launch_bounds__(2 * WN_WAVES * 64, 1) void ns_gemm_big_kernel(GemmA
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave / WN_WAVES, wn = wave % WN_WAVES;
-  constexpr int PER_STAGE = 2 * DMA_PER_WAVE;   // DMA instructions per stage and wave
 
   const char *A = (const char *)cl.a + ((int64_t)mat * cl.sa + (int64_t)tm * kBigTile * cl.lda) * 2;
   const char *B = (const char *)cl.b + ((int64_t)mat * cl.sb + (int64_t)tn * kBigTile * cl.ldb) * 2;
   const int64_t lda_b = (int64_t)cl.lda * 2, ldb_b = (int64_t)cl.ldb * 2;
 
-  // DMA: wave w moves rows [16 DMA_PER_WAVE w, +16 DMA_PER_WAVE) of A and of
-  // B, 16 rows per instruction; lane L covers row L / 4 of the group and
-  // physical chunk L % 4, which holds logical chunk (L % 4) ^ ((L / 4 >> 1) & 3).
-  const int dma_row = lane >> 2;
-  const int dma_chunk = (lane & 3) ^ ((dma_row >> 1) & 3);
-  const uint32_t a_lane = (uint32_t)(dma_row * lda_b) + (uint32_t)(dma_chunk * 16);
-  const uint32_t b_lane = (uint32_t)(dma_row * ldb_b) + (uint32_t)(dma_chunk * 16);
-  const char *a_src = A + (int64_t)(wave * 16 * DMA_PER_WAVE) * lda_b;
-  const char *b_src = B + (int64_t)(wave * 16 * DMA_PER_WAVE) * ldb_b;
+  // DMA: wave w moves rows [8 DMA_PER_WAVE w, +8 DMA_PER_WAVE) of A and of
+  // B, 8 rows per instruction; lane L covers row L / 8 of the group and
+  // physical chunk L % 8, which holds logical chunk (L % 8) ^ (L / 8).
+  const int dma_row = lane >> 3;
+  const int dma_chunk = (lane & 7) ^ dma_row;
+  const char *a_src = A + (int64_t)(wave * 8 * DMA_PER_WAVE + dma_row) * lda_b + dma_chunk * 16;
+  const char *b_src = B + (int64_t)(wave * 8 * DMA_PER_WAVE + dma_row) * ldb_b + dma_chunk * 16;
 
-  // fragment reads: row (16-row block) + lane % 16, logical chunk lane / 16
+  // fragment of k-step ks (32 k) for row block base + lane % 16: logical
+  // chunk 4 ks + lane / 16, physical chunk logical ^ (lane % 8)
   const int fr_row = lane & 15;
-  const int fr_chunk = ((lane >> 4) ^ ((fr_row >> 1) & 3)) * 16;
-  const int a_frag = (wm * 128 + fr_row) * kBigRowBytes + fr_chunk;
-  const int b_frag = (kBigTile + wn * WTN + fr_row) * kBigRowBytes + fr_chunk;
+  const int a_frag = (wm * 128 + fr_row) * kWideRowBytes;
+  const int b_frag = (kBigTile + wn * WTN + fr_row) * kWideRowBytes;
+  const int chunk0 = (((lane >> 4)) ^ (lane & 7)) * 16;       // ks = 0
+  const int chunk1 = ((4 + (lane >> 4)) ^ (lane & 7)) * 16;   // ks = 1
 
   f32x4 acc[FM][FN];
 #pragma unroll
@@ -719,79 +721,54 @@ __global__ __launch_bounds__(2 * WN_WAVES * 64, 1) void ns_gemm_big_kernel(GemmA
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = cl.K / (kBigRowBytes / 2);
+  const int nk = cl.K / (kWideRowBytes / 2);
   if (nk > 0) {
     auto dma = [&](int kb) {
-      char *dst = lds + (kb % kBigRing) * kBigStage + wave * DMA_PER_WAVE * 1024;
+      char *dst = lds + (kb & 1) * kWideStage + wave * DMA_PER_WAVE * 1024;
 #pragma unroll
-      for (int j = 0; j < DMA_PER_WAVE; ++j) {
-        const char *base = a_src + (int64_t)j * 16 * lda_b + (int64_t)kb * kBigRowBytes;
-        __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)(base + a_lane),
-                                         (void __attribute__((address_space(3))) *)(dst + j * 1024), 16, 0, 0);
-      }
+      for (int j = 0; j < DMA_PER_WAVE; ++j)
+        __builtin_amdgcn_global_load_lds(
+            (const void __attribute__((address_space(1))) *)(a_src + (int64_t)j * 8 * lda_b + (int64_t)kb * kWideRowBytes),
+            (void __attribute__((address_space(3))) *)(dst + j * 1024), 16, 0, 0);
 #pragma unroll
-      for (int j = 0; j < DMA_PER_WAVE; ++j) {
-        const char *base = b_src + (int64_t)j * 16 * ldb_b + (int64_t)kb * kBigRowBytes;
-        __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)(base + b_lane),
-                                         (void __attribute__((address_space(3))) *)(dst + kBigTile * kBigRowBytes + j * 1024),
-                                         16, 0, 0);
-      }
+      for (int j = 0; j < DMA_PER_WAVE; ++j)
+        __builtin_amdgcn_global_load_lds(
+            (const void __attribute__((address_space(1))) *)(b_src + (int64_t)j * 8 * ldb_b + (int64_t)kb * kWideRowBytes),
+            (void __attribute__((address_space(3))) *)(dst + kBigTile * kWideRowBytes + j * 1024), 16, 0, 0);
     };
-    auto rd = [&](int kb, int off) -> u32x4 {
-      return *(const u32x4 *)(lds + (kb % kBigRing) * kBigStage + off);
+    // fragment group g = 8 ks + i: A row block i at k-step ks
+    auto rd_a = [&](const char *slot, int g) -> u32x4 {
+      return *(const u32x4 *)(slot + a_frag + (g & 7) * 16 * kWideRowBytes + ((g >> 3) ? chunk1 : chunk0));
     };
-    // prologue: stages 0 .. kBigRing-2 in flight; wait for stage 0 (DMA
-    // completes in issue order, PER_STAGE instructions per stage and wave)
-    static_for<0, kBigRing - 1>([&](auto sc) {
-      constexpr int st = decltype(sc)::value;
-      if (st < nk) dma(st);
-    });
-    {
-      const int inflight = min(nk, kBigRing - 1) - 1;   // stages issued after stage 0
-      waitcnt_vm(inflight * PER_STAGE);
-    }
+    dma(0);
+    if (nk > 1) dma(1);
+    waitcnt_vm((nk > 1 ? 1 : 0) * PER_STAGE);
     __syncthreads();
-    u32x4 bx[FN], by[FN], a_q[kAAhead + 1];
+#pragma unroll 1
+    for (int kb = 0; kb < nk; ++kb) {
+      const char *slot = lds + (kb & 1) * kWideStage;
+      u32x4 b0[FN], b1[FN], a_q[kAAhead + 1];
 #pragma unroll
-    for (int j = 0; j < FN; ++j) bx[j] = rd(0, b_frag + j * 16 * kBigRowBytes);
+      for (int j = 0; j < FN; ++j) b0[j] = *(const u32x4 *)(slot + b_frag + j * 16 * kWideRowBytes + chunk0);
 #pragma unroll
-    for (int q = 0; q < kAAhead; ++q) a_q[q] = rd(0, a_frag + q * 16 * kBigRowBytes);
-
-    // one stage: MFMAs on (a_cur stream, bc), reading bn and the next a_cur
-    auto stage = [&](int kb, u32x4 (&bc)[FN], u32x4 (&bn)[FN]) {
-      // Stage kb+1 must be visible before its fragments are read below: this
-      // wave's DMA of kb+1 is done once at most one stage is outstanding; the
-      // barrier covers the other waves.  The barrier is raw (no fence) so the
-      // DMA of stage kb+2 stays in flight; the memory clobber keeps the
-      // compiler from moving LDS reads across it.
-      // DMAs issued so far cover stages up to kb + kBigRing - 2; all but the
-      // ones after kb+1 must have landed
-      waitcnt_vm(max(0, min(nk - (kb + 2), kBigRing - 3)) * PER_STAGE);
+      for (int q = 0; q < kAAhead; ++q) a_q[q] = rd_a(slot, q);
+      static_for<0, 16>([&](auto gc) {
+        constexpr int g = decltype(gc)::value;
+        constexpr int i = g & 7;
+        if constexpr (g + kAAhead < 16) a_q[(g + kAAhead) % (kAAhead + 1)] = rd_a(slot, g + kAAhead);
+        if constexpr (g < FN) b1[g] = *(const u32x4 *)(slot + b_frag + g * 16 * kWideRowBytes + chunk1);
+        __builtin_amdgcn_sched_barrier(0);   // reads issue before the MFMAs that hide them
+#pragma unroll
+        for (int j = 0; j < FN; ++j) Mma<T>::run(a_q[g % (kAAhead + 1)], (g < 8) ? b0[j] : b1[j], acc[i][j]);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      // stage kb+1 has landed (its DMA is the only one outstanding) and every
+      // wave is done with stage kb: its slot takes stage kb+2
+      waitcnt_vm(0);
       __builtin_amdgcn_sched_barrier(0);
       asm volatile("s_barrier" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
-      if (kb + kBigRing - 1 < nk) dma(kb + kBigRing - 1);
-      // After the last stage the look-ahead reads fetch a stale ring slot
-      // (inside the LDS allocation) and are never used: no branch, so the
-      // accumulators keep one register assignment around the loop.
-      static_for<0, FM>([&](auto ic) {
-        constexpr int i = decltype(ic)::value;
-        constexpr int ia = i + kAAhead;            // A block read in this group
-        a_q[(i + kAAhead) % (kAAhead + 1)] =
-            (ia < FM) ? rd(kb, a_frag + ia * 16 * kBigRowBytes) : rd(kb + 1, a_frag + (ia - FM) * 16 * kBigRowBytes);
-        if constexpr (i < FN) bn[i] = rd(kb + 1, b_frag + i * 16 * kBigRowBytes);
-        __builtin_amdgcn_sched_barrier(0);   // reads issue before the MFMAs that hide them
-#pragma unroll
-        for (int j = 0; j < FN; ++j) Mma<T>::run(a_q[i % (kAAhead + 1)], bc[j], acc[i][j]);
-        __builtin_amdgcn_sched_barrier(0);
-      });
-    };
-    // K is a multiple of the 256 tile, so nk is a multiple of 8: stages
-    // come in pairs and the B fragment sets alternate without copies.
-#pragma unroll 1
-    for (int kb = 0; kb < nk; kb += 2) {
-      stage(kb, bx, by);
-      stage(kb + 1, by, bx);
+      if (kb + 2 < nk) dma(kb + 2);
     }
   }
   epilogue_lds<T, kBigTile, kBigTile, 64, NWAVES * 64, FM, FN>(cl, mat, tm, tn, wm * 128, wn * WTN, acc, (float *)lds);
@@ -800,8 +777,9 @@ __global__ __launch_bounds__(2 * WN_WAVES * 64, 1) void ns_gemm_big_kernel(GemmA
 // ---------------------------------------------------------------------------
 // 64 x 64 block tile for fp16 / bf16 at small sizes, where a step is a chain
 // of memory latencies rather than MFMA work.  Four waves of 32 x 32.  The
-// same swizzled, unpadded 64-byte-row LDS stages as the 256 tile (32 k per
-// stage, 8 KB for A and B), in a ring of RING stages that is filled up front:
+// operands move global -> LDS by DMA into unpadded 64-byte rows (32 k per
+// stage, 8 KB for A and B; 16-byte chunk c of row r stored at chunk
+// c ^ ((r >> 1) & 3)), in a ring of RING stages that is filled up front:
 // a K <= 32 RING panel costs one memory round trip.  Stages are consumed in
 // groups of 4 with one barrier per group; after the barrier the slots of the
 // previous group are refilled with the stages RING ahead.
@@ -923,7 +901,7 @@ hipError_t launch_t(const GemmArgs &args, int tile, hipStream_t s) {
     case 128: hipLaunchKernelGGL((ns_gemm_kernel<T, 128, 128>), dim3(args.total_tiles), dim3(kThreads), 0, s, args); break;
     case 256:
       if constexpr (sizeof(T) == 2) {
-        hipLaunchKernelGGL((ns_gemm_big_kernel<T, 4>), dim3(args.total_tiles), dim3(512), 0, s, args);
+        hipLaunchKernelGGL((ns_gemm_wide_kernel<T, 4>), dim3(args.total_tiles), dim3(512), 0, s, args);
         break;
       } else {
         return hipErrorInvalidValue;
