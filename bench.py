@@ -5,7 +5,7 @@
 A "step" is one full optimizer step over every matrix of the workload (MONA,
 momentum, normalisation, Newton-Schulz, decoupled update), with gradients and
 state already resident in HBM.  Rank 0 prints one JSON line with the step time
-(the headline value), the dominant kernel's roofline (per-launch durations
+(the headline value), the dominant kernel's roofline (kernel durations
 measured with HIP events on the launch stream), and the fp64 CPU oracle timed
 on this host's cores on a bounded sample.
 """
@@ -188,28 +188,32 @@ def gpu_timing(args, w, variant):
     wall = time.perf_counter() - t0
     ms_per_step = start.elapsed_time(end) / args.steps
 
-    # per-launch durations: HIP events recorded by libmuon around every launch
+    # kernel durations: HIP events recorded by libmuon on the launch stream
+    # around every run of consecutive launches of one stage (no event between
+    # the launches of a run, so the events do not separate the kernels)
     tsteps = args.trace_steps or args.steps
     cap = 512
     ev = HipEvents(2 * cap)
     stages = (ctypes.c_int32 * cap)()
     work = (ctypes.c_double * cap)()
+    nl = (ctypes.c_int32 * cap)()
     trace = _lib.MuonTrace(events=ctypes.cast(ev.arr, ctypes.POINTER(ctypes.c_void_p)),
                            stages=ctypes.cast(stages, ctypes.POINTER(ctypes.c_int32)),
-                           work=ctypes.cast(work, ctypes.POINTER(ctypes.c_double)), capacity=cap, count=0)
+                           work=ctypes.cast(work, ctypes.POINTER(ctypes.c_double)), capacity=cap, count=0,
+                           group=1, launches=ctypes.cast(nl, ctypes.POINTER(ctypes.c_int32)))
     per_stage = {}
     launches_per_step = 0
     for _ in range(tsteps):
         nsm.muon_step(params, coeffs=coeffs, step=step_idx, trace=trace, **kw)
         torch.cuda.synchronize()
         n = min(trace.count, cap)
-        launches_per_step = trace.count
+        launches_per_step = sum(nl[i] for i in range(n))
         for i in range(n):
             name = _lib.STAGE_NAMES[stages[i]]
             d = per_stage.setdefault(name, {"ms": 0.0, "work": 0.0, "launches": 0})
             d["ms"] += ev.elapsed_ms(2 * i, 2 * i + 1)
             d["work"] += work[i]
-            d["launches"] += 1
+            d["launches"] += nl[i]
     ev.close()
     for d in per_stage.values():
         d["ms"] /= tsteps

@@ -88,20 +88,29 @@ typedef enum muon_stage {
   MUON_STAGE_E3 = 4      /* decoupled weight-decay update                      */
 } muon_stage;
 
-/* Optional per-launch timing.  When muon_options.trace is non-NULL the library
- * records events[2*i] on the stream before launch i and events[2*i+1] after
- * it, for the first `capacity` launches of the call, and writes each launch's
- * muon_stage into stages[i] and its algorithmic work into work[i] (FLOPs for
- * GEMM launches, bytes moved for the others).  The caller creates the events
- * (hipEventCreate, timing enabled) and reads them after synchronising.
- * `count` returns the number of launches of the call (which may exceed
- * capacity; the excess is not recorded). */
+/* Optional launch timing.  When muon_options.trace is non-NULL the library
+ * records HIP events on the stream around its launches and writes, for each
+ * recorded interval i (at most `capacity`), events[2*i] (before) and
+ * events[2*i+1] (after), the muon_stage of the interval's launches into
+ * stages[i] and their summed algorithmic work into work[i] (FLOPs for GEMM
+ * launches, bytes moved for the others).
+ *   group == 0: one interval per launch.
+ *   group != 0: one interval per run of consecutive launches of the same
+ *               stage, with no event between the launches of a run (so the
+ *               events do not separate them); launches[i] receives the
+ *               number of launches in interval i.
+ * The caller creates the events (hipEventCreate, timing enabled) and reads
+ * them after synchronising.  `count` returns the number of intervals of the
+ * call (which may exceed capacity; the excess is not recorded).  `launches`
+ * may be NULL when group == 0. */
 typedef struct muon_trace {
   void **events;         /* 2 * capacity hipEvent_t handles                   */
   int32_t *stages;       /* capacity entries, out                             */
   double *work;          /* capacity entries, out                             */
   int32_t capacity;
   int32_t count;         /* out                                               */
+  int32_t group;         /* 0: per launch; else per run of one stage          */
+  int32_t *launches;     /* capacity entries, out (group != 0)                */
 } muon_trace;
 
 /* Settings shared by every matrix of a call.  Pass NULL for the defaults. */

@@ -49,6 +49,8 @@ class MuonTrace(ctypes.Structure):
         ("work", ctypes.POINTER(ctypes.c_double)),
         ("capacity", ctypes.c_int32),
         ("count", ctypes.c_int32),
+        ("group", ctypes.c_int32),
+        ("launches", ctypes.POINTER(ctypes.c_int32)),
     ]
 
 

@@ -280,27 +280,51 @@ double sup_poly(double a, double b, double c, double hi, int which) {
 
 bool restart_due(int k, int r) { return r > 0 && k > 1 && (k - 1) % r == 0; }
 
-// Optional per-launch HIP-event timing (muon_trace).
+// Optional HIP-event timing (muon_trace): one interval per launch, or per
+// run of consecutive launches of one stage (group mode; the run's end event
+// is recorded when the run closes, so no event separates its launches).
 struct Tracer {
   muon_trace *t;
   hipStream_t s;
+  int open = -1;   // group mode: interval still accepting launches
+  hipError_t close() {
+    if (!t || open < 0) return hipSuccess;
+    const int i = open;
+    open = -1;
+    return hipEventRecord((hipEvent_t)t->events[2 * i + 1], s);
+  }
   template <typename F>
   hipError_t run(int stage, double work, F &&launch) {
-    const int i = t ? t->count : 0;
-    const bool rec = t && i < t->capacity;
+    if (!t) return launch();
+    if (t->group && open >= 0 && t->stages[open] == stage) {
+      hipError_t e = launch();
+      if (e != hipSuccess) return e;
+      t->work[open] += work;
+      t->launches[open] += 1;
+      return hipSuccess;
+    }
+    hipError_t e = close();
+    if (e != hipSuccess) return e;
+    const int i = t->count;
+    const bool rec = i < t->capacity;
     if (rec) {
-      hipError_t e = hipEventRecord((hipEvent_t)t->events[2 * i], s);
+      e = hipEventRecord((hipEvent_t)t->events[2 * i], s);
       if (e != hipSuccess) return e;
     }
-    hipError_t e = launch();
+    e = launch();
     if (e != hipSuccess) return e;
     if (rec) {
-      e = hipEventRecord((hipEvent_t)t->events[2 * i + 1], s);
-      if (e != hipSuccess) return e;
       t->stages[i] = stage;
       t->work[i] = work;
+      if (t->launches) t->launches[i] = 1;
+      if (t->group) {
+        open = i;
+      } else {
+        e = hipEventRecord((hipEvent_t)t->events[2 * i + 1], s);
+        if (e != hipSuccess) return e;
+      }
     }
-    if (t) t->count++;
+    t->count++;
     return hipSuccess;
   }
 };
@@ -705,7 +729,7 @@ muon_status muon_step(const muon_param *params, int n, float lr, float mu, float
   char *ws = (char *)workspace;
   muon_trace *trace = opts ? opts->trace : nullptr;
   if (trace) {
-    if (trace->capacity > 0 && (!trace->events || !trace->stages || !trace->work))
+    if (trace->capacity > 0 && (!trace->events || !trace->stages || !trace->work || (trace->group && !trace->launches)))
       return fail(MUON_ERR_INVALID_ARG, "trace arrays are NULL");
     trace->count = 0;
   }
@@ -769,6 +793,7 @@ muon_status muon_step(const muon_param *params, int n, float lr, float mu, float
     st = flush();
     if (st != MUON_OK) return st;
   }
+  HIP_TRY(tr.close());   // a traced run of launches ends where its stage ends
 
   // ---- norm finalize
   const Scaler S{set.ns_dtype == kF16};
@@ -792,6 +817,7 @@ muon_status muon_step(const muon_param *params, int n, float lr, float mu, float
       m.scale_idx = i;
     }
     if (a.nmat) HIP_TRY(tr.run(MUON_STAGE_NORM, 0.0, [&]() { return launch_norm(a, hs); }));
+    HIP_TRY(tr.close());
   }
 
   // ---- E2: X0 into X[0] / XT[0]
@@ -840,6 +866,7 @@ muon_status muon_step(const muon_param *params, int n, float lr, float mu, float
       bytes += (4.0 + 2.0 * (double)es) * (double)(params[i].rows * params[i].cols);
     }
     if (a.nmat) HIP_TRY(tr.run(MUON_STAGE_E2, bytes, [&]() { return launch_e2(a, blocks, hs); }));
+    HIP_TRY(tr.close());
   }
 
   // ---- Newton-Schulz
@@ -848,6 +875,7 @@ muon_status muon_step(const muon_param *params, int n, float lr, float mu, float
     st = (variant == MUON_NS_DIRECT) ? run_direct(plan, ws, tr, sx0, lr, lambda, res)
                                      : run_gram(plan, ws, tr, sx0, lr, lambda, res);
     if (st != MUON_OK) return st;
+    HIP_TRY(tr.close());
   }
 
   // ---- E3: only without Newton-Schulz steps (O = X0); otherwise the last
@@ -890,6 +918,7 @@ muon_status muon_step(const muon_param *params, int n, float lr, float mu, float
     }
     if (a.nmat) HIP_TRY(tr.run(MUON_STAGE_E3, bytes, [&]() { return launch_e3(a, blocks, hs); }));
   }
+  HIP_TRY(tr.close());
   g_last_error.clear();
   return MUON_OK;
 }

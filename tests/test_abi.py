@@ -43,11 +43,12 @@ def test_struct_layout_matches_header(tmp_path):
 #include <stddef.h>
 #include "muon.h"
 int main(void) {
-  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(muon_param), offsetof(muon_param, grad),
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(muon_param), offsetof(muon_param, grad),
          offsetof(muon_param, prev_grad), offsetof(muon_param, rows), offsetof(muon_param, gamma),
          offsetof(muon_param, ortho_out), sizeof(muon_options), offsetof(muon_options, coeffs),
          offsetof(muon_options, divisor), offsetof(muon_options, step), offsetof(muon_options, trace),
-         sizeof(muon_trace), offsetof(muon_trace, capacity));
+         sizeof(muon_trace), offsetof(muon_trace, capacity), offsetof(muon_trace, group),
+         offsetof(muon_trace, launches));
   return 0;
 }
 ''')
@@ -57,7 +58,8 @@ int main(void) {
     P, O = _lib.MuonParam, _lib.MuonOptions
     want = [ctypes.sizeof(P), P.grad.offset, P.prev_grad.offset, P.rows.offset, P.gamma.offset, P.ortho_out.offset,
             ctypes.sizeof(O), O.coeffs.offset, O.divisor.offset, O.step.offset, O.trace.offset,
-            ctypes.sizeof(_lib.MuonTrace), _lib.MuonTrace.capacity.offset]
+            ctypes.sizeof(_lib.MuonTrace), _lib.MuonTrace.capacity.offset, _lib.MuonTrace.group.offset,
+            _lib.MuonTrace.launches.offset]
     assert got == want
 
 

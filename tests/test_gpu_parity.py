@@ -245,3 +245,47 @@ def test_symmetric_input_gram_f32():
     torch.cuda.synchronize()
     ref = oracle.newton_schulz_gram(oracle.frobenius_normalize(to64(g)), oracle.coefficient_table("quintic", 5))
     assert rel_fro(to64(params[0]["ortho_out"]), ref) < 1e-5
+
+
+# ---------------------------------------------------------------- launch timing
+
+def _traced_step(group):
+    import ctypes
+    import newton_schulz_matrix_momentum_amd as nsm
+    from newton_schulz_matrix_momentum_amd import _lib
+    import bench
+    shapes = [(192, 192)] * 4 + [(192, 768), (768, 192)]
+    params = make_params(shapes, "bf16", False, 31)
+    for p, g in zip(params, draw_grads(shapes, "bf16", 32)):
+        p["grad"] = g
+    cap = 64
+    ev = bench.HipEvents(2 * cap)
+    stages = (ctypes.c_int32 * cap)()
+    work = (ctypes.c_double * cap)()
+    nl = (ctypes.c_int32 * cap)()
+    tr = _lib.MuonTrace(events=ctypes.cast(ev.arr, ctypes.POINTER(ctypes.c_void_p)),
+                        stages=ctypes.cast(stages, ctypes.POINTER(ctypes.c_int32)),
+                        work=ctypes.cast(work, ctypes.POINTER(ctypes.c_double)), capacity=cap, count=0,
+                        group=group, launches=ctypes.cast(nl, ctypes.POINTER(ctypes.c_int32)))
+    nsm.muon_step(params, lr=0.02, mu=0.95, ns_dtype="bf16", trace=tr)
+    torch.cuda.synchronize()
+    out = [(_lib.STAGE_NAMES[stages[i]], nl[i], work[i], ev.elapsed_ms(2 * i, 2 * i + 1)) for i in range(tr.count)]
+    ev.close()
+    return out
+
+
+def test_trace_per_launch_and_grouped():
+    """Per-launch mode: one interval per launch (E1, E2, 3 x 5 products).
+    Grouped mode: one interval per run of one stage, launch counts and work
+    summed."""
+    per = _traced_step(0)
+    assert [s for s, _, _, _ in per] == ["e1", "e2"] + ["gemm"] * 15
+    assert all(ms > 0 for _, _, _, ms in per)
+    grp = _traced_step(1)
+    assert [(s, n) for s, n, _, _ in grp] == [("e1", 1), ("e2", 1), ("gemm", 15)]
+    assert grp[2][2] == pytest.approx(sum(w for s, _, w, _ in per if s == "gemm"))
+    # 5 quintic steps on 4 x 192^2 and 2 x (192 x 768): half Gram, half square, full update
+    s = 192.0
+    flops = 5 * (4 * (s * (s + 1) * s * 2 + 2 * s * s * s) + 2 * (s * (s + 1) * 768 + s * (s + 1) * s + 2 * s * s * 768))
+    assert grp[2][2] == pytest.approx(flops)
+    assert grp[2][3] > 0
