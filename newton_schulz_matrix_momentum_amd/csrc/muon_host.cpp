@@ -89,12 +89,15 @@ bool is_finite(double v) { return std::isfinite(v); }
 
 // Largest square block tile whose zero padding of the short side stays under
 // 7% (the padded s x s products grow with its square); small sides use 64.
+#ifndef MUON_PAD_LIMIT
+#define MUON_PAD_LIMIT 1.07
+#endif
 int pick_tile(int64_t s, int64_t l, int ns_dtype) {
   (void)l;
   for (int t : {256, 128}) {
     if (t == 256 && ns_dtype == kF32) continue;   // the 256 tile is 16-bit only
     if (s < 2 * t) continue;
-    if ((double)round_up(s, t) <= 1.07 * (double)s) return t;
+    if ((double)round_up(s, t) <= MUON_PAD_LIMIT * (double)s) return t;
   }
   return 64;
 }
