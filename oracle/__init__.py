@@ -11,6 +11,8 @@ from .muon_oracle import (  # noqa: F401
     coefficient_table,
     restart_due,
     mona_acceleration,
+    mona_lite_acceleration,
+    round_bf16,
     momentum_update,
     frobenius_normalize,
     newton_schulz_direct,

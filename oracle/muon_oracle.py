@@ -12,6 +12,9 @@ Sources (the pages this follows):
   the curvature-aware gradient, heavy-ball momentum, Newton-Schulz
   orthogonalisation and the decoupled weight-decay update.  Sub-section
   "Ontwerprichtlijnen": the acceleration is applied before orthogonalisation.
+* The same MONA summary, "Efficiëntie en Implementatie" (MONA-Lite): the
+  auxiliary state is stored in bfloat16 and the gradient difference is
+  formed in place, so no separate previous-gradient buffer is kept.
 * The Telegram post on Gram Newton-Schulz (quant_prune_distill, post 677),
   main body: polar(X) = U V^T for X = U S V^T; the Gram form
   X (X^T X)^{-1/2} with the inverse square root found by Newton-Schulz on the
@@ -38,6 +41,10 @@ design notes):
   (k - 1) mod r == 0: the iterate Y Q is materialised (and divided by
   sqrt(d)), its Gram recomputed, and the accumulated factor reset to I.
 * MONA's first step has no previous gradient: D_0 = 0.
+* MONA-Lite keeps one bfloat16 state C_k = beta_a A_k - (1 - beta_a) G_k, so
+  that A_{k+1} = C_k + (1 - beta_a) G_{k+1} is MONA's A_{k+1} exactly in real
+  arithmetic and G_{k-1} is never stored; C is rounded to bfloat16 (nearest,
+  ties to even) each time it is stored.
 * gamma (the scale on O in the update) is a per-matrix number, default 1.
 
 Everything is computed in float64 from inputs upcast exactly from their stored
@@ -93,6 +100,49 @@ def mona_acceleration(grad, accel, prev_grad, step: int, beta_a: float, alpha: f
     a_new = beta_a * np.asarray(accel, dtype=np.float64) + (1.0 - beta_a) * diff
     g_tilde = g + alpha * a_new
     return g_tilde, a_new, g.copy()
+
+
+def round_bf16(x) -> np.ndarray:
+    """Round to the nearest bfloat16 value (ties to even), returned as float64.
+
+    bfloat16 keeps float32's exponent range with 8 significant bits: normal
+    numbers are multiples of 2^(e-7) for 2^e <= |x| < 2^(e+1), e >= -126;
+    below 2^-126 the spacing is the fixed 2^-133; magnitudes that round
+    beyond the largest finite value (2 - 2^-7) 2^127 become infinity.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    out = np.array(x, dtype=np.float64, copy=True)
+    finite = np.isfinite(x) & (x != 0.0)
+    v = x[finite]
+    _, e = np.frexp(v)                      # v = f 2^e, 0.5 <= |f| < 1, so 2^(e-1) <= |v|
+    exp = np.maximum(e - 1, -126)           # exponent of the leading bit (subnormals: -126)
+    quantum = np.ldexp(1.0, exp - 7)
+    r = np.rint(v / quantum) * quantum      # rint rounds halves to even
+    big = np.ldexp(2.0 - 2.0 ** -7, 127)
+    r = np.where(np.abs(r) > big, np.copysign(np.inf, v), r)
+    out[finite] = r
+    return out
+
+
+def mona_lite_acceleration(grad, state, step: int, beta_a: float, alpha: float, store=round_bf16):
+    """MONA-Lite (MONA summary, "Efficiëntie en Implementatie"): MONA steps
+    1-3 with a single bfloat16 state instead of A and G_{k-1}.
+
+    The state is C_{k-1} = beta_a A_{k-1} - (1 - beta_a) G_{k-1}, so
+        A_k  = C_{k-1} + (1 - beta_a) G_k      (= beta_a A_{k-1} + (1 - beta_a) D_k)
+        G~_k = G_k + alpha A_k
+        C_k  = store(beta_a A_k - (1 - beta_a) G_k)
+    with A_0 = 0 on the first step (no previous gradient).  ``store`` is the
+    state's storage rounding (bfloat16).  Returns (G~_k, A_k, C_k).
+    """
+    g = np.asarray(grad, dtype=np.float64)
+    if step == 0:
+        a_new = np.zeros_like(g)
+    else:
+        a_new = np.asarray(state, dtype=np.float64) + (1.0 - beta_a) * g
+    g_tilde = g + alpha * a_new
+    c_new = store(beta_a * a_new - (1.0 - beta_a) * g)
+    return g_tilde, a_new, c_new
 
 
 def momentum_update(momentum, g_tilde, mu: float):
@@ -185,16 +235,21 @@ def decoupled_update(weight, ortho, lr: float, weight_decay: float, gamma: float
 
 def muon_step_matrix(weight, grad, momentum, *, lr, mu, weight_decay, coeffs,
                      variant="direct", divisor=1.0, restart_every=0, gamma=1.0,
-                     accel=None, prev_grad=None, beta_a=0.0, alpha=0.0, step=0):
+                     accel=None, prev_grad=None, beta_a=0.0, alpha=0.0, step=0, lite_state=None):
     """One optimizer step for one weight matrix, in the pages' order.
 
-    MONA (if ``accel`` is given) -> momentum -> normalise -> Newton-Schulz ->
-    decoupled update.  The acceleration enters before orthogonalisation
-    (MONA summary, "Ontwerprichtlijnen").  Returns a dict with every stage's
-    output, all float64.
+    MONA (if ``accel`` is given) or MONA-Lite (if ``lite_state`` is given) ->
+    momentum -> normalise -> Newton-Schulz -> decoupled update.  The
+    acceleration enters before orthogonalisation (MONA summary,
+    "Ontwerprichtlijnen").  Returns a dict with every stage's output, all
+    float64.
     """
     out = {}
-    if accel is not None:
+    if lite_state is not None:
+        g_tilde, a_new, c_new = mona_lite_acceleration(grad, lite_state, step, beta_a, alpha)
+        out["accel"] = a_new
+        out["lite_state"] = c_new
+    elif accel is not None:
         g_tilde, a_new, prev_new = mona_acceleration(grad, accel, prev_grad, step, beta_a, alpha)
         out["accel"] = a_new
         out["prev_grad"] = prev_new
@@ -215,7 +270,8 @@ def muon_step(params: Iterable[dict], *, lr, mu, weight_decay, coeffs, variant="
     """Apply :func:`muon_step_matrix` to each param dict independently.
 
     Each dict holds ``weight``, ``grad``, ``momentum`` and optionally
-    ``accel``, ``prev_grad`` and ``gamma`` (numpy arrays / floats).
+    ``accel`` and ``prev_grad`` (MONA), ``lite_state`` (MONA-Lite) and
+    ``gamma`` (numpy arrays / floats).
     """
     results = []
     for p in params:
@@ -223,5 +279,5 @@ def muon_step(params: Iterable[dict], *, lr, mu, weight_decay, coeffs, variant="
             p["weight"], p["grad"], p["momentum"], lr=lr, mu=mu, weight_decay=weight_decay,
             coeffs=coeffs, variant=variant, divisor=divisor, restart_every=restart_every,
             gamma=p.get("gamma", 1.0), accel=p.get("accel"), prev_grad=p.get("prev_grad"),
-            beta_a=beta_a, alpha=alpha, step=step))
+            beta_a=beta_a, alpha=alpha, step=step, lite_state=p.get("lite_state")))
     return results

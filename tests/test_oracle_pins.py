@@ -372,3 +372,113 @@ def test_planted_mistakes_are_caught():
 
     for bad in (wrong_gram_side, dropped_square, gram_rp_only, divisor_on_gram_not_iterate, sign_slip):
         assert not _check_all(bad), bad.__name__
+
+
+# ---------------------------------------------------------------- MONA-Lite
+
+BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
+
+
+def test_round_bf16_hand_values():
+    """bfloat16 rounding from its definition: 8 significant bits, ties to even,
+    float32's exponent range, fixed spacing 2^-133 below 2^-126."""
+    r = oracle.round_bf16
+    cases = [
+        (1.0, 1.0),
+        (1.0 + 2.0 ** -8, 1.0),                       # tie -> even (1.0000000)
+        (1.0 + 3 * 2.0 ** -8, 1.0 + 2.0 ** -6),       # tie -> even (1.0000010)
+        (1.0 + 2.0 ** -8 + 2.0 ** -20, 1.0 + 2.0 ** -7),
+        (-(1.0 + 2.0 ** -8 + 2.0 ** -20), -(1.0 + 2.0 ** -7)),
+        (0.1, 0.10009765625),
+        (2.0 ** -130, 2.0 ** -130),                   # subnormal, exact
+        (2.0 ** -134, 0.0),                           # half the subnormal spacing -> even (0)
+        (3 * 2.0 ** -134, 2.0 ** -132),               # 1.5 spacings -> 2
+        (BF16_MAX, BF16_MAX),                          # (2 - 2^-7) 2^127, largest finite
+        (BF16_MAX + 2.0 ** 118, BF16_MAX),             # below half a spacing (2^120)
+        (BF16_MAX + 2.0 ** 119, np.inf),               # tie -> even -> 2^128 overflows
+        (4.0e38, np.inf),
+        (-4.0e38, -np.inf),
+        (0.0, 0.0),
+    ]
+    for x, want in cases:
+        assert r(np.array([x]))[0] == want, (x, r(np.array([x]))[0], want)
+    assert np.isnan(r(np.array([np.nan]))[0])
+    assert r(np.array([np.inf]))[0] == np.inf
+
+
+def test_round_bf16_matches_torch_on_float32_inputs():
+    """Float32 inputs round once to bfloat16: torch's conversion must agree."""
+    import torch
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal(20000) * 10.0 ** rng.uniform(-30, 30, 20000)).astype(np.float32).astype(np.float64)
+    want = torch.from_numpy(x).float().to(torch.bfloat16).double().numpy()
+    np.testing.assert_array_equal(oracle.round_bf16(x), want)
+
+
+def test_mona_lite_exact_state_equals_mona():
+    """Without the bfloat16 rounding, the Lite state reproduces MONA's A_k and
+    G~_k exactly (the identity A_{k+1} = C_k + (1 - beta_a) G_{k+1})."""
+    rng = np.random.default_rng(6)
+    beta, alpha = 0.9, 0.5
+    a = np.zeros((5, 7))
+    prev = np.zeros((5, 7))
+    c = None
+    for step in range(6):
+        g = rng.standard_normal((5, 7))
+        gt_m, a, prev = oracle.mona_acceleration(g, a, prev, step, beta, alpha)
+        gt_l, a_l, c = oracle.mona_lite_acceleration(g, c, step, beta, alpha, store=lambda v: v)
+        np.testing.assert_allclose(a_l, a, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(gt_l, gt_m, rtol=1e-12, atol=1e-13)
+
+
+def test_mona_lite_rounded_state_stays_close():
+    """With the bfloat16 state the acceleration differs from MONA's by the
+    state's rounding only: relative Frobenius error below 1e-2 after 8 steps."""
+    rng = np.random.default_rng(7)
+    beta, alpha = 0.9, 0.5
+    a = np.zeros((16, 24))
+    prev = np.zeros((16, 24))
+    c = None
+    for step in range(8):
+        g = rng.standard_normal((16, 24))
+        _, a, prev = oracle.mona_acceleration(g, a, prev, step, beta, alpha)
+        _, a_l, c = oracle.mona_lite_acceleration(g, c, step, beta, alpha)
+        assert np.all(oracle.round_bf16(c) == c)        # the stored state is bfloat16
+    assert np.linalg.norm(a_l - a) / np.linalg.norm(a) < 1e-2
+    assert np.linalg.norm(a_l - a) > 0                   # and the rounding is visible
+
+
+@pytest.mark.parametrize("variant", ["direct", "gram"])
+def test_golden_scalar_mona_lite_two_steps(variant):
+    g = load_golden("mona_lite_scalar_two_steps.txt")
+    coeffs = oracle.coefficient_table("quintic", 5)
+    w, m, c = np.array([[g["w0"]]]), np.zeros((1, 1)), None
+    for step, (gk, a_want, m_want, w_want, c_want) in enumerate(
+            [(g["g0"], g["a1"], g["m1"], g["w1"], g["c1"]), (g["g1"], g["a2"], g["m2"], g["w2"], g["c2"])]):
+        r = oracle.muon_step_matrix(w, np.array([[gk]]), m, lr=g["lr"], mu=g["mu"], weight_decay=g["weight_decay"],
+                                    coeffs=coeffs, variant=variant, gamma=g["gamma"], beta_a=g["beta_a"],
+                                    alpha=g["alpha"], step=step, lite_state=c if c is not None else np.zeros((1, 1)))
+        assert r["accel"][0, 0] == pytest.approx(a_want, abs=1e-15)
+        assert r["momentum"][0, 0] == pytest.approx(m_want, abs=1e-14)
+        assert r["weight"][0, 0] == pytest.approx(w_want, abs=1e-12)
+        assert r["lite_state"][0, 0] == c_want
+        w, m, c = r["weight"], r["momentum"], r["lite_state"]
+
+
+def test_mona_lite_alpha_zero_is_plain_muon():
+    """alpha = 0: the momentum, and so the step, equal plain Muon's bitwise."""
+    rng = np.random.default_rng(8)
+    coeffs = oracle.coefficient_table("quintic", 5)
+    w = rng.standard_normal((6, 9))
+    m_l = m_p = np.zeros((6, 9))
+    w_l = w_p = w
+    c = np.zeros((6, 9))
+    for step in range(3):
+        g = rng.standard_normal((6, 9))
+        rl = oracle.muon_step_matrix(w_l, g, m_l, lr=0.02, mu=0.95, weight_decay=0.01, coeffs=coeffs, beta_a=0.9,
+                                     alpha=0.0, step=step, lite_state=c)
+        rp = oracle.muon_step_matrix(w_p, g, m_p, lr=0.02, mu=0.95, weight_decay=0.01, coeffs=coeffs)
+        np.testing.assert_array_equal(rl["momentum"], rp["momentum"])
+        np.testing.assert_array_equal(rl["weight"], rp["weight"])
+        w_l, m_l, c = rl["weight"], rl["momentum"], rl["lite_state"]
+        w_p, m_p = rp["weight"], rp["momentum"]
