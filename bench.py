@@ -34,6 +34,8 @@ def parse():
     ap.add_argument("--workload", default="nanochat_6l_d192")
     ap.add_argument("--variant", default=None, help="direct | gram (default: the workload's first)")
     ap.add_argument("--no-graph", action="store_true", help="launch kernels directly instead of a HIP graph")
+    ap.add_argument("--mona-lite", action="store_true",
+                    help="MONA workloads keep one bfloat16 MONA-Lite state instead of A and G_prev")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--trace-steps", type=int, default=None, help="steps timed per launch (default: --steps)")
@@ -114,11 +116,11 @@ class HipEvents:
             self.hip.hipEventDestroy(self.arr[i])
 
 
-def setup(w, variant, device):
+def setup(w, variant, device, mona_lite=False):
     import torch
     from workloads import make_grads, make_state
     gen_dev = device if w.name.startswith("gram_tall") else "cpu"
-    state = make_state(w, device=gen_dev)
+    state = make_state(w, device=gen_dev, mona="lite" if (mona_lite and w.mona) else None)
     grads = make_grads(w, step=1, device=gen_dev)
     params = []
     for st, g in zip(state, grads):
@@ -148,7 +150,7 @@ def gpu_timing(args, w, variant):
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    params = setup(w, variant, dev)
+    params = setup(w, variant, dev, args.mona_lite)
     kw = step_kwargs(w, variant)
     coeffs = coeff_table(w)
     # MONA workloads time steps after the first (D = G - G_prev is live)
@@ -250,7 +252,8 @@ def cpu_baseline(args, w, variant, params):
             oracle.muon_step_matrix(snap["weight"], snap["grad"], snap["momentum"], lr=w.lr, mu=w.mu,
                                     weight_decay=w.weight_decay, coeffs=coeffs, variant=variant, divisor=divisor,
                                     restart_every=restart, accel=snap.get("accel"), prev_grad=snap.get("prev_grad"),
-                                    beta_a=w.beta_a, alpha=w.alpha, step=1 if w.mona else 0)
+                                    lite_state=snap.get("mona_lite"), beta_a=w.beta_a, alpha=w.alpha,
+                                    step=1 if w.mona else 0)
             spent += time.perf_counter() - t0
             reps += 1
         per = spent / reps
@@ -325,9 +328,10 @@ def main():
         "vs_baseline": None,
         "dtype": w.ns_dtype,
         "data": "synthetic",
-        "config": {"workload": w.name, "matrices": len(w.shapes), "params": w.numel, "variant": variant,
+        "config": {"workload": w.name + ("+mona_lite" if args.mona_lite and w.mona else ""), "matrices": len(w.shapes),
+                   "params": w.numel, "variant": variant,
                    "ns_steps": w.ns_steps, "coeffs": w.coeffs, "grad_dtype": w.grad_dtype, "ns_dtype": w.ns_dtype,
-                   "mona": w.mona, "hip_graph": graphed, "parallelism": "single_gpu"},
+                   "mona": ("lite" if args.mona_lite else True) if w.mona else False, "hip_graph": graphed, "parallelism": "single_gpu"},
         "ns_tflops": ns_tflops,
         "ns_frac_of_peak": ns_tflops / peak,
         "elementwise_gbps": ew_gbps,

@@ -9,6 +9,11 @@
  *       D  = G - G_prev          (D = 0 on the first step, opts->step == 0)
  *       A  = beta_a * A + (1 - beta_a) * D
  *       G~ = G + alpha * A ;     G_prev = G
+ *   MONA-Lite (only when `mona_lite` is given) -- MONA summary, "Efficiëntie
+ *   en Implementatie": one bfloat16 state C replaces A and G_prev,
+ *       A  = C + (1 - beta_a) * G  (A = 0 on the first step)
+ *       G~ = G + alpha * A ;       C = bf16(beta_a * A - (1 - beta_a) * G)
+ *   which is MONA's A exactly up to the state's rounding.
  *   Momentum -- same section, step 4:      M = mu * M + G~
  *   Orthogonalisation -- same section, step 4, "O = Newton-Schulz(M)";
  *   polar(X) = U V^T and its Gram form X (X^T X)^{-1/2} with restarts and a
@@ -77,6 +82,9 @@ typedef struct muon_param {
   int64_t rows, cols;   /* >= 1                                                     */
   float gamma;          /* scale on O in the update (gamma of the MONA update)      */
   float *ortho_out;     /* optional fp32 rows*cols: receives O; NULL => not written */
+  void *mona_lite;      /* bfloat16 rows*cols MONA-Lite state, updated in place
+                           (contents ignored on step 0); NULL => not Lite.  Not
+                           together with accel / prev_grad                      */
 } muon_param;
 
 /* Kind of each launch recorded in a muon_trace. */
@@ -148,7 +156,8 @@ size_t muon_workspace_size(const muon_param *params, int n, int ns_steps,
  *              initialisation and are clobbered
  *   stream     hipStream_t (void* here so that C callers need no HIP headers)
  * Errors: MUON_ERR_INVALID_ARG for NULL weight/grad/momentum, accel/prev_grad
- * given without the other, rows or cols < 1, ns_steps out of range,
+ * given without the other, mona_lite together with accel, rows or cols < 1,
+ * ns_steps out of range,
  * non-finite scalars, divisor < 1, restart_every < 0, buffers that overlap;
  * MUON_ERR_UNSUPPORTED for an unknown dtype; MUON_ERR_WORKSPACE_TOO_SMALL;
  * MUON_ERR_HIP when a launch fails. */

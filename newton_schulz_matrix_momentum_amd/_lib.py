@@ -39,6 +39,7 @@ class MuonParam(ctypes.Structure):
         ("cols", ctypes.c_int64),
         ("gamma", ctypes.c_float),
         ("ortho_out", ctypes.c_void_p),
+        ("mona_lite", ctypes.c_void_p),
     ]
 
 

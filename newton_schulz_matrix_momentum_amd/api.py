@@ -61,7 +61,7 @@ def _marshal(params: Sequence[Dict], ns_dtype, coeffs, divisor, restart_every, s
             raise ValueError("all grads of one call must share a dtype (param %d is %s, expected %s)"
                              % (i, g.dtype, grad_dtype))
         device = device or w.device
-        for key in ("grad", "momentum", "accel", "prev_grad", "ortho_out"):
+        for key in ("grad", "momentum", "accel", "prev_grad", "ortho_out", "mona_lite"):
             t = p.get(key)
             if t is not None and t.device != w.device:
                 raise ValueError("param %d: %s is on %s, weight on %s" % (i, key, t.device, w.device))
@@ -74,6 +74,7 @@ def _marshal(params: Sequence[Dict], ns_dtype, coeffs, divisor, restart_every, s
         arr[i].cols = cols
         arr[i].gamma = float(p.get("gamma", 1.0))
         arr[i].ortho_out = _ptr(p.get("ortho_out"), "ortho_out", torch.float32, (rows, cols))
+        arr[i].mona_lite = _ptr(p.get("mona_lite"), "mona_lite", torch.bfloat16, (rows, cols))
     opts = _lib.MuonOptions()
     _lib.load().muon_options_init(ctypes.byref(opts))
     if grad_dtype is not None:
@@ -124,8 +125,9 @@ def muon_step(params: Sequence[Dict], *, lr: float, mu: float, beta_a: float = 0
     """One Muon / MONA step over ``params`` (list of dicts of tensors).
 
     Each dict holds ``weight`` (fp32, updated), ``grad``, ``momentum`` (fp32,
-    updated) and optionally ``accel`` + ``prev_grad`` (MONA state, updated),
-    ``gamma`` (float) and ``ortho_out`` (fp32, receives O).  Enqueued on the
+    updated) and optionally ``accel`` + ``prev_grad`` (MONA state, updated) or
+    ``mona_lite`` (bfloat16 MONA-Lite state, updated), ``gamma`` (float) and
+    ``ortho_out`` (fp32, receives O).  Enqueued on the
     current stream; returns without synchronising.  ``trace`` is an optional
     ``_lib.MuonTrace`` for per-launch HIP-event timing.
     """

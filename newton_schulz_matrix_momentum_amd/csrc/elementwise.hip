@@ -86,20 +86,29 @@ __device__ __forceinline__ int find_mat(const int32_t (&begin)[N], int b) {
 }
 
 // ------------------------------------------------------------------ E1
-template <int GDT, bool MONA>
-__device__ __forceinline__ void e1_elem(float g, float &m, float &a, float prev, const E1Args &args) {
-  if (MONA) {
+// MODE: kE1Plain (Muon), kE1Mona (A and G_prev in their own buffers) or
+// kE1Lite (MONA-Lite: one bfloat16 state C = beta_a A - (1 - beta_a) G, MONA
+// summary "Efficiëntie en Implementatie"; A_k = C_{k-1} + (1 - beta_a) G_k).
+// `s` is A (MONA) or C (Lite) on entry and on exit; `prev` is G_{k-1} (MONA).
+template <int MODE>
+__device__ __forceinline__ void e1_elem(float g, float &m, float &s, float prev, const E1Args &args) {
+  if (MODE == kE1Mona) {
     const float d = args.first_step ? 0.0f : (g - prev);
-    a = args.beta_a * a + (1.0f - args.beta_a) * d;
+    s = args.beta_a * s + (1.0f - args.beta_a) * d;
+    g = g + args.alpha * s;
+  } else if (MODE == kE1Lite) {
+    const float a = args.first_step ? 0.0f : s + (1.0f - args.beta_a) * g;
+    s = args.beta_a * a - (1.0f - args.beta_a) * g;
     g = g + args.alpha * a;
   }
   m = args.mu * m + g;
 }
 
-template <int GDT, bool MONA>
+template <int GDT, int MODE>
 __global__ __launch_bounds__(kE1Threads) void e1_kernel(E1Args args) {
   typedef typename Elem<GDT>::raw graw;
   typedef typename Vec4<GDT>::type gvec;
+  constexpr bool MONA = MODE == kE1Mona, LITE = MODE == kE1Lite;
   constexpr int G = kE1ElemsPerThread / 4;   // groups of 4 elements per thread
   const int mi = find_mat(args.begin, (int)blockIdx.x);
   const E1Mat &mt = args.mats[mi];
@@ -120,14 +129,17 @@ __global__ __launch_bounds__(kE1Threads) void e1_kernel(E1Args args) {
   graw *prev = (graw *)mt.prev;
   float *mom = mt.mom;
   float *acc = mt.accel;
+  uint16_t *lite = (uint16_t *)mt.lite;
   const bool vec_ok = ((((uintptr_t)grad) | ((uintptr_t)mom) | ((uintptr_t)acc) | ((uintptr_t)prev)) & 15) == 0 &&
-                      (sizeof(graw) == 4 || ((((uintptr_t)grad) | ((uintptr_t)prev)) & 7) == 0);
+                      (sizeof(graw) == 4 || ((((uintptr_t)grad) | ((uintptr_t)prev)) & 7) == 0) &&
+                      (((uintptr_t)lite) & 7) == 0;
   float sq = 0.0f;
   if (vec_ok) {
     // Groups of 4 elements, predicated on lying inside the matrix; every load
     // of the thread is issued before the first use (no serial tail loop).
     gvec gv[G], pv[G];
     float4 mv[G], av[G];
+    uint2 lv[G];
 #pragma unroll
     for (int it = 0; it < G; ++it) {
       const int64_t e = base + ((int64_t)it * kE1Threads + threadIdx.x) * 4;
@@ -138,6 +150,7 @@ __global__ __launch_bounds__(kE1Threads) void e1_kernel(E1Args args) {
           av[it] = *(const float4 *)(acc + e);
           if (!args.first_step) pv[it] = *(const gvec *)(prev + e);
         }
+        if (LITE && !args.first_step) lv[it] = *(const uint2 *)(lite + e);
       }
     }
 #pragma unroll
@@ -150,9 +163,10 @@ __global__ __launch_bounds__(kE1Threads) void e1_kernel(E1Args args) {
           a[0] = av[it].x; a[1] = av[it].y; a[2] = av[it].z; a[3] = av[it].w;
           if (!args.first_step) Vec4<GDT>::unpack(pv[it], p);
         }
+        if (LITE && !args.first_step) Vec4<kBF16>::unpack(lv[it], a);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          e1_elem<GDT, MONA>(g[q], m[q], a[q], p[q], args);
+          e1_elem<MODE>(g[q], m[q], a[q], p[q], args);
           sq += m[q] * m[q];
         }
         *(float4 *)(mom + e) = make_float4(m[0], m[1], m[2], m[3]);
@@ -160,6 +174,7 @@ __global__ __launch_bounds__(kE1Threads) void e1_kernel(E1Args args) {
           *(float4 *)(acc + e) = make_float4(a[0], a[1], a[2], a[3]);
           *(gvec *)(prev + e) = gv[it];  // exact copy of the stored gradient
         }
+        if (LITE) *(uint2 *)(lite + e) = Vec4<kBF16>::pack(a);
       } else if (e < numel) {
         // the matrix's last numel % 4 elements
         for (int64_t j = e; j < numel; ++j) {
@@ -169,13 +184,15 @@ __global__ __launch_bounds__(kE1Threads) void e1_kernel(E1Args args) {
             a = acc[j];
             if (!args.first_step) pp = Elem<GDT>::to_f32(prev[j]);
           }
-          e1_elem<GDT, MONA>(Elem<GDT>::to_f32(graw_v), m, a, pp, args);
+          if (LITE && !args.first_step) a = bf16_to_f32(lite[j]);
+          e1_elem<MODE>(Elem<GDT>::to_f32(graw_v), m, a, pp, args);
           sq += m * m;
           mom[j] = m;
           if (MONA) {
             acc[j] = a;
             prev[j] = graw_v;
           }
+          if (LITE) lite[j] = f32_to_bf16(a);
         }
       }
     }
@@ -190,13 +207,15 @@ __global__ __launch_bounds__(kE1Threads) void e1_kernel(E1Args args) {
         a = acc[j];
         if (!args.first_step) p = Elem<GDT>::to_f32(prev[j]);
       }
-      e1_elem<GDT, MONA>(g, m, a, p, args);
+      if (LITE && !args.first_step) a = bf16_to_f32(lite[j]);
+      e1_elem<MODE>(g, m, a, p, args);
       sq += m * m;
       mom[j] = m;
       if (MONA) {
         acc[j] = a;
         prev[j] = graw_v;
       }
+      if (LITE) lite[j] = f32_to_bf16(a);
     }
   }
   // fixed-order block reduction: lanes (fp64 butterfly), then waves in order
@@ -365,16 +384,21 @@ __global__ __launch_bounds__(kE3Threads) void e3_kernel(E3Args args) {
 }  // namespace
 
 hipError_t launch_e1(const E1Args &args, int blocks, hipStream_t s) {
-  const bool mona = args.mats[0].accel != nullptr;
-  switch (args.grad_dtype * 2 + (mona ? 1 : 0)) {
-    case kF32 * 2 + 0: hipLaunchKernelGGL((e1_kernel<kF32, false>), dim3(blocks), dim3(kE1Threads), 0, s, args); break;
-    case kF32 * 2 + 1: hipLaunchKernelGGL((e1_kernel<kF32, true>), dim3(blocks), dim3(kE1Threads), 0, s, args); break;
-    case kF16 * 2 + 0: hipLaunchKernelGGL((e1_kernel<kF16, false>), dim3(blocks), dim3(kE1Threads), 0, s, args); break;
-    case kF16 * 2 + 1: hipLaunchKernelGGL((e1_kernel<kF16, true>), dim3(blocks), dim3(kE1Threads), 0, s, args); break;
-    case kBF16 * 2 + 0: hipLaunchKernelGGL((e1_kernel<kBF16, false>), dim3(blocks), dim3(kE1Threads), 0, s, args); break;
-    case kBF16 * 2 + 1: hipLaunchKernelGGL((e1_kernel<kBF16, true>), dim3(blocks), dim3(kE1Threads), 0, s, args); break;
+  const dim3 g(blocks), b(kE1Threads);
+#define MUON_E1(GDT, MODE) hipLaunchKernelGGL((e1_kernel<GDT, MODE>), g, b, 0, s, args); break;
+  switch (args.grad_dtype * 3 + args.mode) {
+    case kF32 * 3 + kE1Plain: MUON_E1(kF32, kE1Plain)
+    case kF32 * 3 + kE1Mona: MUON_E1(kF32, kE1Mona)
+    case kF32 * 3 + kE1Lite: MUON_E1(kF32, kE1Lite)
+    case kF16 * 3 + kE1Plain: MUON_E1(kF16, kE1Plain)
+    case kF16 * 3 + kE1Mona: MUON_E1(kF16, kE1Mona)
+    case kF16 * 3 + kE1Lite: MUON_E1(kF16, kE1Lite)
+    case kBF16 * 3 + kE1Plain: MUON_E1(kBF16, kE1Plain)
+    case kBF16 * 3 + kE1Mona: MUON_E1(kBF16, kE1Mona)
+    case kBF16 * 3 + kE1Lite: MUON_E1(kBF16, kE1Lite)
     default: return hipErrorInvalidValue;
   }
+#undef MUON_E1
   return hipGetLastError();
 }
 

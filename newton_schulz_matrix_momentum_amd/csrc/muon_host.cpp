@@ -151,6 +151,8 @@ muon_status check_params(const muon_param *p, int n, const Settings &set) {
     if (!q.weight || !q.grad || !q.momentum) return fail(MUON_ERR_INVALID_ARG, "param %d: weight, grad and momentum must be non-NULL", i);
     if ((q.accel == nullptr) != (q.prev_grad == nullptr))
       return fail(MUON_ERR_INVALID_ARG, "param %d: accel and prev_grad must both be given or both be NULL", i);
+    if (q.mona_lite && q.accel)
+      return fail(MUON_ERR_INVALID_ARG, "param %d: mona_lite cannot be combined with accel / prev_grad", i);
     if (q.rows < 1 || q.cols < 1) return fail(MUON_ERR_INVALID_ARG, "param %d: rows and cols must be >= 1", i);
     if (q.rows > kMaxDim || q.cols > kMaxDim || q.rows * q.cols > kMaxNumel)
       return fail(MUON_ERR_UNSUPPORTED, "param %d: %lld x %lld exceeds the supported size", i, (long long)q.rows, (long long)q.cols);
@@ -165,6 +167,7 @@ muon_status check_params(const muon_param *p, int n, const Settings &set) {
       ranges.push_back({(uintptr_t)q.prev_grad, (uintptr_t)q.prev_grad + gb, i, "prev_grad"});
     }
     if (q.ortho_out) ranges.push_back({(uintptr_t)q.ortho_out, (uintptr_t)q.ortho_out + ne * 4, i, "ortho_out"});
+    if (q.mona_lite) ranges.push_back({(uintptr_t)q.mona_lite, (uintptr_t)q.mona_lite + ne * 2, i, "mona_lite"});
   }
   std::sort(ranges.begin(), ranges.end(), [](const Range &a, const Range &b) { return a.lo < b.lo; });
   for (size_t i = 1; i < ranges.size(); ++i) {
@@ -741,12 +744,13 @@ muon_status muon_step(const muon_param *params, int n, float lr, float mu, float
   double *partials = (double *)(ws + plan.off_partials);
   float *scales = (float *)(ws + plan.off_scales);
 
-  // ---- E1, launched separately for plain and MONA matrices
-  for (int mona = 0; mona < 2; ++mona) {
+  // ---- E1, launched separately for plain, MONA and MONA-Lite matrices
+  for (int mode = kE1Plain; mode <= kE1Lite; ++mode) {
     E1Args a;
     std::memset(&a, 0, sizeof(a));
     for (int j = 0; j < kE1MaxMats; ++j) a.begin[j] = INT32_MAX;
     a.grad_dtype = set.grad_dtype;
+    a.mode = mode;
     a.first_step = set.step == 0 ? 1 : 0;
     a.mu = mu;
     a.beta_a = beta_a;
@@ -765,7 +769,8 @@ muon_status muon_step(const muon_param *params, int n, float lr, float mu, float
       return MUON_OK;
     };
     for (int i = 0; i < n; ++i) {
-      if ((params[i].accel != nullptr) != (mona == 1)) continue;
+      const int m_i = params[i].mona_lite ? kE1Lite : params[i].accel ? kE1Mona : kE1Plain;
+      if (m_i != mode) continue;
       if (a.nmat == kE1MaxMats) {
         st = flush();
         if (st != MUON_OK) return st;
@@ -775,6 +780,7 @@ muon_status muon_step(const muon_param *params, int n, float lr, float mu, float
       m.mom = params[i].momentum;
       m.accel = params[i].accel;
       m.prev = params[i].prev_grad;
+      m.lite = params[i].mona_lite;
       m.numel = params[i].rows * params[i].cols;
       a.begin[a.nmat - 1] = blocks;
       m.partial_off = plan.partial_off[i];
@@ -786,10 +792,12 @@ muon_status muon_step(const muon_param *params, int n, float lr, float mu, float
       m.desc_idx = plan.K > 0 ? plan.classes[plan.cls_of[i]].desc_base + plan.idx_in_cls[i] : -1;
       blocks += plan.e1_blocks[i];
       {
-        // G read, M read+write; MONA: A read+write, G_prev written (and read after step 0)
+        // G read, M read+write; MONA: A read+write, G_prev written (and read
+        // after step 0); MONA-Lite: C written (and read after step 0)
         const double gs = (double)elem_size(set.grad_dtype);
         double per = gs + 8.0;
-        if (mona) per += 8.0 + gs + (set.step == 0 ? 0.0 : gs);
+        if (mode == kE1Mona) per += 8.0 + gs + (set.step == 0 ? 0.0 : gs);
+        if (mode == kE1Lite) per += 2.0 + (set.step == 0 ? 0.0 : 2.0);
         bytes += per * (double)m.numel;
       }
     }

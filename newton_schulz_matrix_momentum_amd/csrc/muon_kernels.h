@@ -23,12 +23,17 @@ constexpr int kE1ElemsPerThread = 32;                      // 8 groups of 4
 constexpr int kE1BlockElems = kE1Threads * kE1ElemsPerThread;  // 8192
 constexpr int kE1MaxMats = 40;
 
+// E1 modes: plain Muon, MONA (A fp32 + previous gradient), MONA-Lite (one
+// bfloat16 state).
+enum E1Mode : int32_t { kE1Plain = 0, kE1Mona = 1, kE1Lite = 2 };
+
 struct FinalDesc;
 struct E1Mat {
   const void *grad;
   float *mom;
-  float *accel;     // nullptr => plain Muon
-  void *prev;       // previous gradient (grad dtype); nullptr iff accel == nullptr
+  float *accel;     // MONA: A
+  void *prev;       // MONA: previous gradient (grad dtype)
+  void *lite;       // MONA-Lite: bfloat16 state
   float *weight;    // for the FinalDesc written by the matrix's block 0
   float *ortho_out;
   int64_t numel;
@@ -45,8 +50,8 @@ struct E1Mat {
 struct E1Args {
   int32_t nmat;
   int32_t grad_dtype;
-  int32_t first_step;    // MONA: D = 0
-  int32_t pad0;
+  int32_t first_step;    // MONA / MONA-Lite: D = 0
+  int32_t mode;          // E1Mode of every matrix of the launch
   float mu, beta_a, alpha, pad1;
   double *partials;      // workspace
   FinalDesc *desc;       // workspace

@@ -43,12 +43,12 @@ def test_struct_layout_matches_header(tmp_path):
 #include <stddef.h>
 #include "muon.h"
 int main(void) {
-  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(muon_param), offsetof(muon_param, grad),
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(muon_param), offsetof(muon_param, grad),
          offsetof(muon_param, prev_grad), offsetof(muon_param, rows), offsetof(muon_param, gamma),
          offsetof(muon_param, ortho_out), sizeof(muon_options), offsetof(muon_options, coeffs),
          offsetof(muon_options, divisor), offsetof(muon_options, step), offsetof(muon_options, trace),
          sizeof(muon_trace), offsetof(muon_trace, capacity), offsetof(muon_trace, group),
-         offsetof(muon_trace, launches));
+         offsetof(muon_trace, launches), offsetof(muon_param, mona_lite));
   return 0;
 }
 ''')
@@ -59,7 +59,7 @@ int main(void) {
     want = [ctypes.sizeof(P), P.grad.offset, P.prev_grad.offset, P.rows.offset, P.gamma.offset, P.ortho_out.offset,
             ctypes.sizeof(O), O.coeffs.offset, O.divisor.offset, O.step.offset, O.trace.offset,
             ctypes.sizeof(_lib.MuonTrace), _lib.MuonTrace.capacity.offset, _lib.MuonTrace.group.offset,
-            _lib.MuonTrace.launches.offset]
+            _lib.MuonTrace.launches.offset, P.mona_lite.offset]
     assert got == want
 
 
@@ -147,6 +147,14 @@ def test_invalid_arguments(lib):
     assert step(lib, [param(0)], o=opts(lib, coeffs=ctypes.cast(bad, ctypes.POINTER(ctypes.c_float)))) == E
     assert step(lib, [param(0)], ws=None) == E
     assert step(lib, [param(0)], ws=BASE * 4 + 8) == E     # unaligned workspace
+    p = param(0, mona=True)
+    p.mona_lite = BASE + 7 * (1 << 28)
+    assert step(lib, [p]) == E                             # MONA-Lite and MONA state together
+    assert "mona_lite" in _lib.last_error()
+    p = param(0)
+    p.mona_lite = p.momentum + 16                          # overlaps momentum
+    assert step(lib, [p]) == E
+    assert "overlap" in _lib.last_error()
 
 
 def test_unsupported(lib):

@@ -18,9 +18,9 @@ from workloads import WORKLOADS, make_grads, make_state
 pytestmark = pytest.mark.gpu
 
 
-def _setup(w, device):
+def _setup(w, device, lite=False):
     gen_dev = device if w.name.startswith("gram_tall") else "cpu"
-    state = make_state(w, device=gen_dev)
+    state = make_state(w, device=gen_dev, mona="lite" if lite else None)
     params = []
     for st in state:
         params.append({k: v.to(device) for k, v in st.items()})
@@ -37,12 +37,12 @@ def _sample_indices(w):
     return idx
 
 
-def _run_workload(name, variant):
+def _run_workload(name, variant, lite=False):
     import newton_schulz_matrix_momentum_amd as nsm
     w = WORKLOADS[name]
     dev = torch.device("cuda:0")
     print("workload %s variant %s: %d matrices" % (name, variant, len(w.shapes)), flush=True)
-    params, gen_dev = _setup(w, dev)
+    params, gen_dev = _setup(w, dev, lite)
     sample = _sample_indices(w)
     for i in sample:
         params[i]["ortho_out"] = torch.empty_like(params[i]["weight"])
@@ -61,7 +61,7 @@ def _run_workload(name, variant):
             n = p["weight"].numel()
             pos = torch.from_numpy(rng.integers(0, n, 16)).to(dev)
             probes.append((i, pos, {k: p[k].flatten()[pos].double().cpu().numpy()
-                                    for k in ("grad", "momentum", "accel", "prev_grad") if k in p}))
+                                    for k in ("grad", "momentum", "accel", "prev_grad", "mona_lite") if k in p}))
         w_gpu_before = {i: to64(params[i]["weight"]) for i in sample}
         nsm.muon_step(params, lr=w.lr, mu=w.mu, beta_a=w.beta_a, alpha=w.alpha, weight_decay=w.weight_decay,
                       ns_steps=w.ns_steps, variant=variant, ns_dtype=w.ns_dtype, coeffs=coeffs.tolist(),
@@ -69,8 +69,16 @@ def _run_workload(name, variant):
         torch.cuda.synchronize()
         for i, pos, before in probes:
             p = params[i]
-            m_ref = w.mu * before["momentum"]
-            if "accel" in before:
+            beta, alpha, mu = (float(np.float32(v)) for v in (w.beta_a, w.alpha, w.mu))
+            m_ref = mu * before["momentum"]
+            if "mona_lite" in before:
+                g = before["grad"]
+                a_ref = np.zeros_like(g) if step == 0 else before["mona_lite"] + (1 - beta) * g
+                c_ref = oracle.round_bf16(beta * a_ref - (1 - beta) * g)
+                m_ref = m_ref + g + alpha * a_ref
+                c_gpu = p["mona_lite"].flatten()[pos].double().cpu().numpy()
+                np.testing.assert_allclose(c_gpu, c_ref, rtol=2.0 ** -7, atol=2.0 ** -21 * float(np.max(np.abs(g))))
+            elif "accel" in before:
                 d = np.zeros_like(before["grad"]) if step == 0 else before["grad"] - before["prev_grad"]
                 a_ref = w.beta_a * before["accel"] + (1 - w.beta_a) * d
                 m_ref = m_ref + before["grad"] + w.alpha * a_ref
@@ -88,7 +96,8 @@ def _run_workload(name, variant):
             ref = oracle.muon_step_matrix(s["weight"], g, s["momentum"], lr=w.lr, mu=w.mu,
                                           weight_decay=w.weight_decay, coeffs=coeffs, variant=variant,
                                           divisor=divisor, restart_every=restart, accel=s.get("accel"),
-                                          prev_grad=s.get("prev_grad"), beta_a=w.beta_a, alpha=w.alpha, step=step)
+                                          prev_grad=s.get("prev_grad"), lite_state=s.get("mona_lite"),
+                                          beta_a=w.beta_a, alpha=w.alpha, step=step)
             p = params[i]
             assert rel_fro(to64(p["momentum"]), ref["momentum"]) <= TOL_STATE
             if "accel" in p:
@@ -100,8 +109,10 @@ def _run_workload(name, variant):
             assert o_err <= tol and dw_err <= tol
             # carry the oracle's own state forward (never the GPU's)
             s["weight"], s["momentum"] = ref["weight"], ref["momentum"]
-            if "accel" in ref:
+            if "prev_grad" in ref:
                 s["accel"], s["prev_grad"] = ref["accel"], ref["prev_grad"]
+            if "lite_state" in ref:
+                s["mona_lite"] = ref["lite_state"]
 
 
 def test_full_single_64x256_f32():
@@ -114,6 +125,10 @@ def test_full_nanochat_6l_d192():
 
 def test_full_llama430m_24l_d1024():
     _run_workload("llama430m_24l_d1024", "direct")
+
+
+def test_full_llama430m_24l_d1024_mona_lite():
+    _run_workload("llama430m_24l_d1024", "direct", lite=True)
 
 
 @pytest.mark.parametrize("variant", ["direct", "gram"])

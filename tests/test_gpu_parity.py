@@ -13,7 +13,8 @@ import pytest
 import torch
 
 import oracle
-from helpers import (compare, draw_grads, make_params, oracle_step, snapshot, to64, rel_fro, TOL_STATE)
+from helpers import (advance_oracle_state, compare, draw_grads, make_params, oracle_state, oracle_step, snapshot,
+                     to64, rel_fro, TOL_STATE, TOL_STATE_LITE)
 
 pytestmark = pytest.mark.gpu
 
@@ -37,19 +38,24 @@ def run_case(shapes, *, grad_dtype, ns_dtype, variant="direct", kind="quintic", 
         p["ortho_out"] = torch.full(p["weight"].shape, float("nan"), dtype=torch.float32, device="cuda")
     coeffs = oracle.coefficient_table(kind, ns_steps)
     worst = (0.0, 0.0)
+    ostate = oracle_state(snapshot(params))   # the oracle carries its own state
+    lite_bounds = {}
     for step in range(steps):
         grads = draw_grads(shapes, grad_dtype, seed * 100 + step, grad_kind)
         for p, g in zip(params, grads):
             p["grad"] = g
         before = snapshot(params)
-        ref = oracle_step(before, grads, lr=lr, mu=mu, wd=wd, coeffs=coeffs, variant=variant, divisor=divisor,
+        ref = oracle_step(ostate, grads, lr=lr, mu=mu, wd=wd, coeffs=coeffs, variant=variant, divisor=divisor,
                           restart_every=restart_every, beta_a=beta_a, alpha=alpha, step=step)
         nsm.muon_step(params, lr=lr, mu=mu, beta_a=beta_a, alpha=alpha, weight_decay=wd, ns_steps=ns_steps,
                       variant=variant, ns_dtype=ns_dtype, coeffs=coeffs.tolist(), divisor=divisor,
                       restart_every=restart_every, step=step)
         torch.cuda.synchronize()
-        w = compare(params, before, ref, grads, ns_dtype, label + " step %d" % step)
+        w = compare(params, before, ref, grads, ns_dtype, label + " step %d" % step, ref_before=ostate,
+                    tol_state=TOL_STATE_LITE if (mona == "lite" and step > 0) else TOL_STATE, beta_a=beta_a,
+                    lite_bounds=lite_bounds)
         worst = (max(worst[0], w[0]), max(worst[1], w[1]))
+        ostate = advance_oracle_state(ostate, ref)
     print("  worst O err %.3g, worst dW err %.3g" % worst, flush=True)
     return worst
 
@@ -289,3 +295,58 @@ def test_trace_per_launch_and_grouped():
     flops = 5 * (4 * (s * (s + 1) * s * 2 + 2 * s * s * s) + 2 * (s * (s + 1) * 768 + s * (s + 1) * s + 2 * s * s * 768))
     assert grp[2][2] == pytest.approx(flops)
     assert grp[2][3] > 0
+
+
+# ---------------------------------------------------------------- MONA-Lite
+
+@pytest.mark.parametrize("grad_dtype", ["f32", "bf16", "f16"])
+def test_mona_lite_three_steps(grad_dtype):
+    """MONA-Lite (one bfloat16 state) over three steps, ragged shapes and
+    every gradient dtype; the state is checked to one bfloat16 spacing."""
+    run_case([(200, 330), (330, 200), (77, 5), (1, 4099), (256, 256)], grad_dtype=grad_dtype, ns_dtype="bf16",
+             mona="lite", steps=3, grad_kind="spectral")
+
+
+def test_mona_lite_gram_fp16():
+    run_case([(300, 700), (700, 300)], grad_dtype="f16", ns_dtype="f16", variant="gram", mona="lite", steps=2,
+             divisor=1.03, restart_every=3)
+
+
+def test_mona_lite_alpha_zero_equals_plain_muon_bitwise():
+    import newton_schulz_matrix_momentum_amd as nsm
+    shapes = [(96, 200), (200, 96)]
+    pl = make_params(shapes, "bf16", "lite", 41)
+    pp = make_params(shapes, "bf16", False, 41)
+    for step in range(2):
+        grads = draw_grads(shapes, "bf16", 410 + step)
+        for a, p, g in zip(pl, pp, grads):
+            a["grad"] = g
+            p["grad"] = g
+        nsm.muon_step(pl, lr=0.02, mu=0.95, beta_a=0.9, alpha=0.0, weight_decay=0.01, ns_dtype="bf16", step=step)
+        nsm.muon_step(pp, lr=0.02, mu=0.95, weight_decay=0.01, ns_dtype="bf16", step=step)
+    torch.cuda.synchronize()
+    for a, p in zip(pl, pp):
+        assert torch.equal(a["weight"], p["weight"])
+        assert torch.equal(a["momentum"], p["momentum"])
+
+
+def test_mona_lite_and_mona_in_one_call():
+    """Plain, MONA and MONA-Lite matrices mixed in one call."""
+    import newton_schulz_matrix_momentum_amd as nsm
+    shapes = [(128, 320), (320, 128), (64, 64)]
+    params = make_params(shapes[:1], "bf16", False, 42) + make_params(shapes[1:2], "bf16", True, 43) + \
+        make_params(shapes[2:], "bf16", "lite", 44)
+    ostate = oracle_state(snapshot(params))
+    lite_bounds = {}
+    for step in range(2):
+        grads = draw_grads(shapes, "bf16", 420 + step)
+        for p, g in zip(params, grads):
+            p["grad"] = g
+        before = snapshot(params)
+        ref = oracle_step(ostate, grads, lr=0.02, mu=0.95, wd=0.01, coeffs=oracle.coefficient_table("quintic", 5),
+                          variant="direct", divisor=1.0, restart_every=0, beta_a=0.9, alpha=0.5, step=step)
+        nsm.muon_step(params, lr=0.02, mu=0.95, beta_a=0.9, alpha=0.5, weight_decay=0.01, ns_dtype="bf16", step=step)
+        torch.cuda.synchronize()
+        compare(params, before, ref, grads, "bf16", "mixed step %d" % step, ref_before=ostate,
+                tol_state=TOL_STATE_LITE if step > 0 else TOL_STATE, lite_bounds=lite_bounds)
+        ostate = advance_oracle_state(ostate, ref)

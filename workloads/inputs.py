@@ -135,7 +135,8 @@ def make_grads(w: Workload, step: int, device="cpu", shapes=None) -> List[torch.
 
 def make_state(w: Workload, device="cpu", shapes=None, mona=None):
     """Initial optimizer state: W ~ N(0, 0.02^2) fp32, M = 0 (fp32), and for
-    MONA A = 0 (fp32) and a previous-gradient buffer (grad dtype, zeros)."""
+    MONA A = 0 (fp32) and a previous-gradient buffer (grad dtype, zeros), or
+    for mona="lite" one bfloat16 MONA-Lite state (zeros)."""
     shapes = shapes or w.shapes
     mona = w.mona if mona is None else mona
     dt = _DTYPES[w.grad_dtype]
@@ -146,7 +147,9 @@ def make_state(w: Workload, device="cpu", shapes=None, mona=None):
             "weight": (0.02 * torch.randn(r, c, generator=gen, dtype=torch.float64, device=device)).float(),
             "momentum": torch.zeros(r, c, dtype=torch.float32, device=device),
         }
-        if mona:
+        if mona == "lite":
+            p["mona_lite"] = torch.zeros(r, c, dtype=torch.bfloat16, device=device)
+        elif mona:
             p["accel"] = torch.zeros(r, c, dtype=torch.float32, device=device)
             p["prev_grad"] = torch.zeros(r, c, dtype=dt, device=device)
         state.append(p)
