@@ -21,4 +21,5 @@ from .muon_oracle import (  # noqa: F401
     decoupled_update,
     muon_step_matrix,
     muon_step,
+    adamw_step,
 )

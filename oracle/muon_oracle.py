@@ -20,6 +20,11 @@ Sources (the pages this follows):
   X (X^T X)^{-1/2} with the inverse square root found by Newton-Schulz on the
   smaller Gram matrix; restarts to control the Gram's eigenvalues; a 1.02-1.05
   safety divisor so that the eigenvalues land in [0, 1].
+* The same MONA summary, "Ontwerprichtlijnen": vector-shaped parameters
+  (embeddings, biases) keep AdamW, as in Muon.  The pages give AdamW no
+  formula or hyper-parameters; the oracle follows the textbook decoupled
+  form (I. Loshchilov, F. Hutter, "Decoupled Weight Decay Regularization",
+  ICLR 2019, Algorithm 2, with the bias corrections of Adam).
 * Textbook Newton-Schulz for the polar factor (N. J. Higham, "Functions of
   Matrices", 2008, section 8.3): the cubic map X <- (3X - X X^T X)/2, which
   needs sigma_max(X) < sqrt(3); Frobenius normalisation guarantees
@@ -263,6 +268,26 @@ def muon_step_matrix(weight, grad, momentum, *, lr, mu, weight_decay, coeffs,
     out["ortho"] = o
     out["weight"] = decoupled_update(weight, o, lr, weight_decay, gamma)
     return out
+
+
+def adamw_step(param, grad, exp_avg, exp_avg_sq, *, step: int, lr: float, beta1: float, beta2: float,
+               eps: float, weight_decay: float):
+    """Decoupled AdamW (Loshchilov & Hutter 2019, Algorithm 2) for one tensor;
+    ``step`` is 0-based, so t = step + 1 in the bias corrections:
+        m = beta1 m + (1 - beta1) g,       v = beta2 v + (1 - beta2) g^2
+        m^ = m / (1 - beta1^t),            v^ = v / (1 - beta2^t)
+        p = p - lr (m^ / (sqrt(v^) + eps) + weight_decay p)
+    Returns (p, m, v) in float64.
+    """
+    g = np.asarray(grad, dtype=np.float64)
+    p = np.asarray(param, dtype=np.float64)
+    m = beta1 * np.asarray(exp_avg, dtype=np.float64) + (1.0 - beta1) * g
+    v = beta2 * np.asarray(exp_avg_sq, dtype=np.float64) + (1.0 - beta2) * g * g
+    t = step + 1
+    m_hat = m / (1.0 - beta1 ** t)
+    v_hat = v / (1.0 - beta2 ** t)
+    p_new = p - lr * (m_hat / (np.sqrt(v_hat) + eps) + weight_decay * p)
+    return p_new, m, v
 
 
 def muon_step(params: Iterable[dict], *, lr, mu, weight_decay, coeffs, variant="direct",

@@ -482,3 +482,44 @@ def test_mona_lite_alpha_zero_is_plain_muon():
         np.testing.assert_array_equal(rl["weight"], rp["weight"])
         w_l, m_l, c = rl["weight"], rl["momentum"], rl["lite_state"]
         w_p, m_p = rp["weight"], rp["momentum"]
+
+
+# ---------------------------------------------------------------- AdamW (vector parameters)
+
+def test_adamw_matches_torch_adamw_float64():
+    """The textbook decoupled AdamW against torch.optim.AdamW (an independent
+    implementation) in float64 over 5 steps."""
+    import torch
+    rng = np.random.default_rng(9)
+    hp = dict(lr=3e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1)
+    p0 = rng.standard_normal(257)
+    tp = torch.nn.Parameter(torch.from_numpy(p0.copy()))
+    opt = torch.optim.AdamW([tp], lr=hp["lr"], betas=(hp["beta1"], hp["beta2"]), eps=hp["eps"],
+                            weight_decay=hp["weight_decay"])
+    p, m, v = p0.copy(), np.zeros(257), np.zeros(257)
+    for step in range(5):
+        g = rng.standard_normal(257) * 10.0 ** rng.uniform(-3, 1)
+        tp.grad = torch.from_numpy(g.copy())
+        opt.step()
+        p, m, v = oracle.adamw_step(p, g, m, v, step=step, **hp)
+        np.testing.assert_allclose(p, tp.detach().numpy(), rtol=1e-13, atol=1e-15)
+        np.testing.assert_allclose(m, opt.state[tp]["exp_avg"].numpy(), rtol=1e-13, atol=1e-16)
+        np.testing.assert_allclose(v, opt.state[tp]["exp_avg_sq"].numpy(), rtol=1e-13, atol=1e-18)
+
+
+def test_adamw_first_step_is_signed_step():
+    """At t = 1 the bias corrections give m^ = g and v^ = g^2, so the update
+    is lr g / (|g| + eps): a step of ~lr against the gradient's sign."""
+    g = np.array([3.0, -0.5, 1e-3, 0.0])
+    p, m, v = oracle.adamw_step(np.zeros(4), g, np.zeros(4), np.zeros(4), step=0, lr=0.01, beta1=0.9,
+                                beta2=0.999, eps=1e-8, weight_decay=0.0)
+    np.testing.assert_allclose(p, -0.01 * g / (np.abs(g) + 1e-8), rtol=1e-14, atol=0)
+    np.testing.assert_allclose(m, 0.1 * g)
+    np.testing.assert_allclose(v, 0.001 * g * g)
+
+
+def test_adamw_zero_gradient_is_pure_decay():
+    p0 = np.array([1.0, -2.0])
+    p, _, _ = oracle.adamw_step(p0, np.zeros(2), np.zeros(2), np.zeros(2), step=3, lr=0.1, beta1=0.9,
+                                beta2=0.99, eps=1e-8, weight_decay=0.5)
+    np.testing.assert_allclose(p, p0 * (1 - 0.1 * 0.5))
