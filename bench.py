@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--trace-steps", type=int, default=None, help="steps timed per launch (default: --steps)")
+    ap.add_argument("--adamw", type=int, default=0, metavar="MELEMS",
+                    help="only time muon_adamw_step over a synthetic set of MELEMS million vector-parameter "
+                         "elements (bf16 grads) and print its own JSON line")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB --steps times (counter calibration)")
     return ap.parse_args()
@@ -85,6 +88,51 @@ def copy_probe(args):
         y.copy_(x)
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "launches": args.steps}), flush=True)
+
+
+def adamw_probe(args):
+    """AdamW over a synthetic vector-parameter set: 96 tensors whose sizes span
+    three decades (norm weights to embedding rows), ``args.adamw`` million
+    elements in all, bf16 gradients.  Kernel time from HIP events around the
+    library's launches (muon_trace, grouped)."""
+    import torch
+    import newton_schulz_matrix_momentum_amd as nsm
+    from newton_schulz_matrix_momentum_amd import _lib
+    gen = torch.Generator().manual_seed(7)
+    w = 10.0 ** (3.0 * torch.rand(96, generator=gen, dtype=torch.float64))
+    sizes = [max(1, int(v)) for v in (w / w.sum() * args.adamw * 1e6).tolist()]
+    dev = torch.device("cuda:0")
+    params = [{"param": torch.randn(n, device=dev), "grad": torch.randn(n, device=dev).to(torch.bfloat16),
+               "exp_avg": torch.zeros(n, device=dev), "exp_avg_sq": torch.zeros(n, device=dev)} for n in sizes]
+    hp = dict(lr=3e-4, betas=(0.9, 0.95), eps=1e-8, weight_decay=0.1)
+    for s in range(args.warmup):
+        nsm.adamw_step(params, step=s, **hp)
+    torch.cuda.synchronize()
+    cap = 8
+    ev = HipEvents(2 * cap)
+    stages = (ctypes.c_int32 * cap)()
+    work = (ctypes.c_double * cap)()
+    nl = (ctypes.c_int32 * cap)()
+    tr = _lib.MuonTrace(events=ctypes.cast(ev.arr, ctypes.POINTER(ctypes.c_void_p)),
+                        stages=ctypes.cast(stages, ctypes.POINTER(ctypes.c_int32)),
+                        work=ctypes.cast(work, ctypes.POINTER(ctypes.c_double)), capacity=cap, count=0,
+                        group=1, launches=ctypes.cast(nl, ctypes.POINTER(ctypes.c_int32)))
+    ms = bytes_ = 0.0
+    launches = 0
+    for s in range(args.steps):
+        nsm.adamw_step(params, step=args.warmup + s, trace=tr, **hp)
+        torch.cuda.synchronize()
+        for i in range(min(tr.count, cap)):
+            ms += ev.elapsed_ms(2 * i, 2 * i + 1)
+            bytes_ += work[i]
+            launches += nl[i]
+    ev.close()
+    gbps = bytes_ / (ms * 1e-3) / 1e9
+    print(json.dumps({"metric": "AdamW GB/s (vector parameters)", "value": gbps, "unit": "GB/s",
+                      "higher_is_better": True, "tensors": len(sizes), "elements": sum(sizes),
+                      "ms_per_step": ms / args.steps, "launches_per_step": launches / args.steps,
+                      "bytes_per_step": bytes_ / args.steps, "frac_of_hbm": gbps / PEAK_HBM_GBPS,
+                      "grad_dtype": "bf16", "data": "synthetic"}), flush=True)
 
 
 class HipEvents:
@@ -277,6 +325,9 @@ def main():
         sys.exit(1)
     if args.copy_probe:
         copy_probe(args)
+        return
+    if args.adamw:
+        adamw_probe(args)
         return
     w = WORKLOADS[args.workload]
     variant = args.variant or w.variants[0]

@@ -93,7 +93,8 @@ typedef enum muon_stage {
   MUON_STAGE_NORM = 1,   /* per-matrix normalisation scale                     */
   MUON_STAGE_E2 = 2,     /* X0 in the Newton-Schulz dtype, both orientations   */
   MUON_STAGE_GEMM = 3,   /* one grouped Newton-Schulz matrix product           */
-  MUON_STAGE_E3 = 4      /* decoupled weight-decay update                      */
+  MUON_STAGE_E3 = 4,     /* decoupled weight-decay update                      */
+  MUON_STAGE_ADAMW = 5   /* AdamW over vector parameters (muon_adamw_step)     */
 } muon_stage;
 
 /* Optional launch timing.  When muon_options.trace is non-NULL the library
@@ -165,6 +166,34 @@ muon_status muon_step(const muon_param *params, int n,
                       float lr, float mu, float beta_a, float alpha, float lambda,
                       int ns_steps, muon_variant variant, const muon_options *opts,
                       void *workspace, size_t workspace_bytes, void *stream);
+
+/* One vector-shaped parameter (bias, norm weight, embedding: anything the
+ * caller keeps out of Muon) and its AdamW state.  Every buffer holds numel
+ * contiguous elements on the device; none may overlap another. */
+typedef struct muon_adamw_param {
+  float *param;         /* fp32, updated in place                                  */
+  const void *grad;     /* grad_dtype, read only                                   */
+  float *exp_avg;       /* fp32 first moment m, updated; zero before step 0        */
+  float *exp_avg_sq;    /* fp32 second moment v, updated; zero before step 0       */
+  int64_t numel;        /* >= 1                                                    */
+} muon_adamw_param;
+
+/* One decoupled AdamW step over `n` tensors (n >= 0), the optimizer the MONA
+ * summary ("Ontwerprichtlijnen") keeps for vector-shaped parameters.  The
+ * pages give no formula; this is the textbook decoupled form (Loshchilov &
+ * Hutter 2019, Algorithm 2), with t = step + 1:
+ *     m = beta1 m + (1 - beta1) g ;  v = beta2 v + (1 - beta2) g^2
+ *     p = p - lr (m / (1 - beta1^t) / (sqrt(v / (1 - beta2^t)) + eps) + weight_decay p)
+ * All tensors of a call share grad_dtype and the hyper-parameters, and are
+ * updated by one launch per 64 tensors on `stream`.  `trace` (optional) records
+ * the launches as MUON_STAGE_ADAMW (see muon_trace).
+ * Errors: MUON_ERR_INVALID_ARG for NULL pointers, numel < 1, non-finite
+ * scalars, beta1 or beta2 outside [0, 1), eps < 0, step < 0, overlapping
+ * buffers; MUON_ERR_UNSUPPORTED for an unknown grad_dtype or numel above
+ * 2^31 - 1; MUON_ERR_HIP when a launch fails. */
+muon_status muon_adamw_step(const muon_adamw_param *params, int n, muon_dtype grad_dtype,
+                            float lr, float beta1, float beta2, float eps, float weight_decay,
+                            int64_t step, muon_trace *trace, void *stream);
 
 /* Static description of a status code. */
 const char *muon_status_string(muon_status s);

@@ -5,7 +5,7 @@ kernels); this package is its Python binding.  PyTorch provides device memory
 and streams only.
 """
 from ._lib import MuonError, load, version, last_error, EXPORTS  # noqa: F401
-from .api import muon_step, muon_workspace_size, Workspace  # noqa: F401
+from .api import muon_step, muon_workspace_size, adamw_step, Workspace  # noqa: F401
 from .optim import Muon  # noqa: F401
 
-__all__ = ["muon_step", "muon_workspace_size", "Workspace", "Muon", "MuonError", "load", "version"]
+__all__ = ["muon_step", "muon_workspace_size", "adamw_step", "Workspace", "Muon", "MuonError", "load", "version"]

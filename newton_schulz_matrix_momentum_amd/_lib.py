@@ -24,7 +24,7 @@ MUON_F32, MUON_F16, MUON_BF16 = 0, 1, 2
 MUON_NS_DIRECT, MUON_NS_GRAM = 0, 1
 
 # every entry point declared in include/muon.h
-EXPORTS = ("muon_options_init", "muon_workspace_size", "muon_step", "muon_status_string",
+EXPORTS = ("muon_options_init", "muon_workspace_size", "muon_step", "muon_adamw_step", "muon_status_string",
            "muon_last_error", "muon_version")
 
 
@@ -55,8 +55,8 @@ class MuonTrace(ctypes.Structure):
     ]
 
 
-MUON_STAGE_E1, MUON_STAGE_NORM, MUON_STAGE_E2, MUON_STAGE_GEMM, MUON_STAGE_E3 = range(5)
-STAGE_NAMES = {0: "e1", 1: "norm", 2: "e2", 3: "gemm", 4: "e3"}
+MUON_STAGE_E1, MUON_STAGE_NORM, MUON_STAGE_E2, MUON_STAGE_GEMM, MUON_STAGE_E3, MUON_STAGE_ADAMW = range(6)
+STAGE_NAMES = {0: "e1", 1: "norm", 2: "e2", 3: "gemm", 4: "e3", 5: "adamw"}
 
 
 class MuonOptions(ctypes.Structure):
@@ -68,6 +68,16 @@ class MuonOptions(ctypes.Structure):
         ("restart_every", ctypes.c_int32),
         ("step", ctypes.c_int64),
         ("trace", ctypes.POINTER(MuonTrace)),
+    ]
+
+
+class MuonAdamwParam(ctypes.Structure):
+    _fields_ = [
+        ("param", ctypes.c_void_p),
+        ("grad", ctypes.c_void_p),
+        ("exp_avg", ctypes.c_void_p),
+        ("exp_avg_sq", ctypes.c_void_p),
+        ("numel", ctypes.c_int64),
     ]
 
 
@@ -102,6 +112,10 @@ def load(path: str = LIB_PATH):
                               ctypes.c_int, ctypes.c_int, ctypes.POINTER(MuonOptions),
                               ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.muon_step.restype = ctypes.c_int
+    lib.muon_adamw_step.argtypes = [ctypes.POINTER(MuonAdamwParam), ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                                    ctypes.c_int64, ctypes.POINTER(MuonTrace), ctypes.c_void_p]
+    lib.muon_adamw_step.restype = ctypes.c_int
     lib.muon_status_string.argtypes = [ctypes.c_int]
     lib.muon_status_string.restype = ctypes.c_char_p
     lib.muon_last_error.argtypes = []

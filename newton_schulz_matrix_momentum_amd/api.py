@@ -1,8 +1,9 @@
 """Python entry points with the C ABI's names, over torch tensors.
 
 ``muon_step`` and ``muon_workspace_size`` marshal torch tensors into
-``muon_param`` records and call libmuon; the stream is torch's current stream
-on the tensors' device.  Tensors must be contiguous and live on the GPU.
+``muon_param`` records and call libmuon; ``adamw_step`` does the same for
+``muon_adamw_param``.  The stream is torch's current stream on the tensors'
+device.  Tensors must be contiguous and live on the GPU.
 """
 from __future__ import annotations
 
@@ -150,3 +151,38 @@ def muon_step(params: Sequence[Dict], *, lr: float, mu: float, beta_a: float = 0
     _lib.check(lib.muon_step(arr, n, float(lr), float(mu), float(beta_a), float(alpha), float(weight_decay),
                              int(ns_steps), _VARIANTS[variant], ctypes.byref(opts), ctypes.c_void_p(ws.data_ptr()),
                              ws.numel(), ctypes.c_void_p(stream)))
+
+
+def adamw_step(params: Sequence[Dict], *, lr: float, betas=(0.9, 0.999), eps: float = 1e-8,
+               weight_decay: float = 0.0, step: int = 0, trace=None) -> None:
+    """One decoupled AdamW step (``muon_adamw_step``) over ``params``: dicts of
+    ``param`` (fp32, updated), ``grad``, ``exp_avg`` and ``exp_avg_sq`` (fp32,
+    updated; zero before step 0), any shape, all grads of one dtype.
+    ``step`` is 0-based.  Enqueued on the current stream."""
+    n = len(params)
+    arr = (_lib.MuonAdamwParam * max(n, 1))()
+    grad_dtype = None
+    device = None
+    for i, p in enumerate(params):
+        t = p["param"]
+        g = p["grad"]
+        if grad_dtype is None:
+            grad_dtype = g.dtype
+        elif g.dtype != grad_dtype:
+            raise ValueError("all grads of one call must share a dtype (param %d is %s, expected %s)"
+                             % (i, g.dtype, grad_dtype))
+        device = device or t.device
+        for key in ("grad", "exp_avg", "exp_avg_sq"):
+            if p[key].device != t.device:
+                raise ValueError("adamw param %d: %s is on %s, param on %s" % (i, key, p[key].device, t.device))
+        arr[i].param = _ptr(t, "param", torch.float32)
+        arr[i].grad = _ptr(g, "grad", None, tuple(t.shape))
+        arr[i].exp_avg = _ptr(p["exp_avg"], "exp_avg", torch.float32, tuple(t.shape))
+        arr[i].exp_avg_sq = _ptr(p["exp_avg_sq"], "exp_avg_sq", torch.float32, tuple(t.shape))
+        arr[i].numel = t.numel()
+    lib = _lib.load()
+    stream = torch.cuda.current_stream(device).cuda_stream if device is not None else 0
+    _lib.check(lib.muon_adamw_step(arr, n, _DT[grad_dtype] if grad_dtype is not None else _lib.MUON_F32,
+                                   float(lr), float(betas[0]), float(betas[1]), float(eps), float(weight_decay),
+                                   int(step), ctypes.pointer(trace) if trace is not None else None,
+                                   ctypes.c_void_p(stream)))

@@ -381,6 +381,74 @@ __global__ __launch_bounds__(kE3Threads) void e3_kernel(E3Args args) {
   }
 }
 
+// ------------------------------------------------------------------ AdamW
+// Decoupled AdamW (MONA summary, "Ontwerprichtlijnen": vector parameters
+// keep AdamW; the update is the textbook one of Loshchilov & Hutter 2019,
+// Algorithm 2):  m = b1 m + (1-b1) g ; v = b2 v + (1-b2) g^2 ;
+// p = p - lr wd p - (lr / (1-b1^t)) m / (sqrt(v) / sqrt(1-b2^t) + eps).
+template <int GDT>
+__device__ __forceinline__ void adam_elem(float g, float &p, float &m, float &v, const AdamArgs &a) {
+  m = a.beta1 * m + a.one_minus_beta1 * g;
+  v = a.beta2 * v + a.one_minus_beta2 * (g * g);
+  const float denom = sqrtf(v) * a.inv_sqrt_bc2 + a.eps;
+  p = p - a.decay * p - a.step_size * (m / denom);
+}
+
+template <int GDT>
+__global__ __launch_bounds__(kAdamThreads) void adamw_kernel(AdamArgs args) {
+  typedef typename Elem<GDT>::raw graw;
+  typedef typename Vec4<GDT>::type gvec;
+  constexpr int G = kAdamBlockElems / kAdamThreads / 4;   // groups of 4 per thread
+  const int ti = find_mat(args.begin, (int)blockIdx.x);
+  const AdamTensor &t = args.t[ti];
+  const int64_t base = ((int64_t)blockIdx.x - args.begin[ti]) * kAdamBlockElems;
+  const graw *grad = (const graw *)t.grad;
+  if (t.vec_ok) {
+    gvec gv[G];
+    float4 pv[G], mv[G], vv[G];
+#pragma unroll
+    for (int it = 0; it < G; ++it) {
+      const int64_t e = base + ((int64_t)it * kAdamThreads + threadIdx.x) * 4;
+      if (e + 4 <= t.numel) {
+        gv[it] = *(const gvec *)(grad + e);
+        pv[it] = *(const float4 *)(t.param + e);
+        mv[it] = *(const float4 *)(t.m + e);
+        vv[it] = *(const float4 *)(t.v + e);
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < G; ++it) {
+      const int64_t e = base + ((int64_t)it * kAdamThreads + threadIdx.x) * 4;
+      if (e + 4 <= t.numel) {
+        float g[4], p[4] = {pv[it].x, pv[it].y, pv[it].z, pv[it].w}, m[4] = {mv[it].x, mv[it].y, mv[it].z, mv[it].w},
+              v[4] = {vv[it].x, vv[it].y, vv[it].z, vv[it].w};
+        Vec4<GDT>::unpack(gv[it], g);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) adam_elem<GDT>(g[q], p[q], m[q], v[q], args);
+        *(float4 *)(t.param + e) = make_float4(p[0], p[1], p[2], p[3]);
+        *(float4 *)(t.m + e) = make_float4(m[0], m[1], m[2], m[3]);
+        *(float4 *)(t.v + e) = make_float4(v[0], v[1], v[2], v[3]);
+      } else if (e < t.numel) {
+        for (int64_t j = e; j < t.numel; ++j) {
+          float p = t.param[j], m = t.m[j], v = t.v[j];
+          adam_elem<GDT>(Elem<GDT>::to_f32(grad[j]), p, m, v, args);
+          t.param[j] = p;
+          t.m[j] = m;
+          t.v[j] = v;
+        }
+      }
+    }
+  } else {
+    for (int64_t j = base + threadIdx.x; j < t.numel && j < base + kAdamBlockElems; j += kAdamThreads) {
+      float p = t.param[j], m = t.m[j], v = t.v[j];
+      adam_elem<GDT>(Elem<GDT>::to_f32(grad[j]), p, m, v, args);
+      t.param[j] = p;
+      t.m[j] = m;
+      t.v[j] = v;
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_e1(const E1Args &args, int blocks, hipStream_t s) {
@@ -422,6 +490,16 @@ hipError_t launch_e3(const E3Args &args, int blocks, hipStream_t s) {
     case kF32: hipLaunchKernelGGL(e3_kernel<kF32>, dim3(blocks), dim3(kE3Threads), 0, s, args); break;
     case kF16: hipLaunchKernelGGL(e3_kernel<kF16>, dim3(blocks), dim3(kE3Threads), 0, s, args); break;
     case kBF16: hipLaunchKernelGGL(e3_kernel<kBF16>, dim3(blocks), dim3(kE3Threads), 0, s, args); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_adamw(const AdamArgs &args, int blocks, hipStream_t s) {
+  switch (args.grad_dtype) {
+    case kF32: hipLaunchKernelGGL(adamw_kernel<kF32>, dim3(blocks), dim3(kAdamThreads), 0, s, args); break;
+    case kF16: hipLaunchKernelGGL(adamw_kernel<kF16>, dim3(blocks), dim3(kAdamThreads), 0, s, args); break;
+    case kBF16: hipLaunchKernelGGL(adamw_kernel<kBF16>, dim3(blocks), dim3(kAdamThreads), 0, s, args); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -46,7 +46,7 @@ muon_status fail(muon_status s, const char *fmt, ...) {
 
 constexpr int kMaxSteps = 64;
 static_assert(sizeof(GemmArgs) <= 4096 && sizeof(E1Args) <= 4096 && sizeof(E2Args) <= 4096 &&
-                  sizeof(E3Args) <= 4096 && sizeof(NormArgs) <= 4096,
+                  sizeof(E3Args) <= 4096 && sizeof(NormArgs) <= 4096 && sizeof(AdamArgs) <= 4096,
               "kernel arguments must stay within 4 KB");
 constexpr int64_t kMaxDim = int64_t(1) << 20;
 constexpr int64_t kMaxNumel = (int64_t(1) << 31) - 1;
@@ -929,6 +929,94 @@ muon_status muon_step(const muon_param *params, int n, float lr, float mu, float
     }
     if (a.nmat) HIP_TRY(tr.run(MUON_STAGE_E3, bytes, [&]() { return launch_e3(a, blocks, hs); }));
   }
+  HIP_TRY(tr.close());
+  g_last_error.clear();
+  return MUON_OK;
+}
+
+muon_status muon_adamw_step(const muon_adamw_param *params, int n, muon_dtype grad_dtype, float lr, float beta1,
+                            float beta2, float eps, float weight_decay, int64_t step, muon_trace *trace,
+                            void *stream) {
+  if (n < 0) return fail(MUON_ERR_INVALID_ARG, "n must be >= 0");
+  if (n > 0 && !params) return fail(MUON_ERR_INVALID_ARG, "params is NULL");
+  if (grad_dtype != MUON_F32 && grad_dtype != MUON_F16 && grad_dtype != MUON_BF16)
+    return fail(MUON_ERR_UNSUPPORTED, "unknown grad_dtype %d", (int)grad_dtype);
+  if (!is_finite(lr) || !is_finite(beta1) || !is_finite(beta2) || !is_finite(eps) || !is_finite(weight_decay))
+    return fail(MUON_ERR_INVALID_ARG, "lr, beta1, beta2, eps and weight_decay must be finite");
+  if (beta1 < 0.0f || beta1 >= 1.0f || beta2 < 0.0f || beta2 >= 1.0f)
+    return fail(MUON_ERR_INVALID_ARG, "beta1 and beta2 must lie in [0, 1)");
+  if (eps < 0.0f) return fail(MUON_ERR_INVALID_ARG, "eps must be >= 0");
+  if (step < 0) return fail(MUON_ERR_INVALID_ARG, "step must be >= 0");
+  if (trace && trace->capacity > 0 && (!trace->events || !trace->stages || !trace->work || (trace->group && !trace->launches)))
+    return fail(MUON_ERR_INVALID_ARG, "trace arrays are NULL");
+  const int gs = elem_size((int)grad_dtype);
+  std::vector<Range> ranges;
+  ranges.reserve((size_t)n * 4);
+  for (int i = 0; i < n; ++i) {
+    const muon_adamw_param &q = params[i];
+    if (!q.param || !q.grad || !q.exp_avg || !q.exp_avg_sq)
+      return fail(MUON_ERR_INVALID_ARG, "adamw param %d: param, grad, exp_avg and exp_avg_sq must be non-NULL", i);
+    if (q.numel < 1) return fail(MUON_ERR_INVALID_ARG, "adamw param %d: numel must be >= 1", i);
+    if (q.numel > kMaxNumel) return fail(MUON_ERR_UNSUPPORTED, "adamw param %d: %lld elements exceed the supported size", i, (long long)q.numel);
+    const uint64_t ne = (uint64_t)q.numel;
+    ranges.push_back({(uintptr_t)q.param, (uintptr_t)q.param + ne * 4, i, "param"});
+    ranges.push_back({(uintptr_t)q.grad, (uintptr_t)q.grad + ne * (uint64_t)gs, i, "grad"});
+    ranges.push_back({(uintptr_t)q.exp_avg, (uintptr_t)q.exp_avg + ne * 4, i, "exp_avg"});
+    ranges.push_back({(uintptr_t)q.exp_avg_sq, (uintptr_t)q.exp_avg_sq + ne * 4, i, "exp_avg_sq"});
+  }
+  std::sort(ranges.begin(), ranges.end(), [](const Range &a, const Range &b) { return a.lo < b.lo; });
+  for (size_t i = 1; i < ranges.size(); ++i)
+    if (ranges[i].lo < ranges[i - 1].hi)
+      return fail(MUON_ERR_INVALID_ARG, "buffers overlap: adamw param %d %s and adamw param %d %s", ranges[i - 1].param,
+                  ranges[i - 1].what, ranges[i].param, ranges[i].what);
+  if (trace) trace->count = 0;
+  if (n == 0) {
+    g_last_error.clear();
+    return MUON_OK;
+  }
+  hipStream_t hs = (hipStream_t)stream;
+  Tracer tr{trace, hs};
+  AdamArgs a;
+  std::memset(&a, 0, sizeof(a));
+  const double t = (double)step + 1.0;
+  a.grad_dtype = (int32_t)grad_dtype;
+  a.beta1 = beta1;
+  a.beta2 = beta2;
+  a.one_minus_beta1 = (float)(1.0 - (double)beta1);
+  a.one_minus_beta2 = (float)(1.0 - (double)beta2);
+  a.step_size = (float)((double)lr / (1.0 - std::pow((double)beta1, t)));
+  a.inv_sqrt_bc2 = (float)(1.0 / std::sqrt(1.0 - std::pow((double)beta2, t)));
+  a.eps = eps;
+  a.decay = (float)((double)lr * (double)weight_decay);
+  int blocks = 0;
+  double bytes = 0.0;
+  auto reset = [&]() {
+    a.nt = 0;
+    for (int j = 0; j < kAdamMaxTensors; ++j) a.begin[j] = INT32_MAX;
+    blocks = 0;
+    bytes = 0.0;
+  };
+  reset();
+  for (int i = 0; i < n; ++i) {
+    if (a.nt == kAdamMaxTensors) {
+      HIP_TRY(tr.run(MUON_STAGE_ADAMW, bytes, [&]() { return launch_adamw(a, blocks, hs); }));
+      reset();
+    }
+    const muon_adamw_param &q = params[i];
+    AdamTensor &d = a.t[a.nt];
+    d.param = q.param;
+    d.grad = q.grad;
+    d.m = q.exp_avg;
+    d.v = q.exp_avg_sq;
+    d.numel = q.numel;
+    d.vec_ok = (((((uintptr_t)q.param) | ((uintptr_t)q.exp_avg) | ((uintptr_t)q.exp_avg_sq)) & 15) == 0 &&
+                (((uintptr_t)q.grad) & (gs == 4 ? 15 : 7)) == 0) ? 1 : 0;
+    a.begin[a.nt] = blocks;
+    a.nt++;
+    blocks += (int)((q.numel + kAdamBlockElems - 1) / kAdamBlockElems);
+    bytes += (24.0 + (double)gs) * (double)q.numel;   // p, m, v read + written, g read
+  }
+  if (a.nt) HIP_TRY(tr.run(MUON_STAGE_ADAMW, bytes, [&]() { return launch_adamw(a, blocks, hs); }));
   HIP_TRY(tr.close());
   g_last_error.clear();
   return MUON_OK;

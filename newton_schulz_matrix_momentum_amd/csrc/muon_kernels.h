@@ -179,11 +179,39 @@ struct GemmArgs {
   GemmClass cls[kGemmMaxClasses];
 };
 
+// ------------------------------------------------------------------ AdamW
+// Decoupled AdamW over a list of fp32 tensors (vector-shaped parameters).
+constexpr int kAdamThreads = 256;
+constexpr int kAdamBlockElems = kAdamThreads * 16;
+constexpr int kAdamMaxTensors = 64;
+struct AdamTensor {
+  float *param;
+  const void *grad;
+  float *m;
+  float *v;
+  int64_t numel;
+  int32_t vec_ok;        // 16-byte aligned fp32 buffers, 8-byte aligned 16-bit grad
+  int32_t pad;
+};
+struct AdamArgs {
+  int32_t nt;
+  int32_t grad_dtype;
+  float beta1, beta2;
+  float one_minus_beta1, one_minus_beta2;
+  float step_size;       // lr / (1 - beta1^t)
+  float inv_sqrt_bc2;    // 1 / sqrt(1 - beta2^t)
+  float eps;
+  float decay;           // lr * weight_decay
+  int32_t begin[kAdamMaxTensors];   // first block of each tensor (see E1Args)
+  AdamTensor t[kAdamMaxTensors];
+};
+
 // Launchers (return the launch status).
 hipError_t launch_e1(const E1Args &args, int blocks, hipStream_t s);
 hipError_t launch_norm(const NormArgs &args, hipStream_t s);
 hipError_t launch_e2(const E2Args &args, int blocks, hipStream_t s);
 hipError_t launch_e3(const E3Args &args, int blocks, hipStream_t s);
+hipError_t launch_adamw(const AdamArgs &args, int blocks, hipStream_t s);
 // tile = 64 or 128 (square block tile); dtype selects the operand type.
 hipError_t launch_gemm(const GemmArgs &args, int dtype, int tile, hipStream_t s);
 

@@ -201,3 +201,61 @@ def test_product_path_has_no_oracle_import():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text, f
                 assert "numpy" not in text, f
+
+
+# ---------------------------------------------------------------- AdamW entry point
+
+def test_adamw_param_layout_matches_header(tmp_path):
+    src = tmp_path / "adam_layout.c"
+    src.write_text(r'''
+#include <stdio.h>
+#include <stddef.h>
+#include "muon.h"
+int main(void) {
+  printf("%zu %zu %zu %zu %zu\n", sizeof(muon_adamw_param), offsetof(muon_adamw_param, grad),
+         offsetof(muon_adamw_param, exp_avg), offsetof(muon_adamw_param, exp_avg_sq), offsetof(muon_adamw_param, numel));
+  return 0;
+}
+''')
+    exe = tmp_path / "adam_layout"
+    subprocess.check_call(["gcc", "-std=c99", "-Wall", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)])
+    got = [int(v) for v in subprocess.check_output([str(exe)]).split()]
+    A = _lib.MuonAdamwParam
+    assert got == [ctypes.sizeof(A), A.grad.offset, A.exp_avg.offset, A.exp_avg_sq.offset, A.numel.offset]
+
+
+def adam_param(i, numel=1000):
+    a = _lib.MuonAdamwParam()
+    step = 1 << 28
+    a.param = BASE + i * 8 * step
+    a.grad = BASE + (i * 8 + 1) * step
+    a.exp_avg = BASE + (i * 8 + 2) * step
+    a.exp_avg_sq = BASE + (i * 8 + 3) * step
+    a.numel = numel
+    return a
+
+
+def adam(lib, ps, n=None, dtype=_lib.MUON_F32, lr=1e-3, b1=0.9, b2=0.999, eps=1e-8, wd=0.0, step=0):
+    arr_ = (_lib.MuonAdamwParam * max(len(ps), 1))(*ps)
+    return lib.muon_adamw_step(arr_, len(ps) if n is None else n, dtype, lr, b1, b2, eps, wd, step, None, None)
+
+
+def test_adamw_validation(lib):
+    E, U = _lib.MUON_ERR_INVALID_ARG, _lib.MUON_ERR_UNSUPPORTED
+    assert lib.muon_adamw_step(None, 0, 0, 1e-3, 0.9, 0.999, 1e-8, 0.0, 0, None, None) == _lib.MUON_OK
+    assert adam(lib, [adam_param(0)], n=-1) == E
+    assert adam(lib, [adam_param(0, numel=0)]) == E
+    p = adam_param(0)
+    p.exp_avg = None
+    assert adam(lib, [p]) == E
+    assert adam(lib, [adam_param(0)], b1=1.0) == E
+    assert adam(lib, [adam_param(0)], b2=-0.1) == E
+    assert adam(lib, [adam_param(0)], eps=-1e-8) == E
+    assert adam(lib, [adam_param(0)], lr=float("nan")) == E
+    assert adam(lib, [adam_param(0)], step=-1) == E
+    assert adam(lib, [adam_param(0)], dtype=7) == U
+    assert adam(lib, [adam_param(0, numel=1 << 31)]) == U
+    a, b = adam_param(0), adam_param(1)
+    b.exp_avg_sq = a.param + 8          # inside a's param
+    assert adam(lib, [a, b]) == E
+    assert "overlap" in _lib.last_error()

@@ -350,3 +350,79 @@ def test_mona_lite_and_mona_in_one_call():
         compare(params, before, ref, grads, "bf16", "mixed step %d" % step, ref_before=ostate,
                 tol_state=TOL_STATE_LITE if step > 0 else TOL_STATE, lite_bounds=lite_bounds)
         ostate = advance_oracle_state(ostate, ref)
+
+
+# ---------------------------------------------------------------- AdamW (vector parameters)
+
+def _adam_case(sizes, grad_dtype, steps, hp, seed, offset_first=False):
+    import newton_schulz_matrix_momentum_amd as nsm
+    from helpers import f32
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[grad_dtype]
+    gen = torch.Generator().manual_seed(seed)
+    params, ref = [], []
+    for k, n in enumerate(sizes):
+        p0 = torch.randn(n, generator=gen, dtype=torch.float64).float()
+        if offset_first and k == 0:
+            # a view 4 bytes into its buffer: the unaligned element-wise path
+            p = torch.zeros(n + 1, device="cuda")[1:]
+            p.copy_(p0.cuda())
+        else:
+            p = p0.cuda()
+        params.append({"param": p, "exp_avg": torch.zeros(n, device="cuda"), "exp_avg_sq": torch.zeros(n, device="cuda")})
+        ref.append((p0.double().numpy(), np.zeros(n), np.zeros(n)))
+    for step in range(steps):
+        for q in params:
+            n = q["param"].numel()
+            q["grad"] = (torch.randn(n, generator=gen, dtype=torch.float64) * 10.0 ** (3 * torch.rand(1, generator=gen).item() - 2)).to(dt).cuda()
+        nsm.adamw_step(params, lr=hp["lr"], betas=(hp["beta1"], hp["beta2"]), eps=hp["eps"],
+                       weight_decay=hp["weight_decay"], step=step)
+        torch.cuda.synchronize()
+        new_ref = []
+        for q, (p, m, v) in zip(params, ref):
+            p, m, v = oracle.adamw_step(p, to64(q["grad"]), m, v, step=step, lr=f32(hp["lr"]), beta1=f32(hp["beta1"]),
+                                        beta2=f32(hp["beta2"]), eps=f32(hp["eps"]), weight_decay=f32(hp["weight_decay"]))
+            # fp32 arithmetic: each quantity within a few fp32 ulp of its size per step
+            np.testing.assert_allclose(to64(q["exp_avg"]), m, rtol=1e-5, atol=1e-6 * np.abs(m).max())
+            np.testing.assert_allclose(to64(q["exp_avg_sq"]), v, rtol=1e-5, atol=1e-6 * np.abs(v).max())
+            dp_gpu = to64(q["param"]) - p                       # vs the oracle's own trajectory
+            assert np.max(np.abs(dp_gpu)) <= 1e-5 * (np.abs(p).max() + hp["lr"] * (step + 1)), (step, np.max(np.abs(dp_gpu)))
+            new_ref.append((p, m, v))
+        ref = new_ref
+
+
+@pytest.mark.parametrize("grad_dtype", ["f32", "bf16", "f16"])
+def test_adamw_matches_oracle(grad_dtype):
+    """Ragged sizes (1, 3, one block, one block +/- 1, multi-block), three steps."""
+    hp = dict(lr=3e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1)
+    _adam_case([1, 3, 4095, 4096, 4097, 100003, 192], grad_dtype, 3, hp, seed=51, offset_first=True)
+
+
+def test_adamw_many_tensors_and_late_step():
+    """More tensors than one launch holds (64), and bias corrections at a
+    large step count."""
+    hp = dict(lr=1e-3, beta1=0.8, beta2=0.999, eps=1e-6, weight_decay=0.0)
+    _adam_case([17 + 13 * k for k in range(70)], "bf16", 2, hp, seed=52)
+
+
+def test_optimizer_routes_vectors_to_adamw():
+    """The torch.optim wrapper: 2-D weights take the Muon step, a bias and a
+    norm vector take AdamW, in one optimizer step."""
+    import newton_schulz_matrix_momentum_amd as nsm
+    from helpers import f32
+    torch.manual_seed(53)
+    w = torch.nn.Parameter(torch.randn(96, 160, device="cuda") * 0.02)
+    b = torch.nn.Parameter(torch.randn(96, device="cuda"))
+    w0, b0 = w.detach().clone(), b.detach().clone()
+    opt = nsm.Muon([w, b], lr=0.02, momentum=0.95, weight_decay=0.01, ns_dtype="bf16", adamw_lr=1e-3,
+                   adamw_betas=(0.9, 0.95), adamw_eps=1e-8, adamw_weight_decay=0.05)
+    w.grad = torch.randn(96, 160, device="cuda")
+    b.grad = torch.randn(96, device="cuda")
+    opt.step()
+    torch.cuda.synchronize()
+    r = oracle.muon_step_matrix(to64(w0), to64(w.grad), np.zeros((96, 160)), lr=f32(0.02), mu=f32(0.95),
+                                weight_decay=f32(0.01), coeffs=oracle.coefficient_table("quintic", 5))
+    assert rel_fro(to64(w) - to64(w0), r["weight"] - to64(w0)) < 2e-2
+    pb, _, _ = oracle.adamw_step(to64(b0), to64(b.grad), np.zeros(96), np.zeros(96), step=0, lr=f32(1e-3),
+                                 beta1=f32(0.9), beta2=f32(0.95), eps=f32(1e-8), weight_decay=f32(0.05))
+    np.testing.assert_allclose(to64(b), pb, rtol=1e-6, atol=1e-7)
+    assert opt.state[b]["step"] == 1 and "exp_avg" in opt.state[b] and "momentum" in opt.state[w]
