@@ -18,8 +18,11 @@ enum DType : int32_t { kF32 = 0, kF16 = 1, kBF16 = 2 };
 
 // ------------------------------------------------------------------ E1
 // MONA difference + EMA, momentum, per-block partial sums of M^2.
-constexpr int kE1Threads = 256;
-constexpr int kE1ElemsPerThread = 32;                      // 8 groups of 4
+#ifndef MUON_E1_THREADS
+#define MUON_E1_THREADS 1024
+#endif
+constexpr int kE1Threads = MUON_E1_THREADS;
+constexpr int kE1ElemsPerThread = 8192 / kE1Threads;       // groups of 4
 constexpr int kE1BlockElems = kE1Threads * kE1ElemsPerThread;  // 8192
 constexpr int kE1MaxMats = 40;
 

@@ -649,7 +649,6 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(GemmArgs args) {
 // ---------------------------------------------------------------------------
 // Stage formats shared by the 16-bit DMA kernels.
 constexpr int kBigTile = 256;
-constexpr int kBigRowBytes = 64;   // 32 x 16-bit k per stage row (64 x 64 tile)
 #ifndef MUON_A_AHEAD
 #define MUON_A_AHEAD 3
 #endif
@@ -777,23 +776,23 @@ __global__ __launch_bounds__(2 * WN_WAVES * 64, 1) void ns_gemm_wide_kernel(Gemm
 // ---------------------------------------------------------------------------
 // 64 x 64 block tile for fp16 / bf16 at small sizes, where a step is a chain
 // of memory latencies rather than MFMA work.  Four waves of 32 x 32.  The
-// operands move global -> LDS by DMA into unpadded 64-byte rows (32 k per
-// stage, 8 KB for A and B; 16-byte chunk c of row r stored at chunk
-// c ^ ((r >> 1) & 3)), in a ring of RING stages that is filled up front:
-// a K <= 32 RING panel costs one memory round trip.  Stages are consumed in
-// groups of 4 with one barrier per group; after the barrier the slots of the
-// previous group are refilled with the stages RING ahead.
+// operands move global -> LDS by DMA in 64-k stages of 128-byte rows (A and
+// B: 16 KB), so each 8-lane group of a DMA instruction fetches one whole
+// 128-byte line (8 rows x 128 bytes per instruction); 16-byte chunk c of row
+// r stored at c ^ (r & 7).  Ring of RING stages: RING <= 6 holds the whole K
+// and is filled up front (a K <= 64 RING panel costs one memory round trip);
+// RING == 8 is refilled, two stages consumed per barrier.  Cin is prefetched
+// before the K loop.
 constexpr int kSmallTile = 64;
-constexpr int kSmallStage = 2 * kSmallTile * kBigRowBytes;   // 8 KB
-constexpr int kSmallGroup = 4;
+constexpr int kSmallStage = 2 * kSmallTile * kWideRowBytes;   // 16 KB
+constexpr int kSmallGroup = 2;
 
-// RING < 16 is launched only when the whole K fits in the ring (no refill);
-// RING == 16 refills and keeps at least two groups of look-ahead.
 template <typename T, int RING>
 __global__ __launch_bounds__(kThreads) void ns_gemm_small_kernel(GemmArgs args) {
   static_assert(sizeof(T) == 2, "16-bit operands only");
-  static_assert(RING < 16 || RING >= 2 * kSmallGroup, "refilling ring needs two groups of look-ahead");
+  static_assert(RING < 8 || RING >= 2 * kSmallGroup, "refilling ring needs two groups of look-ahead");
   constexpr int FM = 2, FN = 2;
+  constexpr int PER_STAGE = 4;   // DMA instructions per stage and wave
   __shared__ __attribute__((aligned(1024))) char lds[RING * kSmallStage];
 
   const TileRef tr = locate_tile(args);
@@ -807,17 +806,19 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_small_kernel(GemmArgs args) 
   const char *B = (const char *)cl.b + ((int64_t)mat * cl.sb + (int64_t)tn * kSmallTile * cl.ldb) * 2;
   const int64_t lda_b = (int64_t)cl.lda * 2, ldb_b = (int64_t)cl.ldb * 2;
 
-  // DMA: wave w moves rows [16 w, 16 w + 16) of A and of B (one instruction
-  // each per stage); lane L covers row L / 4 and physical chunk L % 4.
-  const int dma_row = lane >> 2;
-  const int dma_chunk = (lane & 3) ^ ((dma_row >> 1) & 3);
+  // DMA: wave w moves rows [16 w, 16 w + 16) of A and of B, 8 rows per
+  // instruction; lane L covers row L / 8 of the group and physical chunk
+  // L % 8, which holds logical chunk (L % 8) ^ (L / 8).
+  const int dma_row = lane >> 3;
+  const int dma_chunk = (lane & 7) ^ dma_row;
   const char *a_src = A + (int64_t)(wave * 16 + dma_row) * lda_b + dma_chunk * 16;
   const char *b_src = B + (int64_t)(wave * 16 + dma_row) * ldb_b + dma_chunk * 16;
 
   const int fr_row = lane & 15;
-  const int fr_chunk = ((lane >> 4) ^ ((fr_row >> 1) & 3)) * 16;
-  const int a_frag = (wm * 32 + fr_row) * kBigRowBytes + fr_chunk;
-  const int b_frag = (kSmallTile + wn * 32 + fr_row) * kBigRowBytes + fr_chunk;
+  const int a_frag = (wm * 32 + fr_row) * kWideRowBytes;
+  const int b_frag = (kSmallTile + wn * 32 + fr_row) * kWideRowBytes;
+  const int chunk0 = (((lane >> 4)) ^ (lane & 7)) * 16;
+  const int chunk1 = ((4 + (lane >> 4)) ^ (lane & 7)) * 16;
 
   f32x4 acc[FM][FN];
 #pragma unroll
@@ -827,15 +828,18 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_small_kernel(GemmArgs args) 
   float cin[FM][FN][4];
   load_cin<T, FM, FN>(cl, mat, tm * kSmallTile + wm * 32, tn * kSmallTile + wn * 32, cin);
 
-  const int nk = cl.K / (kBigRowBytes / 2);
+  const int nk = cl.K / (kWideRowBytes / 2);
   if (nk > 0) {
     auto dma = [&](int kb) {
-      char *dst = lds + (kb % RING) * kSmallStage + wave * 1024;
-      __builtin_amdgcn_global_load_lds((const void *)(a_src + (int64_t)kb * kBigRowBytes),
-                                       (void __attribute__((address_space(3))) *)dst, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void *)(b_src + (int64_t)kb * kBigRowBytes),
-                                       (void __attribute__((address_space(3))) *)(dst + kSmallTile * kBigRowBytes),
-                                       16, 0, 0);
+      char *dst = lds + (kb % RING) * kSmallStage + wave * 2048;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        __builtin_amdgcn_global_load_lds((const void *)(a_src + (int64_t)j * 8 * lda_b + (int64_t)kb * kWideRowBytes),
+                                         (void __attribute__((address_space(3))) *)(dst + j * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void *)(b_src + (int64_t)j * 8 * ldb_b + (int64_t)kb * kWideRowBytes),
+                                         (void __attribute__((address_space(3))) *)(dst + kSmallTile * kWideRowBytes + j * 1024),
+                                         16, 0, 0);
+      }
     };
     const int first = min(nk, RING);
 #pragma unroll 1
@@ -845,13 +849,13 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_small_kernel(GemmArgs args) 
 #pragma unroll 1
     for (int g = 0; g < ngroups; ++g) {
       const int s0 = g * kSmallGroup, s1 = min(nk, s0 + kSmallGroup);
-      // stages after this group may stay in flight (2 DMA per stage and wave)
-      waitcnt_vm(2 * (issued - s1));
+      // stages after this group may stay in flight
+      waitcnt_vm(PER_STAGE * (issued - s1));
       __builtin_amdgcn_sched_barrier(0);
       asm volatile("s_barrier" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
       // every wave is past group g-1: refill its slots with the stages RING ahead
-      if constexpr (RING >= 16) {
+      if constexpr (RING >= 8) {
         if (g > 0) {
           const int r1 = min(nk, s0 + RING);
 #pragma unroll 1
@@ -861,15 +865,19 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_small_kernel(GemmArgs args) 
 #pragma unroll 1
       for (int kb = s0; kb < s1; ++kb) {
         const char *st = lds + (kb % RING) * kSmallStage;
-        u32x4 fa[FM], fb[FN];
 #pragma unroll
-        for (int i = 0; i < FM; ++i) fa[i] = *(const u32x4 *)(st + a_frag + i * 16 * kBigRowBytes);
+        for (int ks = 0; ks < 2; ++ks) {
+          const int ch = ks ? chunk1 : chunk0;
+          u32x4 fa[FM], fb[FN];
 #pragma unroll
-        for (int j = 0; j < FN; ++j) fb[j] = *(const u32x4 *)(st + b_frag + j * 16 * kBigRowBytes);
+          for (int i = 0; i < FM; ++i) fa[i] = *(const u32x4 *)(st + a_frag + i * 16 * kWideRowBytes + ch);
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+          for (int j = 0; j < FN; ++j) fb[j] = *(const u32x4 *)(st + b_frag + j * 16 * kWideRowBytes + ch);
 #pragma unroll
-          for (int j = 0; j < FN; ++j) Mma<T>::run(fa[i], fb[j], acc[i][j]);
+          for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) Mma<T>::run(fa[i], fb[j], acc[i][j]);
+        }
       }
     }
   }
@@ -882,18 +890,18 @@ hipError_t launch_t(const GemmArgs &args, int tile, hipStream_t s) {
   switch (tile) {
     case 64:
       if constexpr (sizeof(T) == 2) {
-        // ring just deep enough for the longest K of the launch (max 16 stages)
+        // ring just deep enough for the longest K of the launch (8 stages
+        // and refills beyond), so more blocks fit per CU
         int kmax = 0;
         for (int c = 0; c < args.nclass; ++c) kmax = max(kmax, args.cls[c].K);
-        const int nk = kmax / (kBigRowBytes / 2);
+        const int nk = kmax / (kWideRowBytes / 2);
         const dim3 g(args.total_tiles), b(kThreads);
-        // the ring is as small as the longest K allows, so more blocks fit per CU
-        if (nk <= 2) hipLaunchKernelGGL((ns_gemm_small_kernel<T, 2>), g, b, 0, s, args);
+        if (nk <= 1) hipLaunchKernelGGL((ns_gemm_small_kernel<T, 1>), g, b, 0, s, args);
+        else if (nk <= 2) hipLaunchKernelGGL((ns_gemm_small_kernel<T, 2>), g, b, 0, s, args);
+        else if (nk <= 3) hipLaunchKernelGGL((ns_gemm_small_kernel<T, 3>), g, b, 0, s, args);
         else if (nk <= 4) hipLaunchKernelGGL((ns_gemm_small_kernel<T, 4>), g, b, 0, s, args);
         else if (nk <= 6) hipLaunchKernelGGL((ns_gemm_small_kernel<T, 6>), g, b, 0, s, args);
-        else if (nk <= 8) hipLaunchKernelGGL((ns_gemm_small_kernel<T, 8>), g, b, 0, s, args);
-        else if (nk <= 12) hipLaunchKernelGGL((ns_gemm_small_kernel<T, 12>), g, b, 0, s, args);
-        else hipLaunchKernelGGL((ns_gemm_small_kernel<T, 16>), g, b, 0, s, args);
+        else hipLaunchKernelGGL((ns_gemm_small_kernel<T, 8>), g, b, 0, s, args);
       } else {
         hipLaunchKernelGGL((ns_gemm_kernel<T, 64, 64>), dim3(args.total_tiles), dim3(kThreads), 0, s, args);
       }
