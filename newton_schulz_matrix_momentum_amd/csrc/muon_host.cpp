@@ -344,9 +344,11 @@ struct StageBuilder {
   Tracer &tr;
   std::vector<GemmClass> per_class;
   std::vector<double> per_flops;
+  std::vector<char> skip;   // classes launched elsewhere in this stage
   explicit StageBuilder(const Plan &p, char *w, Tracer &t) : plan(p), ws(w), tr(t) {
     per_class.resize(p.classes.size());
     per_flops.assign(p.classes.size(), 0.0);
+    skip.assign(p.classes.size(), 0);
   }
   hipError_t launch() {
     for (int tile : {64, 128, 256}) {
@@ -363,7 +365,7 @@ struct StageBuilder {
         return tr.run(MUON_STAGE_GEMM, flops, [&]() { return launch_gemm(a, dt, tile, tr.s); });
       };
       for (size_t c = 0; c < per_class.size(); ++c) {
-        if (plan.classes[c].tile != tile) continue;
+        if (plan.classes[c].tile != tile || skip[c]) continue;
         GemmClass g = per_class[c];
         if (args.nclass == kGemmMaxClasses) {
           hipError_t e = go();
@@ -496,6 +498,76 @@ std::vector<DirectStep> direct_steps(const Plan &plan, double sx0) {
   return out;
 }
 
+// Direct steps of classes with a short side of at most 192 (16-bit, 64
+// tiles) form B = b A + c A^2 inside the update launch
+// (ns_poly_update_kernel) instead of in a launch of its own: at these sizes
+// a launch costs more than the redundant panel products.
+bool poly_fused(const Plan &plan, const ClassInfo &cl) {
+  return plan.set.ns_dtype != kF32 && cl.tile == 64 && cl.Sp <= 192;
+}
+
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// Launch the fused update of every poly_fused class, one launch per padded
+// short side.  Output row tiles are grouped per block (sharing the block's
+// panel of B) just enough for the launch to fit the device in one wave of
+// blocks.
+hipError_t launch_poly_stage(const Plan &plan, Tracer &tr, const std::vector<GemmClass> &gc,
+                             const std::vector<double> &flops, const std::vector<char> &use) {
+  for (int sp : {64, 128, 192}) {
+    int64_t pairs = 0;
+    for (size_t c = 0; c < gc.size(); ++c)
+      if (use[c] && plan.classes[c].Sp == sp) pairs += (int64_t)gc[c].count * gc[c].m_tiles * gc[c].tiles_n;
+    if (pairs == 0) continue;
+    const int64_t cap = (int64_t)device_cus() * poly_blocks_per_cu(sp);
+    const int group = (int)std::min<int64_t>(poly_max_group(sp), std::max<int64_t>(1, (pairs + cap - 1) / cap));
+    GemmArgs args;
+    double work = 0.0;
+    auto reset = [&]() {
+      std::memset(&args, 0, sizeof(args));
+      for (int i = 0; i < kGemmMaxClasses; ++i) args.tile_begin[i] = INT32_MAX;
+      work = 0.0;
+    };
+    auto go = [&]() -> hipError_t {
+      const GemmArgs a = args;
+      const int dt = plan.set.ns_dtype;
+      return tr.run(MUON_STAGE_GEMM, work, [&]() { return launch_poly_update(a, dt, sp, tr.s); });
+    };
+    reset();
+    for (size_t c = 0; c < gc.size(); ++c) {
+      if (!use[c] || plan.classes[c].Sp != sp) continue;
+      GemmClass g = gc[c];
+      g.m_group = group;
+      g.tiles_m = (g.m_tiles + group - 1) / group;
+      g.tiles_per_mat = g.tiles_m * g.tiles_n;
+      if (args.nclass == kGemmMaxClasses) {
+        hipError_t e = go();
+        if (e != hipSuccess) return e;
+        reset();
+      }
+      args.tile_begin[args.nclass] = args.total_tiles;
+      args.cls[args.nclass++] = g;
+      args.total_tiles += g.tiles_per_mat * g.count;
+      work += flops[c] * (double)g.count;
+    }
+    if (args.nclass > 0) {
+      hipError_t e = go();
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
 muon_status run_direct(const Plan &plan, char *ws, Tracer &st, double sx0, float lr, float wd, NsResult &res) {
   const size_t es = (size_t)elem_size(plan.set.ns_dtype);
   const std::vector<DirectStep> steps = direct_steps(plan, sx0);
@@ -515,9 +587,17 @@ muon_status run_direct(const Plan &plan, char *ws, Tracer &st, double sx0, float
       }
       HIP_TRY(sb.launch());
     }
-    // B = b A + c A^2
+    // B = b A + c A^2 (fused into the update for poly_fused classes)
+    std::vector<char> fuse(plan.classes.size(), 0);
+    bool any_fused = false;
+    if (!ds.cubic)
+      for (size_t ci = 0; ci < plan.classes.size(); ++ci) {
+        fuse[ci] = poly_fused(plan, plan.classes[ci]) ? 1 : 0;
+        any_fused = any_fused || fuse[ci];
+      }
     if (!ds.cubic) {
       StageBuilder sb(plan, ws, st);
+      sb.skip = fuse;
       for (size_t ci = 0; ci < plan.classes.size(); ++ci) {
         const ClassInfo &cl = plan.classes[ci];
         GemmClass g = make_gemm(cl, es, ws, cl.sq[0], cl.Sp, cl.Sp, cl.sq[0], cl.Sp, cl.Sp, cl.Sp, true);
@@ -534,6 +614,9 @@ muon_status run_direct(const Plan &plan, char *ws, Tracer &st, double sx0, float
     // O (true scale) goes straight into the weight update
     {
       StageBuilder sb(plan, ws, st);
+      sb.skip = fuse;
+      std::vector<GemmClass> pg(plan.classes.size());
+      std::vector<double> pf(plan.classes.size(), 0.0);
       for (size_t ci = 0; ci < plan.classes.size(); ++ci) {
         const ClassInfo &cl = plan.classes[ci];
         GemmClass g = make_gemm(cl, es, ws, cl.XT[cur], cl.Lp, cl.Sp, cl.sq[1], cl.Sp, cl.Sp, cl.Sp, false);
@@ -545,7 +628,17 @@ muon_status run_direct(const Plan &plan, char *ws, Tracer &st, double sx0, float
         g.beta = (float)ds.upd_beta;
         sb.per_class[ci] = g;
         sb.per_flops[ci] = full_flops(cl);
+        if (fuse[ci]) {
+          // same product with A in place of B; the block forms its panel of B
+          g.b = ws + cl.sq[0];
+          g.sq_alpha = (float)ds.sq_alpha;
+          g.sq_beta = (float)ds.sq_beta;
+          g.m_tiles = (int32_t)(cl.Lp / 64);
+          pg[ci] = g;
+          pf[ci] = full_flops(cl) + half_flops(cl, cl.s);
+        }
       }
+      if (any_fused) HIP_TRY(launch_poly_stage(plan, st, pg, pf, fuse));
       HIP_TRY(sb.launch());
     }
     cur = 1 - cur;

@@ -174,6 +174,12 @@ struct GemmClass {
   int32_t desc_base;
   const FinalDesc *desc;
   float lr, wd;
+  // Fused polynomial update (launch_poly_update only): b points at the
+  // symmetric s x s matrix A, and each block first forms its panel of
+  // B = sq_alpha A A + sq_beta A in LDS.  Output tile rows come in groups
+  // of m_group tiles (of m_tiles), one group per block: tiles_m counts groups.
+  float sq_alpha, sq_beta;
+  int32_t m_group, m_tiles;
 };
 struct GemmArgs {
   int32_t nclass;
@@ -217,5 +223,12 @@ hipError_t launch_e3(const E3Args &args, int blocks, hipStream_t s);
 hipError_t launch_adamw(const AdamArgs &args, int blocks, hipStream_t s);
 // tile = 64 or 128 (square block tile); dtype selects the operand type.
 hipError_t launch_gemm(const GemmArgs &args, int dtype, int tile, hipStream_t s);
+// X'^T = alpha X^T (sq_alpha A A + sq_beta A) + beta X^T for short sides
+// padded to sp (64, 128 or 192; every class of the launch has K == sp),
+// 16-bit dtypes only.  m_group <= poly_max_group(sp) <= kPolyMaxGroup.
+constexpr int kPolyMaxGroup = 4;
+int poly_blocks_per_cu(int sp);
+int poly_max_group(int sp);
+hipError_t launch_poly_update(const GemmArgs &args, int dtype, int sp, hipStream_t s);
 
 }  // namespace muon

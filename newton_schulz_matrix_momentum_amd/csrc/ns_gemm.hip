@@ -33,7 +33,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // s_waitcnt vmcnt(n), leaving expcnt and lgkmcnt alone.  gfx9 encoding:
-// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].  n >= 32 waits
+// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].  n >= 64 waits
 // for vmcnt(0) (always safe).
 #define MUON_VMCNT(n) (0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
 #define MUON_VMCASE(n) case n: __builtin_amdgcn_s_waitcnt(MUON_VMCNT(n)); break;
@@ -43,7 +43,12 @@ __device__ __forceinline__ void waitcnt_vm(int n) {
     MUON_VMCASE(8) MUON_VMCASE(9) MUON_VMCASE(10) MUON_VMCASE(11) MUON_VMCASE(12) MUON_VMCASE(13) MUON_VMCASE(14)
     MUON_VMCASE(15) MUON_VMCASE(16) MUON_VMCASE(17) MUON_VMCASE(18) MUON_VMCASE(19) MUON_VMCASE(20) MUON_VMCASE(21)
     MUON_VMCASE(22) MUON_VMCASE(23) MUON_VMCASE(24) MUON_VMCASE(25) MUON_VMCASE(26) MUON_VMCASE(27) MUON_VMCASE(28)
-    MUON_VMCASE(29) MUON_VMCASE(30) MUON_VMCASE(31)
+    MUON_VMCASE(29) MUON_VMCASE(30) MUON_VMCASE(31) MUON_VMCASE(32) MUON_VMCASE(33) MUON_VMCASE(34)
+    MUON_VMCASE(35) MUON_VMCASE(36) MUON_VMCASE(37) MUON_VMCASE(38) MUON_VMCASE(39) MUON_VMCASE(40) MUON_VMCASE(41)
+    MUON_VMCASE(42) MUON_VMCASE(43) MUON_VMCASE(44) MUON_VMCASE(45) MUON_VMCASE(46) MUON_VMCASE(47) MUON_VMCASE(48)
+    MUON_VMCASE(49) MUON_VMCASE(50) MUON_VMCASE(51) MUON_VMCASE(52) MUON_VMCASE(53) MUON_VMCASE(54) MUON_VMCASE(55)
+    MUON_VMCASE(56) MUON_VMCASE(57) MUON_VMCASE(58) MUON_VMCASE(59) MUON_VMCASE(60) MUON_VMCASE(61) MUON_VMCASE(62)
+    MUON_VMCASE(63)
     default: __builtin_amdgcn_s_waitcnt(MUON_VMCNT(0)); break;
   }
 }
@@ -779,10 +784,10 @@ __global__ __launch_bounds__(2 * WN_WAVES * 64, 1) void ns_gemm_wide_kernel(Gemm
 // operands move global -> LDS by DMA in 64-k stages of 128-byte rows (A and
 // B: 16 KB), so each 8-lane group of a DMA instruction fetches one whole
 // 128-byte line (8 rows x 128 bytes per instruction); 16-byte chunk c of row
-// r stored at c ^ (r & 7).  Ring of RING stages: RING <= 6 holds the whole K
+// r stored at c ^ (r & 7).  Ring of RING stages: RING <= 8 holds the whole K
 // and is filled up front (a K <= 64 RING panel costs one memory round trip);
-// RING == 8 is refilled, two stages consumed per barrier.  Cin is prefetched
-// before the K loop.
+// longer K refill the ring of 8, two stages consumed per barrier.  Cin is
+// prefetched before the K loop.
 constexpr int kSmallTile = 64;
 constexpr int kSmallStage = 2 * kSmallTile * kWideRowBytes;   // 16 KB
 constexpr int kSmallGroup = 2;
@@ -885,6 +890,365 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_small_kernel(GemmArgs args) 
                             cin);
 }
 
+// ---------------------------------------------------------------------------
+// Fused polynomial update of a direct Newton-Schulz step for short sides
+// s <= 192 (padded to SP):
+//   X'^T = alpha X^T B + beta X^T,   B = sq_alpha A A + sq_beta A,
+// with A = X X^T symmetric (Muon post: the quintic step a X + (b A + c A^2) X).
+// At these sizes every launch is a chain of memory latencies, so the square
+// A A is not a launch of its own: each block loads all of A (SP x SP) into
+// LDS, forms its 64-row panel of B there (rounded to T exactly as the
+// separate square product stores it), and then runs the update product for a
+// group of up to poly_max_group(SP) output tiles that share the panel.
+//
+// LDS (64-k stages of 128-byte rows, chunk c of row r at c ^ (r & 7)):
+//   region 0  all of A (SP / 64 stages of SP rows); once the panel is formed:
+//             X^T tiles 2 and 3 of the group and the epilogue's staging tiles
+//   panel     SP / 64 stages of 64 rows (rows of B for this block's columns)
+//   X^T       tiles 0 and 1 of the group (SP / 64 stages of 64 rows each)
+// The panel product is computed transposed, P^T = A A_panel^T (A symmetric),
+// so each lane's accumulator holds 4 consecutive k of one panel row and is
+// written with one 8-byte LDS store.  Every X^T tile has landed before the
+// first global store, so the vmcnt-counted DMA waits never count stores.
+//
+// Epilogue per output tile: v = alpha acc + beta X^T (X^T read from LDS) is
+// staged as fp32 in a 64 x 64 tile (two staging tiles alternate, so one
+// barrier per output tile suffices); a row-major sweep stores X'^T rows (or
+// applies the fp32 weight update of a tall W) and a transposed sweep stores
+// the X' copy (or the update of a wide W), 16 bytes per access.  The next
+// tile's operands are read from LDS while the current one is staged.
+template <int SP>
+struct PolyLayout {
+  static constexpr int A_BYTES = SP * SP * 2;
+  static constexpr int P_BYTES = SP * 128;              // 64 rows over all k
+  static constexpr int MAXG = SP == 192 ? 4 : 2;        // tiles 2, 3 need room in region 0
+  static constexpr int S_BYTES = 64 * 64 * 4;            // one fp32 staging tile
+  // staging tiles: SP = 192: region 0 after X^T tiles 2, 3, and the X^T tile 0
+  // buffer once tile 0 is done; otherwise the first two slots of region 0
+  static constexpr int S0_OFF = SP == 192 ? 2 * P_BYTES : 0;
+  static constexpr int R0_BYTES = SP == 192 ? A_BYTES : (A_BYTES > 2 * S_BYTES ? A_BYTES : 2 * S_BYTES);
+  static constexpr int TOTAL = R0_BYTES + 3 * P_BYTES;
+  static_assert(MAXG <= kPolyMaxGroup, "group bound");
+  static_assert(SP != 192 || (S0_OFF + S_BYTES <= A_BYTES && S_BYTES <= P_BYTES), "staging fits");
+};
+
+// Staging position of (row r, column c) of a 64 x 64 fp32 tile: 16-column
+// groups permuted per row so that MFMA-layout writes (4 rows 4 apart x 16
+// columns) and column reads of 16-row groups hit distinct banks, while each
+// 16-column group of a row stays contiguous for row reads.
+__device__ __forceinline__ int spos(int r, int c) { return r * 64 + (c ^ ((((r >> 2) ^ (r >> 4)) & 3) << 4)); }
+
+template <typename T, int SP>
+__global__ __launch_bounds__(kThreads) void ns_poly_update_kernel(GemmArgs args) {
+  static_assert(sizeof(T) == 2, "16-bit operands only");
+  static_assert(SP == 64 || SP == 128 || SP == 192, "short side padded to 64, 128 or 192");
+  typedef PolyLayout<SP> L;
+  constexpr int NST = SP / 64;          // k stages
+  constexpr int NKS = 2 * NST;          // 32-k MFMA steps
+  constexpr int FM1 = SP / 64;          // 16-row blocks per wave in the panel product (SP / 4 rows)
+  constexpr int A_DMA = SP / 32;        // DMA instructions per wave and stage of A (8 rows each)
+  constexpr int X_DMA = 2 * NST;        // DMA instructions per wave for one X^T tile
+  __shared__ __attribute__((aligned(1024))) char lds[L::TOTAL];
+  char *const la = lds;
+  char *const lp = lds + L::R0_BYTES;
+  char *const lx = lp + L::P_BYTES;
+
+  const TileRef tr = locate_tile(args);
+  const GemmClass &cl = args.cls[tr.ci];
+  const int mat = tr.mat, tn = tr.tn;
+  const int tm0 = tr.tm * cl.m_group;
+  const int nt = min(cl.m_group, cl.m_tiles - tm0);   // in [1, MAXG] by construction
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  const char *Am = (const char *)cl.b + (int64_t)mat * cl.sb * 2;
+  const char *Xm = (const char *)cl.a + (int64_t)mat * cl.sa * 2;
+  const int64_t lda_b = (int64_t)cl.lda * 2, ldb_b = (int64_t)cl.ldb * 2;
+  const int dma_row = lane >> 3;
+  const int dma_chunk = (lane & 7) ^ dma_row;
+
+  // all of A, stage by stage: wave w moves rows [w SP/4, (w+1) SP/4)
+#pragma unroll
+  for (int kb = 0; kb < NST; ++kb) {
+#pragma unroll
+    for (int j = 0; j < A_DMA; ++j) {
+      const int r0 = wave * (SP / 4) + j * 8;
+      __builtin_amdgcn_global_load_lds(
+          (const void *)(Am + (int64_t)(r0 + dma_row) * ldb_b + kb * kWideRowBytes + dma_chunk * 16),
+          (void __attribute__((address_space(3))) *)(la + kb * SP * kWideRowBytes + r0 * kWideRowBytes), 16, 0, 0);
+    }
+  }
+  // LDS home of X^T tile t of the group
+  auto xbuf = [&](int t) -> char * { return t < 2 ? lx + t * L::P_BYTES : la + (t - 2) * L::P_BYTES; };
+  // X^T output row tile tm0 + t: wave w moves rows [16 w, 16 w + 16)
+  auto dma_x = [&](int t) {
+    const char *src = Xm + (int64_t)(tm0 + t) * kSmallTile * lda_b;
+    char *dst = xbuf(t);
+#pragma unroll
+    for (int kb = 0; kb < NST; ++kb)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int r0 = wave * 16 + j * 8;
+        __builtin_amdgcn_global_load_lds(
+            (const void *)(src + (int64_t)(r0 + dma_row) * lda_b + kb * kWideRowBytes + dma_chunk * 16),
+            (void __attribute__((address_space(3))) *)(dst + kb * kSmallTile * kWideRowBytes + r0 * kWideRowBytes), 16,
+            0, 0);
+      }
+  };
+  dma_x(0);
+  const int early = nt > 1 ? 2 : 1;
+  if (nt > 1) dma_x(1);
+
+  const int fr_row = lane & 15;
+  const int chunk0 = ((lane >> 4) ^ (lane & 7)) * 16;
+  const int chunk1 = ((4 + (lane >> 4)) ^ (lane & 7)) * 16;
+  auto kchunk = [&](int ks) { return (ks & 1) ? chunk1 : chunk0; };   // 32-k half of a stage
+
+  // ---- panel product: P^T[c][r] = sum_k A[c][k] A[r][k], r in this block's column tile
+  {
+    f32x4 acc[FM1][4];
+#pragma unroll
+    for (int i = 0; i < FM1; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int crow = wave * (SP / 4);
+    u32x4 fa[2][FM1], fb[2][4];
+    auto load = [&](int ks, int b) {
+      const char *st = la + (ks >> 1) * SP * kWideRowBytes;
+      const int ch = kchunk(ks);
+#pragma unroll
+      for (int i = 0; i < FM1; ++i) fa[b][i] = *(const u32x4 *)(st + (crow + i * 16 + fr_row) * kWideRowBytes + ch);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) fb[b][j] = *(const u32x4 *)(st + (tn * 64 + j * 16 + fr_row) * kWideRowBytes + ch);
+    };
+    static_for<0, NST>([&](auto sc) {
+      constexpr int kb = decltype(sc)::value;
+      // stage kb of A has landed (later stages and the X^T tiles may be in flight)
+      waitcnt_vm(A_DMA * (NST - 1 - kb) + X_DMA * early);
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_barrier" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      // both halves' fragments are read up front; the second half's reads
+      // overlap the first half's MFMAs
+      load(2 * kb, 0);
+      load(2 * kb + 1, 1);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < FM1; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) Mma<T>::run(fa[h][i], fb[h][j], acc[i][j]);
+    });
+    // B[r][c .. c+3] = sq_alpha P + sq_beta A[r][c .. c+3], rounded to T, into the panel
+    const float sa = cl.sq_alpha, sb = cl.sq_beta;
+#pragma unroll
+    for (int i = 0; i < FM1; ++i) {
+      const int c = crow + i * 16 + 4 * (lane >> 4);
+      const int coff = (c & 63) >> 3;   // 16-byte chunk of k = c within its stage row
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int rr = j * 16 + fr_row;   // panel row; A row tn * 64 + rr
+        const int r = tn * 64 + rr;
+        const uint2 av = *(const uint2 *)(la + (c >> 6) * SP * kWideRowBytes + r * kWideRowBytes +
+                                          ((coff ^ (r & 7)) << 4) + (c & 7) * 2);
+        const float a0 = (float)__builtin_bit_cast(T, (uint16_t)(av.x & 0xFFFF));
+        const float a1 = (float)__builtin_bit_cast(T, (uint16_t)(av.x >> 16));
+        const float a2 = (float)__builtin_bit_cast(T, (uint16_t)(av.y & 0xFFFF));
+        const float a3 = (float)__builtin_bit_cast(T, (uint16_t)(av.y >> 16));
+        // same rounding as the epilogue of a separate product: fma(beta, Cin,
+        // alpha * acc) in fp32, then to T (the empty asm keeps the compiler
+        // from fusing the fma with the conversion into one rounding)
+        float v0 = __builtin_fmaf(sb, a0, sa * acc[i][j][0]), v1 = __builtin_fmaf(sb, a1, sa * acc[i][j][1]);
+        float v2 = __builtin_fmaf(sb, a2, sa * acc[i][j][2]), v3 = __builtin_fmaf(sb, a3, sa * acc[i][j][3]);
+        asm volatile("" : "+v"(v0), "+v"(v1), "+v"(v2), "+v"(v3));
+        uint2 bv;
+        bv.x = Pack16<T>::pair(v0, v1);
+        bv.y = Pack16<T>::pair(v2, v3);
+        *(uint2 *)(lp + (c >> 6) * kSmallTile * kWideRowBytes + rr * kWideRowBytes + ((coff ^ (rr & 7)) << 4) +
+                   (c & 7) * 2) = bv;
+      }
+    }
+  }
+  lds_barrier();   // panel complete; region 0 (A) is free
+  if constexpr (L::MAXG > 2) {
+    if (nt > 2) dma_x(2);
+    if (nt > 3) dma_x(3);
+  }
+  waitcnt_vm(0);   // every X^T tile of the group has landed
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- update product and epilogue for each output row tile of the group
+  constexpr int FM = 2, FN = 2;
+  const int a_frag = (wm * 32 + fr_row) * kWideRowBytes;
+  const int b_frag = (wn * 32 + fr_row) * kWideRowBytes;
+  const float alpha = cl.alpha, beta = cl.beta;
+  FinalDesc fd{};
+  bool fvec = false;
+  if (cl.final_mode) {
+    fd = cl.desc[cl.desc_base + mat];
+    fvec = (fd.cols & 3) == 0 && ((((uintptr_t)fd.weight) | ((uintptr_t)fd.ortho_out)) & 15) == 0;
+  }
+  void *C = cl.c ? (void *)((char *)cl.c + (int64_t)mat * cl.sc * 2) : nullptr;
+  void *C2 = cl.c2 ? (void *)((char *)cl.c2 + (int64_t)mat * cl.sc2 * 2) : nullptr;
+  // operands of a whole tile (every k step) and its X^T entries for Cin, read
+  // from LDS one tile ahead so the reads overlap the previous tile's epilogue
+  u32x4 fa[NKS][FM], fb[NKS][FN];
+  uint16_t cu[FM][FN][4];
+  auto load_tile = [&](int t) {
+    const char *xb = xbuf(t);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const char *sx = xb + (ks >> 1) * kSmallTile * kWideRowBytes;
+      const char *sp = lp + (ks >> 1) * kSmallTile * kWideRowBytes;
+      const int ch = kchunk(ks);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) fa[ks][i] = *(const u32x4 *)(sx + a_frag + i * 16 * kWideRowBytes + ch);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) fb[ks][j] = *(const u32x4 *)(sp + b_frag + j * 16 * kWideRowBytes + ch);
+    }
+    // the tile's own X^T entries: columns tn * 64 + jc are k stage tn
+    const char *cx = xb + tn * kSmallTile * kWideRowBytes;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int ir = wm * 32 + i * 16 + 4 * (lane >> 4) + q;
+          const int jc = wn * 32 + j * 16 + (lane & 15);
+          cu[i][j][q] = *(const uint16_t *)(cx + ir * kWideRowBytes + (((jc >> 3) ^ (ir & 7)) << 4) + (jc & 7) * 2);
+        }
+  };
+  load_tile(0);
+  static_for<0, L::MAXG>([&](auto tc) {
+    constexpr int t = decltype(tc)::value;
+    if (t < nt) {
+      f32x4 acc[FM][FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) Mma<T>::run(fa[ks][i], fb[ks][j], acc[i][j]);
+      float cin[FM][FN][4];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) cin[i][j][q] = (float)__builtin_bit_cast(T, cu[i][j][q]);
+      if (t + 1 < nt) load_tile(t + 1);
+      // v = alpha acc + beta X^T, staged (alternating staging tiles: the
+      // previous barrier already ordered the sweeps of tile t - 2)
+      float *stg = (t & 1) ? (SP == 192 ? (float *)lx : (float *)(la + L::S_BYTES)) : (float *)(la + L::S0_OFF);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int ir = wm * 32 + i * 16 + 4 * (lane >> 4) + q;
+            const int jc = wn * 32 + j * 16 + (lane & 15);
+            stg[spos(ir, jc)] = __builtin_fmaf(beta, cin[i][j][q], alpha * acc[i][j][q]);
+          }
+      lds_barrier();
+      const int row0 = (tm0 + t) * kSmallTile;   // tile rows index the long side
+      const int col0 = tn * kSmallTile;          // tile columns index the short side
+      // row-major sweep: thread -> (tile row tid / 4, 16 columns)
+      {
+        const int r = tid >> 2, c0 = (tid & 3) * 16;
+        float v[16];
+        const float *src = stg + spos(r, c0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float4 x = *(const float4 *)(src + 4 * e);
+          v[4 * e] = x.x; v[4 * e + 1] = x.y; v[4 * e + 2] = x.z; v[4 * e + 3] = x.w;
+        }
+        if (!cl.final_mode) {
+          if (C) {
+            T *dst = (T *)C + (int64_t)(row0 + r) * cl.ldc + col0 + c0;
+            Pack<T>::copy(dst, (const float4 *)v);
+            Pack<T>::copy(dst + 8, (const float4 *)(v + 8));
+          }
+        } else if (!fd.wide && row0 + r < fd.rows) {
+          const int i = row0 + r, j0 = col0 + c0;
+          const float lr = cl.lr, wd = cl.wd, gm = fd.gamma;
+          float *wrow = fd.weight + (int64_t)i * fd.cols;
+          float *orow = fd.ortho_out ? fd.ortho_out + (int64_t)i * fd.cols : nullptr;
+          if (fvec && j0 + 16 <= fd.cols) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              float4 w = *(const float4 *)(wrow + j0 + 4 * e);
+              w.x = w.x - lr * (gm * v[4 * e] + wd * w.x);
+              w.y = w.y - lr * (gm * v[4 * e + 1] + wd * w.y);
+              w.z = w.z - lr * (gm * v[4 * e + 2] + wd * w.z);
+              w.w = w.w - lr * (gm * v[4 * e + 3] + wd * w.w);
+              *(float4 *)(wrow + j0 + 4 * e) = w;
+              if (orow) *(float4 *)(orow + j0 + 4 * e) = make_float4(v[4 * e], v[4 * e + 1], v[4 * e + 2], v[4 * e + 3]);
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              if (j0 + e < fd.cols) {
+                const float w = wrow[j0 + e];
+                wrow[j0 + e] = w - lr * (gm * v[e] + wd * w);
+                if (orow) orow[j0 + e] = v[e];
+              }
+            }
+          }
+        }
+      }
+      // transposed sweep: thread -> (tile column tid / 4, 16 rows)
+      if (!cl.final_mode ? (C2 != nullptr) : (bool)fd.wide) {
+        const int c = tid >> 2, r0 = (tid & 3) * 16;
+        float v[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) v[e] = stg[spos(r0 + e, c)];
+        if (!cl.final_mode) {
+          T *dst = (T *)C2 + (int64_t)(col0 + c) * cl.ldc2 + row0 + r0;
+          Pack<T>::copy(dst, (const float4 *)v);
+          Pack<T>::copy(dst + 8, (const float4 *)(v + 8));
+        } else if (col0 + c < fd.rows) {
+          // wide W: row col0 + c, columns row0 + r0 ..
+          const int i = col0 + c, j0 = row0 + r0;
+          const float lr = cl.lr, wd = cl.wd, gm = fd.gamma;
+          float *wrow = fd.weight + (int64_t)i * fd.cols;
+          float *orow = fd.ortho_out ? fd.ortho_out + (int64_t)i * fd.cols : nullptr;
+          if (fvec && j0 + 16 <= fd.cols) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              float4 w = *(const float4 *)(wrow + j0 + 4 * e);
+              w.x = w.x - lr * (gm * v[4 * e] + wd * w.x);
+              w.y = w.y - lr * (gm * v[4 * e + 1] + wd * w.y);
+              w.z = w.z - lr * (gm * v[4 * e + 2] + wd * w.z);
+              w.w = w.w - lr * (gm * v[4 * e + 3] + wd * w.w);
+              *(float4 *)(wrow + j0 + 4 * e) = w;
+              if (orow) *(float4 *)(orow + j0 + 4 * e) = make_float4(v[4 * e], v[4 * e + 1], v[4 * e + 2], v[4 * e + 3]);
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              if (j0 + e < fd.cols) {
+                const float w = wrow[j0 + e];
+                wrow[j0 + e] = w - lr * (gm * v[e] + wd * w);
+                if (orow) orow[j0 + e] = v[e];
+              }
+            }
+          }
+        }
+      }
+    }
+  });
+}
+
 template <typename T>
 hipError_t launch_t(const GemmArgs &args, int tile, hipStream_t s) {
   switch (tile) {
@@ -919,7 +1283,42 @@ hipError_t launch_t(const GemmArgs &args, int tile, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <typename T>
+hipError_t launch_poly_t(const GemmArgs &args, int sp, hipStream_t s) {
+  const dim3 g(args.total_tiles), b(kThreads);
+  switch (sp) {
+    case 64: hipLaunchKernelGGL((ns_poly_update_kernel<T, 64>), g, b, 0, s, args); break;
+    case 128: hipLaunchKernelGGL((ns_poly_update_kernel<T, 128>), g, b, 0, s, args); break;
+    case 192: hipLaunchKernelGGL((ns_poly_update_kernel<T, 192>), g, b, 0, s, args); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
+
+int poly_blocks_per_cu(int sp) {
+  const int bytes = sp == 64 ? PolyLayout<64>::TOTAL : sp == 128 ? PolyLayout<128>::TOTAL : PolyLayout<192>::TOTAL;
+  const int n = 160 * 1024 / bytes;
+  return n < 1 ? 1 : (n > 8 ? 8 : n);
+}
+
+int poly_max_group(int sp) {
+  return sp == 64 ? PolyLayout<64>::MAXG : sp == 128 ? PolyLayout<128>::MAXG : PolyLayout<192>::MAXG;
+}
+
+hipError_t launch_poly_update(const GemmArgs &args, int dtype, int sp, hipStream_t s) {
+  if (args.total_tiles <= 0) return hipSuccess;
+  for (int c = 0; c < args.nclass; ++c)
+    if (args.cls[c].K != sp || args.cls[c].m_group < 1 || args.cls[c].m_group > poly_max_group(sp) ||
+        args.cls[c].diag != 0.0f)
+      return hipErrorInvalidValue;
+  switch (dtype) {
+    case kF16: return launch_poly_t<_Float16>(args, sp, s);
+    case kBF16: return launch_poly_t<__bf16>(args, sp, s);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_gemm(const GemmArgs &args, int dtype, int tile, hipStream_t s) {
   if (args.total_tiles <= 0) return hipSuccess;

@@ -96,6 +96,27 @@ def test_f16_ns(variant):
              divisor=1.03, restart_every=3)
 
 
+@pytest.mark.parametrize("ns_dtype", ["bf16", "f16"])
+def test_fused_square_update_groups(ns_dtype):
+    """Short sides <= 192 form B = b A + c A^2 inside the update launch, each
+    block serving a group of output row tiles.  About 1450 (row tile, column
+    tile) pairs at a padded short side of 192 make the groups 4 tiles long
+    with ragged last groups (22 and 11 row tiles); short sides 64 and 128 run
+    in launches of their own in the same step."""
+    shapes = [(192, 1408)] * 6 + [(1408, 192)] * 6 + [(150, 700)] * 10 + [(700, 150)] * 10 + \
+        [(64, 320), (320, 64), (128, 200), (200, 128)]
+    run_case(shapes, grad_dtype="bf16", ns_dtype=ns_dtype, grad_kind="spectral", seed=12)
+
+
+@pytest.mark.parametrize("ns_dtype", ["bf16", "f16"])
+def test_long_k_register_stages(ns_dtype):
+    """64 tiles whose Gram product runs over more k than the LDS ring holds
+    (K = 704: 11 stages of 64, 3 of them carried in registers) in the same
+    launch as classes that fit the ring (K = 64 .. 192)."""
+    shapes = [(100, 700), (700, 100), (64, 650), (130, 130), (192, 192), (5, 60)]
+    run_case(shapes, grad_dtype="bf16", ns_dtype=ns_dtype, grad_kind="spectral", seed=13)
+
+
 @pytest.mark.parametrize("variant", ["direct", "gram"])
 def test_mona_two_steps(variant):
     run_case([(200, 330), (330, 200), (256, 256)], grad_dtype="bf16", ns_dtype="bf16", variant=variant, mona=True,
@@ -281,14 +302,15 @@ def _traced_step(group):
 
 
 def test_trace_per_launch_and_grouped():
-    """Per-launch mode: one interval per launch (E1, E2, 3 x 5 products).
+    """Per-launch mode: one interval per launch (E1, E2, 2 x 5 products: at
+    a short side of 192 the square is formed inside the update launch).
     Grouped mode: one interval per run of one stage, launch counts and work
     summed."""
     per = _traced_step(0)
-    assert [s for s, _, _, _ in per] == ["e1", "e2"] + ["gemm"] * 15
+    assert [s for s, _, _, _ in per] == ["e1", "e2"] + ["gemm"] * 10
     assert all(ms > 0 for _, _, _, ms in per)
     grp = _traced_step(1)
-    assert [(s, n) for s, n, _, _ in grp] == [("e1", 1), ("e2", 1), ("gemm", 15)]
+    assert [(s, n) for s, n, _, _ in grp] == [("e1", 1), ("e2", 1), ("gemm", 10)]
     assert grp[2][2] == pytest.approx(sum(w for s, _, w, _ in per if s == "gemm"))
     # 5 quintic steps on 4 x 192^2 and 2 x (192 x 768): half Gram, half square, full update
     s = 192.0
