@@ -415,22 +415,116 @@ __device__ __forceinline__ void epilogue_lds(const GemmClass &cl, int mat, int t
       }
     }
   };
-
-#pragma unroll 1
-  for (int p = 0; p < BM / HB; ++p) {
-    const int brow = p * HB;   // block-local first row of the band
-    // this thread's Cin chunks for the band, issued before the LDS hand-off
-    u32x4 cinv[NU][4];
-    if (Cin) {
+  // W loads issued together before their stores, in batches of WB rows /
+  // sweep units (the kernels run two waves per SIMD)
+  constexpr int WB = 2;
+  // the same update for 4 consecutive W rows from wr, CQ float4 of columns
+  // from wc each (o[i][h])
+  auto update_w_rows = [&](int wr, int wc, const float4 (&o)[4][CQ]) {
+    if (fvec && wr + 4 <= fd.rows && wc + 4 * CQ <= fd.cols) {
 #pragma unroll
-      for (int k = 0; k < NU; ++k) {
-        const int u = tid + k * NT;
-        const int rg = u / CPR, c = (u - rg * CPR) * CE;
+      for (int i0 = 0; i0 < 4; i0 += WB) {
+      float4 w[WB][CQ];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          cinv[k][i] = *(const u32x4 *)(Cin + (int64_t)(row0 + brow + 4 * rg + i) * cl.ldcin + col0 + c);
+      for (int i = 0; i < WB; ++i)
+#pragma unroll
+        for (int h = 0; h < CQ; ++h) w[i][h] = *(const float4 *)(fd.weight + (int64_t)(wr + i0 + i) * fd.cols + wc + 4 * h);
+#pragma unroll
+      for (int ii = 0; ii < WB; ++ii)
+#pragma unroll
+        for (int h = 0; h < CQ; ++h) {
+          const int i = i0 + ii;
+          float4 x = w[ii][h];
+          const float4 v = o[i][h];
+          x.x = x.x - lrate * (gm * v.x + wd * x.x);
+          x.y = x.y - lrate * (gm * v.y + wd * x.y);
+          x.z = x.z - lrate * (gm * v.z + wd * x.z);
+          x.w = x.w - lrate * (gm * v.w + wd * x.w);
+          const int64_t at = (int64_t)(wr + i) * fd.cols + wc + 4 * h;
+          *(float4 *)(fd.weight + at) = x;
+          if (fd.ortho_out) *(float4 *)(fd.ortho_out + at) = v;
+        }
       }
+      return;
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int h = 0; h < CQ; ++h) update_w(wr + i, wc + 4 * h, o[i][h]);
+  };
+  // wide W: unit n of the transposed sweep of band brow is W row col0 + c,
+  // CE columns from row0 + brow + rr
+  auto update_w_cols = [&](int brow, auto &src) {
+    constexpr int NQ = sizeof(src) / sizeof(src[0]);
+    bool all = fvec;
+#pragma unroll
+    for (int n = 0; n < NQ; ++n) {
+      const int q = tid + n * NT;
+      const int c = q / (HB / CE), rr = (q - c * (HB / CE)) * CE;
+      all = all && col0 + c < fd.rows && row0 + brow + rr + CE <= fd.cols;
+    }
+    if (all) {
+      constexpr int NB = WB < NQ ? WB : NQ;
+#pragma unroll
+      for (int n0 = 0; n0 < NQ; n0 += NB) {
+      float4 w[NB][CQ];
+#pragma unroll
+      for (int nn = 0; nn < NB; ++nn) {
+        const int q = tid + (n0 + nn) * NT;
+        const int c = q / (HB / CE), rr = (q - c * (HB / CE)) * CE;
+#pragma unroll
+        for (int h = 0; h < CQ; ++h)
+          w[nn][h] = *(const float4 *)(fd.weight + (int64_t)(col0 + c) * fd.cols + row0 + brow + rr + 4 * h);
+      }
+#pragma unroll
+      for (int nn = 0; nn < NB; ++nn) {
+        const int n = n0 + nn;
+        const int q = tid + n * NT;
+        const int c = q / (HB / CE), rr = (q - c * (HB / CE)) * CE;
+#pragma unroll
+        for (int h = 0; h < CQ; ++h) {
+          float4 x = w[nn][h];
+          const float4 v = src[n][h];
+          x.x = x.x - lrate * (gm * v.x + wd * x.x);
+          x.y = x.y - lrate * (gm * v.y + wd * x.y);
+          x.z = x.z - lrate * (gm * v.z + wd * x.z);
+          x.w = x.w - lrate * (gm * v.w + wd * x.w);
+          const int64_t at = (int64_t)(col0 + c) * fd.cols + row0 + brow + rr + 4 * h;
+          *(float4 *)(fd.weight + at) = x;
+          if (fd.ortho_out) *(float4 *)(fd.ortho_out + at) = v;
+        }
+      }
+      }
+      return;
+    }
+#pragma unroll
+    for (int n = 0; n < NQ; ++n) {
+      const int q = tid + n * NT;
+      const int c = q / (HB / CE), rr = (q - c * (HB / CE)) * CE;
+#pragma unroll
+      for (int h = 0; h < CQ; ++h) update_w(col0 + c, row0 + brow + rr + 4 * h, src[n][h]);
+    }
+  };
+
+  // this thread's Cin chunks of band p (4 rows x 16 bytes per unit); the
+  // next band's are in flight while a band is staged and swept
+  auto load_cin_band = [&](int p, u32x4 (&dst)[NU][4]) {
+#pragma unroll
+    for (int k = 0; k < NU; ++k) {
+      const int u = tid + k * NT;
+      const int rg = u / CPR, c = (u - rg * CPR) * CE;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        dst[k][i] = *(const u32x4 *)(Cin + (int64_t)(row0 + p * HB + 4 * rg + i) * cl.ldcin + col0 + c);
+    }
+  };
+  u32x4 cinv[NU][4], cin_next[NU][4];
+  if (Cin) load_cin_band(0, cinv);
+
+  // bands unrolled: each band's accumulators are dead once staged
+  static_for<0, BM / HB>([&](auto pc) {
+    constexpr int p = decltype(pc)::value;
+    const int brow = p * HB;   // block-local first row of the band
     lds_barrier();   // previous band (or the main loop) is done with LDS
     static_for<0, FM>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
@@ -446,6 +540,7 @@ __device__ __forceinline__ void epilogue_lds(const GemmClass &cl, int mat, int t
         }
       }
     });
+    if (Cin && p + 1 < BM / HB) load_cin_band(p + 1, cin_next);
     lds_barrier();
     // row-major sweep: units of 4 rows x one 16-byte chunk
 #pragma unroll
@@ -487,14 +582,14 @@ __device__ __forceinline__ void epilogue_lds(const GemmClass &cl, int mat, int t
         }
       }
       if (!out_r) continue;
+      if (cl.final_mode) {
+        // tall W: rows row0 + brow + 4 rg + i, 4 h columns from col0 + c
+        update_w_rows(row0 + brow + 4 * rg, col0 + c, v);
+        continue;
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int R = brow + 4 * rg + i;   // block-local row
-        if (cl.final_mode) {
-#pragma unroll
-          for (int h = 0; h < CQ; ++h) update_w(row0 + R, col0 + c + 4 * h, v[i][h]);
-          continue;
-        }
         T *dst = C + (int64_t)(row0 + R) * cl.ldc + col0 + c;
         if (!diag_tile || c >= R) {
           Pack<T>::copy(dst, v[i]);
@@ -505,8 +600,30 @@ __device__ __forceinline__ void epilogue_lds(const GemmClass &cl, int mat, int t
         }
       }
     }
-    if (!out_t) continue;
+    if (Cin && p + 1 < BM / HB) {
+#pragma unroll
+      for (int k = 0; k < NU; ++k)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cinv[k][i] = cin_next[k][i];
+    }
+    if (!out_t) return;
     if (!direct_t) lds_barrier();   // the transposed copy was filled by the sweep above
+    if (cl.final_mode) {
+      // wide W: row col0 + c, CE columns from row0 + brow + rr; every W load
+      // of the thread is issued before its first store
+      static_assert((BN * HB / CE) % NT == 0, "whole transposed sweep per thread");
+      constexpr int NQ = BN * HB / CE / NT;
+      float4 src[NQ][CQ];
+#pragma unroll
+      for (int n = 0; n < NQ; ++n) {
+        const int q = tid + n * NT;
+        const int c = q / (HB / CE), rr = (q - c * (HB / CE)) * CE;
+#pragma unroll
+        for (int h = 0; h < CQ; ++h) src[n][h] = *(const float4 *)&lt[tpos<HB>(c, rr + 4 * h)];
+      }
+      update_w_cols(brow, src);
+      return;
+    }
     // transposed sweep: chunks of CE band rows of one column
 #pragma unroll 1
     for (int q = tid; q < BN * HB / CE; q += NT) {
@@ -514,11 +631,6 @@ __device__ __forceinline__ void epilogue_lds(const GemmClass &cl, int mat, int t
       float4 src[CQ];
 #pragma unroll
       for (int h = 0; h < CQ; ++h) src[h] = *(const float4 *)&lt[tpos<HB>(c, rr + 4 * h)];
-      if (cl.final_mode) {
-#pragma unroll
-        for (int h = 0; h < CQ; ++h) update_w(col0 + c, row0 + brow + rr + 4 * h, src[h]);
-        continue;
-      }
       T *dst = Ct + (int64_t)(col0 + c) * ldt + row0 + brow + rr;
       const int R0 = brow + rr;   // block-local row of the chunk's first element
       if (!diag_tile || c >= R0 + CE - 1) {
@@ -529,7 +641,7 @@ __device__ __forceinline__ void epilogue_lds(const GemmClass &cl, int mat, int t
           if (c >= R0 + e) Store<T>::store(dst, e, elem(src, e));
       }
     }
-  }
+  });
 }
 
 // Register-staged BM x BN block tile (64 or 128; every fp32 product and the
@@ -542,7 +654,7 @@ constexpr int kStageBytes = 128;               // k bytes per LDS stage per row
 constexpr int kPitch = kStageBytes + 16;       // padded LDS row
 
 template <typename T, int BM, int BN>
-__global__ __launch_bounds__(kThreads) void ns_gemm_kernel(GemmArgs args) {
+__global__ __launch_bounds__(kThreads, 2) void ns_gemm_kernel(GemmArgs args) {
   constexpr int ES = sizeof(T);
   constexpr int KS = kStageBytes / ES;         // k elements per stage
   constexpr int WM = BM / 2, WN = BN / 2;      // 2 x 2 waves
