@@ -417,7 +417,7 @@ __device__ __forceinline__ void epilogue_lds(const GemmClass &cl, int mat, int t
   };
   // W loads issued together before their stores, in batches of WB rows /
   // sweep units (the kernels run two waves per SIMD)
-  constexpr int WB = 2;
+  constexpr int WB = NT >= 512 ? 1 : 2;
   // the same update for 4 consecutive W rows from wr, CQ float4 of columns
   // from wc each (o[i][h])
   auto update_w_rows = [&](int wr, int wc, const float4 (&o)[4][CQ]) {
@@ -506,8 +506,7 @@ __device__ __forceinline__ void epilogue_lds(const GemmClass &cl, int mat, int t
     }
   };
 
-  // this thread's Cin chunks of band p (4 rows x 16 bytes per unit); the
-  // next band's are in flight while a band is staged and swept
+  // this thread's Cin chunks of band p (4 rows x 16 bytes per unit)
   auto load_cin_band = [&](int p, u32x4 (&dst)[NU][4]) {
 #pragma unroll
     for (int k = 0; k < NU; ++k) {
@@ -518,8 +517,11 @@ __device__ __forceinline__ void epilogue_lds(const GemmClass &cl, int mat, int t
         dst[k][i] = *(const u32x4 *)(Cin + (int64_t)(row0 + p * HB + 4 * rg + i) * cl.ldcin + col0 + c);
     }
   };
-  u32x4 cinv[NU][4], cin_next[NU][4];
-  if (Cin) load_cin_band(0, cinv);
+  // every band's Cin is loaded before the first store: the vector memory
+  // counter retires in order, so a load issued after a store could only be
+  // awaited together with that store
+  u32x4 cin_all[BM / HB][NU][4];
+  if (Cin) static_for<0, BM / HB>([&](auto pc) { load_cin_band(decltype(pc)::value, cin_all[decltype(pc)::value]); });
 
   // bands unrolled: each band's accumulators are dead once staged
   static_for<0, BM / HB>([&](auto pc) {
@@ -540,8 +542,8 @@ __device__ __forceinline__ void epilogue_lds(const GemmClass &cl, int mat, int t
         }
       }
     });
-    if (Cin && p + 1 < BM / HB) load_cin_band(p + 1, cin_next);
     lds_barrier();
+    auto &cinv = cin_all[p];
     // row-major sweep: units of 4 rows x one 16-byte chunk
 #pragma unroll
     for (int k = 0; k < NU; ++k) {
@@ -599,12 +601,6 @@ __device__ __forceinline__ void epilogue_lds(const GemmClass &cl, int mat, int t
             if (c + e >= R) Store<T>::store(dst, e, elem(v[i], e));
         }
       }
-    }
-    if (Cin && p + 1 < BM / HB) {
-#pragma unroll
-      for (int k = 0; k < NU; ++k)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) cinv[k][i] = cin_next[k][i];
     }
     if (!out_t) return;
     if (!direct_t) lds_barrier();   // the transposed copy was filled by the sweep above
