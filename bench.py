@@ -238,6 +238,43 @@ def gpu_timing(args, w, variant):
     wall = time.perf_counter() - t0
     ms_per_step = start.elapsed_time(end) / args.steps
 
+    # spread over single steps (outside the timed region): p10 / p50 / p90
+    n_dist = min(args.steps, 200)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_dist)]
+    for a, b in evs:
+        a.record()
+        run()
+        b.record()
+    torch.cuda.synchronize()
+    dist = sorted(a.elapsed_time(b) for a, b in evs)
+    spread = [dist[int(q * (n_dist - 1) + 0.5)] for q in (0.1, 0.5, 0.9)]
+
+    # MONA workloads: the first step (D = 0: no previous gradient is read)
+    # timed on its own graph
+    first_ms = None
+    if w.mona and graph is not None:
+        def step0():
+            nsm.muon_step(params, coeffs=coeffs, step=0, **kw)
+        s0 = torch.cuda.Stream()
+        s0.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s0):
+            step0()
+        torch.cuda.current_stream().wait_stream(s0)
+        torch.cuda.synchronize()
+        g0 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g0):
+            step0()
+        g0.replay()
+        torch.cuda.synchronize()
+        n0 = max(1, min(args.steps, 20))
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(n0):
+            g0.replay()
+        b.record()
+        torch.cuda.synchronize()
+        first_ms = a.elapsed_time(b) / n0
+
     # kernel durations: HIP events recorded by libmuon on the launch stream
     # around every run of consecutive launches of one stage (no event between
     # the launches of a run, so the events do not separate the kernels)
@@ -269,13 +306,20 @@ def gpu_timing(args, w, variant):
         d["ms"] /= tsteps
         d["work"] /= tsteps
         d["launches"] /= tsteps
-    return params, ms_per_step, wall, per_stage, launches_per_step, graph is not None
+    return params, ms_per_step, wall, per_stage, launches_per_step, graph is not None, spread, first_ms
 
 
-def cpu_baseline(args, w, variant, params):
-    """The oracle as it stands, on this host's cores, on a bounded sample:
-    one matrix of each shape class, each repeated until its share of the time
-    budget is spent; the per-step time is extrapolated by matrix counts."""
+def cpu_baseline(args, w, variant, params, single_thread=False, seconds=None):
+    """The oracle as it stands, on this host's cores (or one BLAS thread), on
+    a bounded sample: one matrix of each shape class, each repeated until its
+    share of the time budget is spent; the per-step time is extrapolated by
+    matrix counts."""
+    if single_thread:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1, user_api="blas"):
+            r = cpu_baseline(args, w, variant, params, seconds=seconds)
+        r["cores"] = 1
+        return r
     import numpy as np
     import oracle
     try:
@@ -288,7 +332,7 @@ def cpu_baseline(args, w, variant, params):
     classes = {}
     for i, (r, c) in enumerate(w.shapes):
         classes.setdefault((r, c), []).append(i)
-    budget = args.cpu_seconds / max(len(classes), 1)
+    budget = (args.cpu_seconds if seconds is None else seconds) / max(len(classes), 1)
     total_ms = 0.0
     sample = []
     for (r, c), idx in classes.items():
@@ -333,7 +377,7 @@ def main():
     variant = args.variant or w.variants[0]
     print("bench: workload %s variant %s, %d matrices, %d warmup + %d timed steps" %
           (w.name, variant, len(w.shapes), args.warmup, args.steps), file=sys.stderr, flush=True)
-    params, ms, wall, per_stage, launches, graphed = gpu_timing(args, w, variant)
+    params, ms, wall, per_stage, launches, graphed, spread, first_ms = gpu_timing(args, w, variant)
     print("bench: gpu timing done (%.4f ms/step)" % ms, file=sys.stderr, flush=True)
 
     gemm = per_stage.get("gemm", {"ms": 0.0, "work": 0.0, "launches": 0})
@@ -361,10 +405,13 @@ def main():
                 "work_per_launch": per_launch_work, "traffic": None}
     roof["frac"] = roof["achieved"] / roof["peak"]
 
-    cpu = None
+    cpu = cpu1 = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args, w, variant, params)
         print("bench: cpu baseline done", file=sys.stderr, flush=True)
+        if w.numel <= 4 * 2**20:   # the small sets: also one BLAS thread
+            cpu1 = cpu_baseline(args, w, variant, params, single_thread=True, seconds=args.cpu_seconds / 2)
+            print("bench: single-thread cpu baseline done", file=sys.stderr, flush=True)
 
     out = {
         "metric": METRIC,
@@ -393,7 +440,12 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "wall_s_timed": wall,
+        "step_ms_p10_p50_p90": spread,
     }
+    if first_ms is not None:
+        out["first_step_ms"] = first_ms   # MONA: step 0 (no previous gradient read)
+    if cpu1 is not None:
+        out["cpu_baseline_single_thread"] = cpu1
     print(json.dumps(out), flush=True)
 
 
