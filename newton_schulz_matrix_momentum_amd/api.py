@@ -105,14 +105,35 @@ def muon_workspace_size(params: Sequence[Dict], *, ns_steps: int = 5, variant: s
 
 
 class Workspace:
-    """A reusable device byte buffer for ``muon_step`` (grows on demand)."""
+    """A reusable device byte buffer for ``muon_step`` (grows on demand).
+
+    A buffer handed out while a HIP graph was being captured is never freed
+    when the workspace grows: the captured graph keeps using its address on
+    every replay, and torch releases cached blocks to the driver when the
+    next capture starts, so freeing it would leave the old graph writing
+    into unmapped memory.  Such buffers are kept in ``retired`` for the
+    life of the workspace."""
 
     def __init__(self):
         self.buf = None
+        self.captured = False   # self.buf was handed out during a capture
+        self.retired = []
+
+    @staticmethod
+    def _capturing(device) -> bool:
+        try:
+            return torch.device(device).type == "cuda" and torch.cuda.is_current_stream_capturing()
+        except Exception:  # pragma: no cover - no HIP runtime
+            return False
 
     def get(self, nbytes: int, device) -> torch.Tensor:
-        if self.buf is None or self.buf.numel() < nbytes or self.buf.device != device:
+        if self.buf is None or self.buf.numel() < nbytes or self.buf.device != torch.device(device):
+            if self.buf is not None and self.captured:
+                self.retired.append(self.buf)
             self.buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+            self.captured = False
+        if self._capturing(device):
+            self.captured = True
         return self.buf
 
 

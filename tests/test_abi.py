@@ -259,3 +259,24 @@ def test_adamw_validation(lib):
     b.exp_avg_sq = a.param + 8          # inside a's param
     assert adam(lib, [a, b]) == E
     assert "overlap" in _lib.last_error()
+
+
+def test_workspace_keeps_buffers_used_under_graph_capture(monkeypatch):
+    """A workspace buffer handed out during a graph capture stays alive when the
+    workspace grows (the captured graph keeps its address); one never used
+    under capture is dropped."""
+    import torch
+    from newton_schulz_matrix_momentum_amd.api import Workspace
+    ws = Workspace()
+    capturing = {"on": False}
+    monkeypatch.setattr(Workspace, "_capturing", staticmethod(lambda device: capturing["on"]))
+    a = ws.get(1000, torch.device("cpu"))
+    assert ws.get(500, torch.device("cpu")) is a          # big enough: reused
+    b = ws.get(5000, torch.device("cpu"))                  # grows; a was never captured
+    assert b is not a and ws.retired == []
+    capturing["on"] = True
+    assert ws.get(100, torch.device("cpu")) is b          # handed out during a capture
+    capturing["on"] = False
+    c = ws.get(10000, torch.device("cpu"))                 # grows again: b must survive
+    assert c is not b and len(ws.retired) == 1 and ws.retired[0] is b
+    assert ws.get(20000, torch.device("cpu")) is not c and len(ws.retired) == 1   # c never captured

@@ -448,3 +448,48 @@ def test_optimizer_routes_vectors_to_adamw():
                                  beta1=f32(0.9), beta2=f32(0.95), eps=f32(1e-8), weight_decay=f32(0.05))
     np.testing.assert_allclose(to64(b), pb, rtol=1e-6, atol=1e-7)
     assert opt.state[b]["step"] == 1 and "exp_avg" in opt.state[b] and "momentum" in opt.state[w]
+
+
+# ---------------------------------------------------------------- graphs and the default workspace
+
+def test_graph_survives_workspace_growth():
+    """Capture a step on one set, then step and capture a larger set (the
+    default workspace grows, and the second capture empties torch's cache):
+    replays of the first graph must still match eager steps bitwise, i.e.
+    its workspace buffer was kept alive."""
+    import newton_schulz_matrix_momentum_amd as nsm
+    small = [(128, 256), (256, 128)]
+    big = [(512, 1024), (1024, 512)]
+    kw = dict(lr=0.02, mu=0.95, weight_decay=0.01, ns_dtype="bf16")
+    pa = make_params(small, "bf16", False, 51)
+    ref = make_params(small, "bf16", False, 51)
+    ga_grads = draw_grads(small, "bf16", 52)
+    for p, q, g in zip(pa, ref, ga_grads):
+        p["grad"] = g
+        q["grad"] = g.clone()
+    nsm.muon_step(pa, **kw)                      # warm-up, eager
+    nsm.muon_step(ref, **kw)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    ga = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(ga, stream=s):
+        nsm.muon_step(pa, **kw)
+    torch.cuda.synchronize()
+    pb = make_params(big, "bf16", False, 53)
+    for p, g in zip(pb, draw_grads(big, "bf16", 54)):
+        p["grad"] = g
+    nsm.muon_step(pb, **kw)                      # grows the default workspace
+    gb = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gb, stream=s):         # empties torch's cache first
+        nsm.muon_step(pb, **kw)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        ga.replay()
+        gb.replay()
+        torch.cuda.synchronize()
+        nsm.muon_step(ref, **kw)                 # the same step, eager
+        torch.cuda.synchronize()
+    for p, q in zip(pa, ref):
+        assert torch.equal(p["weight"], q["weight"])
+        assert torch.equal(p["momentum"], q["momentum"])
