@@ -48,12 +48,21 @@ def parse():
 
 
 def kernel_source_hash():
-    """sha256 of the NS GEMM kernel source: HBM-traffic figures in profiles/
-    apply only to the kernel they were measured on."""
+    """sha256 of the NS product kernels' code (ns_gemm.hip and the argument
+    blocks in muon_kernels.h, with comments and whitespace removed):
+    HBM-traffic figures in profiles/ apply only to the code they were
+    measured on, and an edit of a comment does not change that code."""
     import hashlib
-    path = os.path.join(ROOT, "newton_schulz_matrix_momentum_amd", "csrc", "ns_gemm.hip")
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    import re
+    h = hashlib.sha256()
+    for name in ("ns_gemm.hip", "muon_kernels.h"):
+        path = os.path.join(ROOT, "newton_schulz_matrix_momentum_amd", "csrc", name)
+        with open(path) as f:
+            src = f.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
+    return h.hexdigest()
 
 
 def recorded_traffic(workload):
@@ -70,7 +79,7 @@ def recorded_traffic(workload):
             if ":" in line and line.startswith("- "):
                 k, v = line[2:].split(":", 1)
                 vals[k.strip()] = v.strip().strip("`")
-    if vals.get("kernel_source_sha256") != kernel_source_hash():
+    if vals.get("kernel_code_sha256") != kernel_source_hash():
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])

@@ -19,9 +19,11 @@
 // Operands: fp16 / bf16 use v_mfma_f32_16x16x32_{f16,bf16}; fp32 uses
 // v_mfma_f32_16x16x4_f32.  Accumulation is always fp32.  Three block tiles:
 // 64 x 64 (latency-bound small products, 16-bit), 128 x 128 (register-staged
-// loads; also every fp32 product) and 256 x 256 (global -> LDS DMA, 16-bit).
-// All workspace buffers are zero-padded to tile multiples, so the main loops
-// have no bounds checks.
+// loads; also every fp32 product) and 256 x 256 (global -> LDS DMA, 16-bit);
+// and for direct steps with short sides up to 192, one kernel that forms the
+// square A A inside the update product (ns_poly_update_kernel).  All
+// workspace buffers are zero-padded to tile multiples, so the main loops have
+// no bounds checks.
 #include "muon_kernels.h"
 
 namespace muon {
