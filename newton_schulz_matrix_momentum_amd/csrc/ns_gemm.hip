@@ -642,6 +642,198 @@ __device__ __forceinline__ void epilogue_lds(const GemmClass &cl, int mat, int t
   });
 }
 
+// Epilogue of the 256 x 256 block tile (512 threads, 16-bit results): the
+// same values as epilogue_lds, in two bands of 128 rows.  The accumulators
+// (alpha * acc + diag) are staged row-major in LDS; then each thread takes
+// one 8 x 8 unit of the band (lanes arranged 8 x 8, so 8 lanes cover one
+// 128-byte line in either orientation), adds beta * Cin, stores the unit's 8
+// rows as 16-byte vectors and transposes the packed 16-bit values in
+// registers for the 8 transposed (mirror / C2) 16-byte stores: no transposed
+// LDS copy and one barrier per band fewer.  In final mode the unit updates
+// 8 rows of a tall W, or 8 rows of a wide W from the unit's columns.  Every
+// Cin chunk is loaded before the first store (the memory counter retires in
+// order).  On entry every wave must be done reading LDS for the main loop.
+template <typename T, int FM, int FN>
+__device__ __forceinline__ void epilogue_u8(const GemmClass &cl, int mat, int tm, int tn, int wrow, int wcol,
+                                            f32x4 (&acc)[FM][FN], float *lds) {
+  static_assert(sizeof(T) == 2, "16-bit results");
+  constexpr int BM = 256, BN = 256, HB = 128;
+  constexpr int PR = BN + 4;                  // row-major pitch (floats)
+  float *lr = lds;                            // HB x PR
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int row0 = tm * BM, col0 = tn * BN;
+  const float alpha = cl.alpha, beta = cl.beta, diag = cl.diag;
+  const T *Cin = cl.cin ? (const T *)((const char *)cl.cin + (int64_t)mat * cl.scin * 2) : nullptr;
+  {
+    const int rb = row0 + wrow + 4 * (lane >> 4);
+    const int cb = col0 + wcol + (lane & 15);
+    static_for<0, FM>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int col = cb + j * 16;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float v = alpha * acc[i][j][r];
+          if (diag != 0.0f && rb + i * 16 + r == col && col < cl.diag_limit) v += diag;
+          acc[i][j][r] = v;
+        }
+      }
+    });
+  }
+  const bool diag_tile = cl.half && tm == tn;
+  FinalDesc fd{};
+  bool fvec = false;
+  if (cl.final_mode) {
+    fd = cl.desc[cl.desc_base + mat];
+    fvec = (fd.cols & 3) == 0 && ((((uintptr_t)fd.weight) | ((uintptr_t)fd.ortho_out)) & 15) == 0;
+  }
+  T *C = cl.c ? (T *)((char *)cl.c + (int64_t)mat * cl.sc * 2) : nullptr;
+  T *C2 = cl.c2 ? (T *)((char *)cl.c2 + (int64_t)mat * cl.sc2 * 2) : nullptr;
+  T *Ct = cl.half ? C : C2;                   // destination of the transposed stores
+  const int ldt = cl.half ? cl.ldc : cl.ldc2;
+  const float lrate = cl.lr, wd = cl.wd, gm = fd.gamma;
+  // this thread's unit: columns 8 cg .. 8 cg + 7, band rows 8 rg .. 8 rg + 7
+  const int cg = (wave & 3) * 8 + (lane & 7);
+  const int rg = (wave >> 2) * 8 + (lane >> 3);
+  const int c0 = 8 * cg;
+  u32x4 cin[BM / HB][8];
+  if (Cin) {
+#pragma unroll
+    for (int p = 0; p < BM / HB; ++p)
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        cin[p][i] = *(const u32x4 *)(Cin + (int64_t)(row0 + p * HB + 8 * rg + i) * cl.ldcin + col0 + c0);
+  }
+  // W <- W - lr (gamma o + wd W) on 8 consecutive elements of W's row wr from wc
+  auto update_w8 = [&](int wr, int wc, const float (&o)[8]) {
+    if (wr >= fd.rows) return;
+    float *w = fd.weight + (int64_t)wr * fd.cols + wc;
+    float *oo = fd.ortho_out ? fd.ortho_out + (int64_t)wr * fd.cols + wc : nullptr;
+    if (fvec && wc + 8 <= fd.cols) {
+      float4 a = *(const float4 *)w, b = *(const float4 *)(w + 4);
+      a.x = a.x - lrate * (gm * o[0] + wd * a.x);
+      a.y = a.y - lrate * (gm * o[1] + wd * a.y);
+      a.z = a.z - lrate * (gm * o[2] + wd * a.z);
+      a.w = a.w - lrate * (gm * o[3] + wd * a.w);
+      b.x = b.x - lrate * (gm * o[4] + wd * b.x);
+      b.y = b.y - lrate * (gm * o[5] + wd * b.y);
+      b.z = b.z - lrate * (gm * o[6] + wd * b.z);
+      b.w = b.w - lrate * (gm * o[7] + wd * b.w);
+      *(float4 *)w = a;
+      *(float4 *)(w + 4) = b;
+      if (oo) {
+        *(float4 *)oo = make_float4(o[0], o[1], o[2], o[3]);
+        *(float4 *)(oo + 4) = make_float4(o[4], o[5], o[6], o[7]);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (wc + e < fd.cols) {
+          const float x = w[e];
+          w[e] = x - lrate * (gm * o[e] + wd * x);
+          if (oo) oo[e] = o[e];
+        }
+      }
+    }
+  };
+
+  static_for<0, BM / HB>([&](auto pc) {
+    constexpr int p = decltype(pc)::value;
+    const int brow = p * HB;
+    lds_barrier();   // the previous band (or the main loop) is done with LDS
+    static_for<0, FM>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      const int rloc = wrow + i * 16 - brow;   // band-local first row of block i
+      if (rloc >= 0 && rloc < HB) {
+        const int rr = rloc + 4 * (lane >> 4);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int c = wcol + j * 16 + (lane & 15);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) lr[(rr + r) * PR + c] = acc[i][j][r];
+        }
+      }
+    });
+    lds_barrier();
+    const int R0 = brow + 8 * rg;   // block-local first row of the unit
+    uint32_t pk[8][4];               // the unit as T: row i, columns 2k, 2k + 1
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float *src = lr + (8 * rg + i) * PR + c0;
+      const float4 a = *(const float4 *)src, b = *(const float4 *)(src + 4);
+      float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      if (Cin) {
+        const u32x4 w = cin[p][i];
+        auto lo = [](uint32_t x) { return (float)__builtin_bit_cast(T, (uint16_t)(x & 0xFFFFu)); };
+        auto hi = [](uint32_t x) { return (float)__builtin_bit_cast(T, (uint16_t)(x >> 16)); };
+        v[0] += beta * lo(w.x);
+        v[1] += beta * hi(w.x);
+        v[2] += beta * lo(w.y);
+        v[3] += beta * hi(w.y);
+        v[4] += beta * lo(w.z);
+        v[5] += beta * hi(w.z);
+        v[6] += beta * lo(w.w);
+        v[7] += beta * hi(w.w);
+      }
+      if (cl.final_mode) {
+        if (!fd.wide) {
+          update_w8(row0 + R0 + i, col0 + c0, v);          // tall W: rows index the tile rows
+        } else {
+          *(float4 *)src = make_float4(v[0], v[1], v[2], v[3]);   // kept for the column pass below
+          *(float4 *)(src + 4) = make_float4(v[4], v[5], v[6], v[7]);
+        }
+        continue;
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) pk[i][k] = Pack16<T>::pair(v[2 * k], v[2 * k + 1]);
+      if (C) {
+        const int R = R0 + i;
+        T *dst = C + (int64_t)(row0 + R) * cl.ldc + col0 + c0;
+        if (!diag_tile || c0 >= R) {
+          *(u32x4 *)dst = u32x4{pk[i][0], pk[i][1], pk[i][2], pk[i][3]};
+        } else if (c0 + 8 > R) {   // the chunk crossing the diagonal: upper part only
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (c0 + e >= R) ((uint16_t *)dst)[e] = (uint16_t)(pk[i][e >> 1] >> (16 * (e & 1)));
+        }
+      }
+    }
+    if (cl.final_mode) {
+      if (fd.wide) {
+        // wide W: row col0 + c0 + e, columns row0 + R0 .. R0 + 7 (the unit's own values)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float o[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) o[i] = lr[(8 * rg + i) * PR + c0 + e];
+          if (col0 + c0 + e < fd.rows) update_w8(col0 + c0 + e, row0 + R0, o);
+        }
+      }
+      return;
+    }
+    if (!Ct) return;
+    // transposed stores: column c0 + e, rows R0 .. R0 + 7
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int sh = 16 * (e & 1);
+      uint32_t h[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) h[i] = (pk[i][e >> 1] >> sh) & 0xFFFFu;
+      T *dst = Ct + (int64_t)(col0 + c0 + e) * ldt + row0 + R0;
+      const int c = c0 + e;
+      if (!diag_tile || c >= R0 + 7) {
+        *(u32x4 *)dst = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+      } else if (c >= R0) {       // mirror only the upper-triangular sources
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (c >= R0 + i) ((uint16_t *)dst)[i] = (uint16_t)h[i];
+      }
+    }
+  });
+}
+
 // Register-staged BM x BN block tile (64 or 128; every fp32 product and the
 // 16-bit 128 tile): four waves of (BM/2) x (BN/2); k advances 128 bytes per
 // LDS stage, double-buffered through registers, with one barrier per stage.
@@ -798,8 +990,9 @@ __global__ __launch_bounds__(2 * WN_WAVES * 64, 1) void ns_gemm_wide_kernel(Gemm
   constexpr int FM = 8, FN = WTN / 16;           // 128 x WTN per wave
   constexpr int DMA_PER_WAVE = 32 / NWAVES;      // 1 KB DMA instructions per operand per stage
   constexpr int PER_STAGE = 2 * DMA_PER_WAVE;    // DMA instructions per stage and wave
-  constexpr int kLdsBytes = 2 * kWideStage > epilogue_lds_floats<64, kBigTile>() * 4
-                                ? 2 * kWideStage : epilogue_lds_floats<64, kBigTile>() * 4;
+  constexpr int kEpiBytes = 128 * (kBigTile + 4) * 4;   // epilogue_u8's staging band
+  constexpr int kLdsBytes = 2 * kWideStage > kEpiBytes ? 2 * kWideStage : kEpiBytes;
+  static_assert(kLdsBytes <= 160 * 1024, "LDS");
   __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
 
   const TileRef tr = locate_tile(args);
@@ -885,7 +1078,8 @@ __global__ __launch_bounds__(2 * WN_WAVES * 64, 1) void ns_gemm_wide_kernel(Gemm
       if (kb + 2 < nk) dma(kb + 2);
     }
   }
-  epilogue_lds<T, kBigTile, kBigTile, 64, NWAVES * 64, FM, FN>(cl, mat, tm, tn, wm * 128, wn * WTN, acc, (float *)lds);
+  static_assert(NWAVES == 8 && FM == 8 && FN == 4, "epilogue_u8 maps 8 waves of 128 x 64");
+  epilogue_u8<T, FM, FN>(cl, mat, tm, tn, wm * 128, wn * WTN, acc, (float *)lds);
 }
 
 // ---------------------------------------------------------------------------
