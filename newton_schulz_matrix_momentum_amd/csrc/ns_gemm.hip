@@ -642,8 +642,8 @@ __device__ __forceinline__ void epilogue_lds(const GemmClass &cl, int mat, int t
   });
 }
 
-// Epilogue of the 256 x 256 block tile (512 threads, 16-bit results): the
-// same values as epilogue_lds, in two bands of 128 rows.  The accumulators
+// Epilogue of the 16-bit 128 x 128 and 256 x 256 block tiles (2 BM
+// threads): the same values as epilogue_lds, in bands of 128 rows.  The accumulators
 // (alpha * acc + diag) are staged row-major in LDS; then each thread takes
 // one 8 x 8 unit of the band (lanes arranged 8 x 8, so 8 lanes cover one
 // 128-byte line in either orientation), adds beta * Cin, stores the unit's 8
@@ -653,11 +653,13 @@ __device__ __forceinline__ void epilogue_lds(const GemmClass &cl, int mat, int t
 // 8 rows of a tall W, or 8 rows of a wide W from the unit's columns.  Every
 // Cin chunk is loaded before the first store (the memory counter retires in
 // order).  On entry every wave must be done reading LDS for the main loop.
-template <typename T, int FM, int FN>
+template <typename T, int BM, int FM, int FN>
 __device__ __forceinline__ void epilogue_u8(const GemmClass &cl, int mat, int tm, int tn, int wrow, int wcol,
                                             f32x4 (&acc)[FM][FN], float *lds) {
   static_assert(sizeof(T) == 2, "16-bit results");
-  constexpr int BM = 256, BN = 256, HB = 128;
+  static_assert(BM == 128 || BM == 256, "bands of 128 rows, 8 x 8 units over 2 BM threads");
+  constexpr int BN = BM, HB = 128;
+  constexpr int WPR = BM / 64;                // waves per 64-column-unit row of the band
   constexpr int PR = BN + 4;                  // row-major pitch (floats)
   float *lr = lds;                            // HB x PR
   const int lane = threadIdx.x & 63;
@@ -695,8 +697,8 @@ __device__ __forceinline__ void epilogue_u8(const GemmClass &cl, int mat, int tm
   const int ldt = cl.half ? cl.ldc : cl.ldc2;
   const float lrate = cl.lr, wd = cl.wd, gm = fd.gamma;
   // this thread's unit: columns 8 cg .. 8 cg + 7, band rows 8 rg .. 8 rg + 7
-  const int cg = (wave & 3) * 8 + (lane & 7);
-  const int rg = (wave >> 2) * 8 + (lane >> 3);
+  const int cg = (wave % WPR) * 8 + (lane & 7);
+  const int rg = (wave / WPR) * 8 + (lane >> 3);
   const int c0 = 8 * cg;
   u32x4 cin[BM / HB][8];
   if (Cin) {
@@ -777,13 +779,9 @@ __device__ __forceinline__ void epilogue_u8(const GemmClass &cl, int mat, int tm
         v[6] += beta * lo(w.w);
         v[7] += beta * hi(w.w);
       }
-      if (cl.final_mode) {
-        if (!fd.wide) {
-          update_w8(row0 + R0 + i, col0 + c0, v);          // tall W: rows index the tile rows
-        } else {
-          *(float4 *)src = make_float4(v[0], v[1], v[2], v[3]);   // kept for the column pass below
-          *(float4 *)(src + 4) = make_float4(v[4], v[5], v[6], v[7]);
-        }
+      if (cl.final_mode) {   // kept in place for the W pass below
+        *(float4 *)src = make_float4(v[0], v[1], v[2], v[3]);
+        *(float4 *)(src + 4) = make_float4(v[4], v[5], v[6], v[7]);
         continue;
       }
 #pragma unroll
@@ -801,14 +799,56 @@ __device__ __forceinline__ void epilogue_u8(const GemmClass &cl, int mat, int tm
       }
     }
     if (cl.final_mode) {
-      if (fd.wide) {
-        // wide W: row col0 + c0 + e, columns row0 + R0 .. R0 + 7 (the unit's own values)
+      // 8 W rows of 8 elements from the unit's own staged values: a tall W
+      // takes the unit's rows (W row row0 + R0 + q, columns col0 + c0 ..), a
+      // wide W its columns (W row col0 + c0 + q, columns row0 + R0 ..); in
+      // batches of QB rows with every W load issued before the stores (the
+      // staged values are read from LDS after the loads)
+      constexpr int QB = BM == 256 ? 1 : 4;   // registers: two waves per SIMD on the 256 tile
+      const bool tall = !fd.wide;
+      const int wr0 = tall ? row0 + R0 : col0 + c0, wc = tall ? col0 + c0 : row0 + R0;
+      auto staged = [&](int q, float (&o)[8]) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float o[8];
+        for (int e = 0; e < 8; ++e) o[e] = tall ? lr[(8 * rg + q) * PR + c0 + e] : lr[(8 * rg + e) * PR + c0 + q];
+      };
 #pragma unroll
-          for (int i = 0; i < 8; ++i) o[i] = lr[(8 * rg + i) * PR + c0 + e];
-          if (col0 + c0 + e < fd.rows) update_w8(col0 + c0 + e, row0 + R0, o);
+      for (int q0 = 0; q0 < 8; q0 += QB) {
+        if (fvec && wr0 + q0 + QB <= fd.rows && wc + 8 <= fd.cols) {
+          float4 w[QB][2];
+#pragma unroll
+          for (int qq = 0; qq < QB; ++qq) {
+            const float *wp = fd.weight + (int64_t)(wr0 + q0 + qq) * fd.cols + wc;
+            w[qq][0] = *(const float4 *)wp;
+            w[qq][1] = *(const float4 *)(wp + 4);
+          }
+#pragma unroll
+          for (int qq = 0; qq < QB; ++qq) {
+            float x[8];
+            staged(q0 + qq, x);
+            float4 a = w[qq][0], b = w[qq][1];
+            a.x = a.x - lrate * (gm * x[0] + wd * a.x);
+            a.y = a.y - lrate * (gm * x[1] + wd * a.y);
+            a.z = a.z - lrate * (gm * x[2] + wd * a.z);
+            a.w = a.w - lrate * (gm * x[3] + wd * a.w);
+            b.x = b.x - lrate * (gm * x[4] + wd * b.x);
+            b.y = b.y - lrate * (gm * x[5] + wd * b.y);
+            b.z = b.z - lrate * (gm * x[6] + wd * b.z);
+            b.w = b.w - lrate * (gm * x[7] + wd * b.w);
+            const int64_t at = (int64_t)(wr0 + q0 + qq) * fd.cols + wc;
+            *(float4 *)(fd.weight + at) = a;
+            *(float4 *)(fd.weight + at + 4) = b;
+            if (fd.ortho_out) {
+              *(float4 *)(fd.ortho_out + at) = make_float4(x[0], x[1], x[2], x[3]);
+              *(float4 *)(fd.ortho_out + at + 4) = make_float4(x[4], x[5], x[6], x[7]);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int qq = 0; qq < QB; ++qq) {
+            float x[8];
+            staged(q0 + qq, x);
+            update_w8(wr0 + q0 + qq, wc, x);
+          }
         }
       }
       return;
@@ -946,10 +986,14 @@ __global__ __launch_bounds__(kThreads, 2) void ns_gemm_kernel(GemmArgs args) {
 
   static_assert(epilogue_lds_floats<64, BN>() * 4 <= (int)sizeof(lds), "epilogue bands must fit the LDS stages");
   const float no_cin[FM][FN][4] = {};
-  if constexpr (BM == 64)   // latency-bound small tiles: no LDS hand-off
+  if constexpr (BM == 64) {   // latency-bound small tiles: no LDS hand-off
     epilogue<T, FM, FN>(cl, mat, cl.half && tm == tn, tm * BM + wm * WM, tn * BN + wn * WN, acc, no_cin);
-  else
+  } else if constexpr (ES == 2 && BM == 128 && BN == 128) {
+    static_assert(128 * (BN + 4) * 4 <= (int)sizeof(lds) && kThreads == 2 * BM, "epilogue_u8 fits");
+    epilogue_u8<T, BM, FM, FN>(cl, mat, tm, tn, wm * WM, wn * WN, acc, (float *)&lds[0][0]);
+  } else {
     epilogue_lds<T, BM, BN, 64, kThreads, FM, FN>(cl, mat, tm, tn, wm * WM, wn * WN, acc, (float *)&lds[0][0]);
+  }
 }
 
 
@@ -1078,8 +1122,8 @@ __global__ __launch_bounds__(2 * WN_WAVES * 64, 1) void ns_gemm_wide_kernel(Gemm
       if (kb + 2 < nk) dma(kb + 2);
     }
   }
-  static_assert(NWAVES == 8 && FM == 8 && FN == 4, "epilogue_u8 maps 8 waves of 128 x 64");
-  epilogue_u8<T, FM, FN>(cl, mat, tm, tn, wm * 128, wn * WTN, acc, (float *)lds);
+  static_assert(NWAVES == 8, "epilogue_u8 takes 2 BM threads");
+  epilogue_u8<T, kBigTile, FM, FN>(cl, mat, tm, tn, wm * 128, wn * WTN, acc, (float *)lds);
 }
 
 // ---------------------------------------------------------------------------
