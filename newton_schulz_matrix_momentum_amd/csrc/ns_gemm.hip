@@ -999,42 +999,46 @@ __global__ __launch_bounds__(kThreads, 2) void ns_gemm_kernel(GemmArgs args) {
 
 // ---------------------------------------------------------------------------
 // Stage formats shared by the 16-bit DMA kernels.
-constexpr int kBigTile = 256;
 #ifndef MUON_A_AHEAD
 #define MUON_A_AHEAD 3
 #endif
 constexpr int kAAhead = MUON_A_AHEAD;     // A fragments read this many 16-row blocks ahead
 
 // ---------------------------------------------------------------------------
-// 256 x 256 block tile for fp16 / bf16: eight waves (two per SIMD) of
-// 128 x 64 each; the second wave on a SIMD issues MFMAs while the first
+// TILE x TILE block tile for fp16 / bf16 (TILE = 256: eight waves, two per
+// SIMD, of 128 x 64 each, one block per CU; TILE = 128: four waves of 64 x 64,
+// two blocks per CU): the second wave on a SIMD issues MFMAs while the first
 // waits at a barrier or on LDS.
 //
 // Operands move global -> LDS with global_load_lds_dwordx4 (no register
-// staging).  A stage holds 64 k = 128 bytes of every row of the 256-row A
-// and B panels (64 KB); each group of 8 lanes of a DMA instruction fetches
-// one whole 128-byte line (8 rows x 128 bytes per instruction), which halves
-// the L1 -> L2 requests per byte relative to 64-byte row segments.  Two
-// stages (128 KB) form the ring; the DMA of stage kb+2 is issued once every
-// wave is done with stage kb, so a stage has one stage of compute to land.
+// staging).  A stage holds 64 k = 128 bytes of every row of the TILE-row A
+// and B panels (64 KB at TILE = 256); each group of 8 lanes of a DMA
+// instruction fetches one whole 128-byte line (8 rows x 128 bytes per
+// instruction), which halves the L1 -> L2 requests per byte relative to
+// 64-byte row segments.  Two stages form the ring; the DMA of stage kb+2 is
+// issued once every wave is done with stage kb, so a stage has one stage of
+// compute to land.
 // LDS rows are not padded: 16-byte chunk c of row r is stored at chunk
 // c ^ (r & 7), so the fragment reads of 8 consecutive rows at one logical
 // chunk cover all 32 banks.  Within a stage the A fragments are streamed
 // kAAhead 16-row blocks ahead and the second k-step's B fragments are read
 // during the first.
 constexpr int kWideRowBytes = 128;                                  // 64 x 16-bit k per stage
-constexpr int kWideStage = (kBigTile + kBigTile) * kWideRowBytes;   // 64 KB
 
-template <typename T, int WN_WAVES>
-__global__ __launch_bounds__(2 * WN_WAVES * 64, 1) void ns_gemm_wide_kernel(GemmArgs args) {
+template <typename T, int TILE>
+__global__ __launch_bounds__(TILE * 2, TILE == 256 ? 1 : 2) void ns_gemm_wide_kernel(GemmArgs args) {
   static_assert(sizeof(T) == 2, "16-bit operands only");
-  static_assert(16 % (kAAhead + 1) == 0, "A fragment ring must divide the 16 fragment groups");
+  static_assert(TILE == 128 || TILE == 256, "128 or 256 tiles");
+  constexpr int WN_WAVES = TILE / 64;            // 2 x WN_WAVES waves
   constexpr int NWAVES = 2 * WN_WAVES;
-  constexpr int WTN = kBigTile / WN_WAVES;       // wave tile columns
-  constexpr int FM = 8, FN = WTN / 16;           // 128 x WTN per wave
-  constexpr int DMA_PER_WAVE = 32 / NWAVES;      // 1 KB DMA instructions per operand per stage
+  constexpr int WTM = TILE / 2, WTN = 64;        // wave tile
+  constexpr int FM = WTM / 16, FN = WTN / 16;
+  constexpr int NG = 2 * FM;                     // fragment groups per stage (2 k-steps)
+  static_assert(NG % (kAAhead + 1) == 0, "A fragment ring must divide the fragment groups");
+  constexpr int kWideStage = (TILE + TILE) * kWideRowBytes;
+  constexpr int DMA_PER_WAVE = TILE / 8 / NWAVES;   // 1 KB DMA instructions per operand per stage
   constexpr int PER_STAGE = 2 * DMA_PER_WAVE;    // DMA instructions per stage and wave
-  constexpr int kEpiBytes = 128 * (kBigTile + 4) * 4;   // epilogue_u8's staging band
+  constexpr int kEpiBytes = 128 * (TILE + 4) * 4;   // epilogue_u8's staging band
   constexpr int kLdsBytes = 2 * kWideStage > kEpiBytes ? 2 * kWideStage : kEpiBytes;
   static_assert(kLdsBytes <= 160 * 1024, "LDS");
   __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
@@ -1046,8 +1050,8 @@ __global__ __launch_bounds__(2 * WN_WAVES * 64, 1) void ns_gemm_wide_kernel(Gemm
   const int wave = threadIdx.x >> 6;
   const int wm = wave / WN_WAVES, wn = wave % WN_WAVES;
 
-  const char *A = (const char *)cl.a + ((int64_t)mat * cl.sa + (int64_t)tm * kBigTile * cl.lda) * 2;
-  const char *B = (const char *)cl.b + ((int64_t)mat * cl.sb + (int64_t)tn * kBigTile * cl.ldb) * 2;
+  const char *A = (const char *)cl.a + ((int64_t)mat * cl.sa + (int64_t)tm * TILE * cl.lda) * 2;
+  const char *B = (const char *)cl.b + ((int64_t)mat * cl.sb + (int64_t)tn * TILE * cl.ldb) * 2;
   const int64_t lda_b = (int64_t)cl.lda * 2, ldb_b = (int64_t)cl.ldb * 2;
 
   // DMA: wave w moves rows [8 DMA_PER_WAVE w, +8 DMA_PER_WAVE) of A and of
@@ -1061,8 +1065,8 @@ __global__ __launch_bounds__(2 * WN_WAVES * 64, 1) void ns_gemm_wide_kernel(Gemm
   // fragment of k-step ks (32 k) for row block base + lane % 16: logical
   // chunk 4 ks + lane / 16, physical chunk logical ^ (lane % 8)
   const int fr_row = lane & 15;
-  const int a_frag = (wm * 128 + fr_row) * kWideRowBytes;
-  const int b_frag = (kBigTile + wn * WTN + fr_row) * kWideRowBytes;
+  const int a_frag = (wm * WTM + fr_row) * kWideRowBytes;
+  const int b_frag = (TILE + wn * WTN + fr_row) * kWideRowBytes;
   const int chunk0 = (((lane >> 4)) ^ (lane & 7)) * 16;       // ks = 0
   const int chunk1 = ((4 + (lane >> 4)) ^ (lane & 7)) * 16;   // ks = 1
 
@@ -1085,11 +1089,11 @@ __global__ __launch_bounds__(2 * WN_WAVES * 64, 1) void ns_gemm_wide_kernel(Gemm
       for (int j = 0; j < DMA_PER_WAVE; ++j)
         __builtin_amdgcn_global_load_lds(
             (const void __attribute__((address_space(1))) *)(b_src + (int64_t)j * 8 * ldb_b + (int64_t)kb * kWideRowBytes),
-            (void __attribute__((address_space(3))) *)(dst + kBigTile * kWideRowBytes + j * 1024), 16, 0, 0);
+            (void __attribute__((address_space(3))) *)(dst + TILE * kWideRowBytes + j * 1024), 16, 0, 0);
     };
-    // fragment group g = 8 ks + i: A row block i at k-step ks
+    // fragment group g = FM ks + i: A row block i at k-step ks
     auto rd_a = [&](const char *slot, int g) -> u32x4 {
-      return *(const u32x4 *)(slot + a_frag + (g & 7) * 16 * kWideRowBytes + ((g >> 3) ? chunk1 : chunk0));
+      return *(const u32x4 *)(slot + a_frag + (g % FM) * 16 * kWideRowBytes + ((g / FM) ? chunk1 : chunk0));
     };
     dma(0);
     if (nk > 1) dma(1);
@@ -1103,14 +1107,14 @@ __global__ __launch_bounds__(2 * WN_WAVES * 64, 1) void ns_gemm_wide_kernel(Gemm
       for (int j = 0; j < FN; ++j) b0[j] = *(const u32x4 *)(slot + b_frag + j * 16 * kWideRowBytes + chunk0);
 #pragma unroll
       for (int q = 0; q < kAAhead; ++q) a_q[q] = rd_a(slot, q);
-      static_for<0, 16>([&](auto gc) {
+      static_for<0, NG>([&](auto gc) {
         constexpr int g = decltype(gc)::value;
-        constexpr int i = g & 7;
-        if constexpr (g + kAAhead < 16) a_q[(g + kAAhead) % (kAAhead + 1)] = rd_a(slot, g + kAAhead);
+        constexpr int i = g % FM;
+        if constexpr (g + kAAhead < NG) a_q[(g + kAAhead) % (kAAhead + 1)] = rd_a(slot, g + kAAhead);
         if constexpr (g < FN) b1[g] = *(const u32x4 *)(slot + b_frag + g * 16 * kWideRowBytes + chunk1);
         __builtin_amdgcn_sched_barrier(0);   // reads issue before the MFMAs that hide them
 #pragma unroll
-        for (int j = 0; j < FN; ++j) Mma<T>::run(a_q[g % (kAAhead + 1)], (g < 8) ? b0[j] : b1[j], acc[i][j]);
+        for (int j = 0; j < FN; ++j) Mma<T>::run(a_q[g % (kAAhead + 1)], (g < FM) ? b0[j] : b1[j], acc[i][j]);
         __builtin_amdgcn_sched_barrier(0);
       });
       // stage kb+1 has landed (its DMA is the only one outstanding) and every
@@ -1122,8 +1126,8 @@ __global__ __launch_bounds__(2 * WN_WAVES * 64, 1) void ns_gemm_wide_kernel(Gemm
       if (kb + 2 < nk) dma(kb + 2);
     }
   }
-  static_assert(NWAVES == 8, "epilogue_u8 takes 2 BM threads");
-  epilogue_u8<T, kBigTile, FM, FN>(cl, mat, tm, tn, wm * 128, wn * WTN, acc, (float *)lds);
+  static_assert(NWAVES * 64 == 2 * TILE, "epilogue_u8 takes 2 TILE threads");
+  epilogue_u8<T, TILE, FM, FN>(cl, mat, tm, tn, wm * WTM, wn * WTN, acc, (float *)lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -1618,10 +1622,15 @@ hipError_t launch_t(const GemmArgs &args, int tile, hipStream_t s) {
         hipLaunchKernelGGL((ns_gemm_kernel<T, 64, 64>), dim3(args.total_tiles), dim3(kThreads), 0, s, args);
       }
       break;
-    case 128: hipLaunchKernelGGL((ns_gemm_kernel<T, 128, 128>), dim3(args.total_tiles), dim3(kThreads), 0, s, args); break;
+    case 128:
+      if constexpr (sizeof(T) == 2)
+        hipLaunchKernelGGL((ns_gemm_wide_kernel<T, 128>), dim3(args.total_tiles), dim3(256), 0, s, args);
+      else
+        hipLaunchKernelGGL((ns_gemm_kernel<T, 128, 128>), dim3(args.total_tiles), dim3(kThreads), 0, s, args);
+      break;
     case 256:
       if constexpr (sizeof(T) == 2) {
-        hipLaunchKernelGGL((ns_gemm_wide_kernel<T, 4>), dim3(args.total_tiles), dim3(512), 0, s, args);
+        hipLaunchKernelGGL((ns_gemm_wide_kernel<T, 256>), dim3(args.total_tiles), dim3(512), 0, s, args);
         break;
       } else {
         return hipErrorInvalidValue;
