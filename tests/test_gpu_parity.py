@@ -493,3 +493,23 @@ def test_graph_survives_workspace_growth():
     for p, q in zip(pa, ref):
         assert torch.equal(p["weight"], q["weight"])
         assert torch.equal(p["momentum"], q["momentum"])
+
+
+# ---------------------------------------------------------------- tile-selection boundaries
+
+BOUNDARY = [(63, 130), (64, 64), (65, 200), (127, 70), (128, 300), (129, 129), (191, 400), (192, 193),
+            (193, 260), (255, 256), (256, 700), (257, 300), (383, 384), (384, 500), (385, 900), (511, 512),
+            (512, 520), (513, 600), (547, 700), (548, 640), (1024, 1100), (1096, 1200)]
+
+
+@pytest.mark.parametrize("ns_dtype,variant", [("bf16", "direct"), ("f16", "gram")])
+def test_tile_selection_boundaries(ns_dtype, variant):
+    """Short sides just below, at and above every tile and fused-update
+    threshold (64-tile padding to 64/128/192/256+, the 128 and 256 tiles and
+    their 7% padding limit), both orientations, many shape classes in one
+    call (launches split past 8 classes)."""
+    shapes = []
+    for i, (s, l) in enumerate(BOUNDARY):
+        shapes.append((s, l) if i % 2 == 0 else (l, s))
+    run_case(shapes, grad_dtype="bf16", ns_dtype=ns_dtype, variant=variant, grad_kind="spectral", seed=14,
+             divisor=1.03 if variant == "gram" else 1.0, restart_every=3 if variant == "gram" else 0)
