@@ -1246,7 +1246,7 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_small_kernel(GemmArgs args) 
 // Fused polynomial update of a direct Newton-Schulz step for short sides
 // s <= 192 (padded to SP):
 //   X'^T = alpha X^T B + beta X^T,   B = sq_alpha A A + sq_beta A,
-// with A = X X^T symmetric (Muon post: the quintic step a X + (b A + c A^2) X).
+// with A = X X^T symmetric (MONA summary, section 2 "Kernalgoritme": the quintic step a X + (b A + c A^2) X).
 // At these sizes every launch is a chain of memory latencies, so the square
 // A A is not a launch of its own: each block loads all of A (SP x SP) into
 // LDS, forms its 64-row panel of B there (rounded to T exactly as the
