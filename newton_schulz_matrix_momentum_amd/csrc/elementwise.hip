@@ -4,8 +4,9 @@
 //       (MONA summary, section 2 "Kernalgoritme", steps 1-4)
 //   norm_finalize  per-matrix 1 / (sqrt(d) ||M||_F), fixed summation order
 //   E2  X0 = M / (sqrt(d) ||M||_F) rounded to the Newton-Schulz dtype, stored
-//       in both orientations (Gram Newton-Schulz post: the divisor keeps the
-//       Gram's eigenvalues inside [0, 1])
+//       in both orientations, or in the one the products read (Gram
+//       Newton-Schulz post: the divisor keeps the Gram's eigenvalues inside
+//       [0, 1])
 //   E3  W = W - lr (gamma O + lambda W)  (MONA summary, step 4)
 //
 // All loads and stores are 16-byte vectors where alignment allows; every
@@ -315,8 +316,9 @@ __global__ __launch_bounds__(256) void e2_kernel(E2Args args) {
       o[q] = Elem<NDT>::to_f32(Elem<NDT>::from_f32(v[it][q] * scale));
       tile[rr + 16 * it][cg + q] = o[q];
     }
-    *(nvec *)(nat + (int64_t)r * mt.ld_nat + c) = Vec4<NDT>::pack(o);
+    if (nat) *(nvec *)(nat + (int64_t)r * mt.ld_nat + c) = Vec4<NDT>::pack(o);
   }
+  if (!trn) return;   // uniform per matrix
   __syncthreads();
 #pragma unroll
   for (int it = 0; it < 4; ++it) {

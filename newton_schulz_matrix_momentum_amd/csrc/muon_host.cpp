@@ -501,9 +501,20 @@ std::vector<DirectStep> direct_steps(const Plan &plan, double sx0) {
 // Direct steps of classes with a short side of at most 192 (16-bit, 64
 // tiles) form B = b A + c A^2 inside the update launch
 // (ns_poly_update_kernel) instead of in a launch of its own: at these sizes
-// a launch costs more than the redundant panel products.
+// a launch costs more than the redundant panel products.  That kernel reads
+// the iterate in its wide layout X only, so X^T is written only for a cubic
+// step's separate update product (c = 0: no square to fuse).
 bool poly_fused(const Plan &plan, const ClassInfo &cl) {
   return plan.set.ns_dtype != kF32 && cl.tile == 64 && cl.Sp <= 192;
+}
+
+bool step_cubic(const Plan &plan, int k) { return plan.set.coeffs[3 * (k - 1) + 2] == 0.0f; }
+
+// X0^T is needed only when the first product to read the iterate is a
+// separate update product: Gram, or a direct first step that is cubic or not
+// fused.
+bool needs_x0_transposed(const Plan &plan, const ClassInfo &cl) {
+  return !(plan.variant == MUON_NS_DIRECT && plan.K > 0 && poly_fused(plan, cl) && !step_cubic(plan, 1));
 }
 
 int device_cus() {
@@ -629,7 +640,13 @@ muon_status run_direct(const Plan &plan, char *ws, Tracer &st, double sx0, float
         sb.per_class[ci] = g;
         sb.per_flops[ci] = full_flops(cl);
         if (fuse[ci]) {
-          // same product with A in place of B; the block forms its panel of B
+          // same product with A in place of B (the block forms its panel of
+          // B) and X in place of X^T; X'^T only for a following cubic step
+          g.a = ws + cl.X[cur];
+          g.sa = cl.Sp * cl.Lp;
+          g.lda = (int32_t)cl.Lp;
+          g.cin = nullptr;
+          if (k < plan.K && !step_cubic(plan, k + 1)) g.c = nullptr;
           g.b = ws + cl.sq[0];
           g.sq_alpha = (float)ds.sq_alpha;
           g.sq_beta = (float)ds.sq_beta;
@@ -953,6 +970,8 @@ muon_status muon_step(const muon_param *params, int n, float lr, float mu, float
       m.mom = params[i].momentum;
       m.nat = ws + (wide ? cl.X[0] : cl.XT[0]) + j * rect;
       m.trn = ws + (wide ? cl.XT[0] : cl.X[0]) + j * rect;
+      const bool both = needs_x0_transposed(plan, cl);
+      if (!both) (wide ? m.trn : m.nat) = nullptr;   // X^T (the tall layout) is not read
       m.rows = (int32_t)params[i].rows;
       m.cols = (int32_t)params[i].cols;
       const int64_t prow = wide ? cl.Sp : cl.Lp, pcol = wide ? cl.Lp : cl.Sp;
@@ -966,8 +985,8 @@ muon_status muon_step(const muon_param *params, int n, float lr, float mu, float
         m.nparts = plan.e1_blocks[i];
       }
       blocks += (int)((prow / kE2Tile) * (pcol / kE2Tile));
-      // M read (fp32), X0 written in both orientations
-      bytes += (4.0 + 2.0 * (double)es) * (double)(params[i].rows * params[i].cols);
+      // M read (fp32), X0 written in one or both orientations
+      bytes += (4.0 + (both ? 2.0 : 1.0) * (double)es) * (double)(params[i].rows * params[i].cols);
     }
     if (a.nmat) HIP_TRY(tr.run(MUON_STAGE_E2, bytes, [&]() { return launch_e2(a, blocks, hs); }));
     HIP_TRY(tr.close());

@@ -102,8 +102,8 @@ constexpr int kE2InlineParts = 64;
 
 struct E2Mat {
   const float *mom;
-  void *nat;
-  void *trn;
+  void *nat;                 // M's own layout, or NULL when not read
+  void *trn;                 // its transpose, or NULL when not read
   int32_t rows, cols;        // true M shape
   int32_t ld_nat, ld_trn;    // = padded cols, padded rows
   int32_t tiles_c;           // padded cols / 64

@@ -33,6 +33,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 // s_waitcnt vmcnt(n), leaving expcnt and lgkmcnt alone.  gfx9 encoding:
 // vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].  n >= 64 waits
@@ -1253,22 +1254,31 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_small_kernel(GemmArgs args) 
 // separate square product stores it), and then runs the update product for a
 // group of up to poly_max_group(SP) output tiles that share the panel.
 //
-// LDS (64-k stages of 128-byte rows, chunk c of row r at c ^ (r & 7)):
+// X is read in its wide layout (s x l, the buffer the Gram product X X^T
+// reads), so the iterate is kept in one orientation only.  Output row tile t
+// of X'^T needs the 64 columns [64 t, 64 t + 64) of X over all SP rows: one
+// 128-byte row per k.  Its MFMA operand (8 consecutive k of one column per
+// lane) comes from two transposing LDS reads (ds_read_b64_tr_b16: within
+// each 16-lane group, lane l receives element l % 4 of the 8 bytes that lane
+// 4 e + l / 4 addressed, as its element e).
+//
+// LDS (128-byte rows, chunk c of row r at c ^ (r & 7)):
 //   region 0  all of A (SP / 64 stages of SP rows); once the panel is formed:
-//             X^T tiles 2 and 3 of the group and the epilogue's staging tiles
+//             X tiles 2 and 3 of the group and the epilogue's staging tiles
 //   panel     SP / 64 stages of 64 rows (rows of B for this block's columns)
-//   X^T       tiles 0 and 1 of the group (SP / 64 stages of 64 rows each)
+//   X         tiles 0 and 1 of the group (SP rows of 64 columns each)
 // The panel product is computed transposed, P^T = A A_panel^T (A symmetric),
 // so each lane's accumulator holds 4 consecutive k of one panel row and is
-// written with one 8-byte LDS store.  Every X^T tile has landed before the
+// written with one 8-byte LDS store.  Every X tile has landed before the
 // first global store, so the vmcnt-counted DMA waits never count stores.
 //
-// Epilogue per output tile: v = alpha acc + beta X^T (X^T read from LDS) is
+// Epilogue per output tile: v = alpha acc + beta X^T (X read from LDS) is
 // staged as fp32 in a 64 x 64 tile (two staging tiles alternate, so one
-// barrier per output tile suffices); a row-major sweep stores X'^T rows (or
-// applies the fp32 weight update of a tall W) and a transposed sweep stores
-// the X' copy (or the update of a wide W), 16 bytes per access.  The next
-// tile's operands are read from LDS while the current one is staged.
+// barrier per output tile suffices); a transposed sweep stores X' (or applies
+// the fp32 weight update of a wide W) and, only where a later product reads
+// the other orientation, a row-major sweep stores X'^T (or the update of a
+// tall W), 16 bytes per access.  The next tile's operands are read from LDS
+// while the current one is staged.
 template <int SP>
 struct PolyLayout {
   static constexpr int A_BYTES = SP * SP * 2;
@@ -1299,7 +1309,7 @@ __global__ __launch_bounds__(kThreads) void ns_poly_update_kernel(GemmArgs args)
   constexpr int NKS = 2 * NST;          // 32-k MFMA steps
   constexpr int FM1 = SP / 64;          // 16-row blocks per wave in the panel product (SP / 4 rows)
   constexpr int A_DMA = SP / 32;        // DMA instructions per wave and stage of A (8 rows each)
-  constexpr int X_DMA = 2 * NST;        // DMA instructions per wave for one X^T tile
+  constexpr int X_DMA = SP / 32;        // DMA instructions per wave for one X tile (8 rows each)
   __shared__ __attribute__((aligned(1024))) char lds[L::TOTAL];
   char *const la = lds;
   char *const lp = lds + L::R0_BYTES;
@@ -1316,7 +1326,7 @@ __global__ __launch_bounds__(kThreads) void ns_poly_update_kernel(GemmArgs args)
   const int wm = wave >> 1, wn = wave & 1;
 
   const char *Am = (const char *)cl.b + (int64_t)mat * cl.sb * 2;
-  const char *Xm = (const char *)cl.a + (int64_t)mat * cl.sa * 2;
+  const char *Xm = (const char *)cl.a + (int64_t)mat * cl.sa * 2;   // X, wide: SP rows of lda
   const int64_t lda_b = (int64_t)cl.lda * 2, ldb_b = (int64_t)cl.ldb * 2;
   const int dma_row = lane >> 3;
   const int dma_chunk = (lane & 7) ^ dma_row;
@@ -1332,22 +1342,19 @@ __global__ __launch_bounds__(kThreads) void ns_poly_update_kernel(GemmArgs args)
           (void __attribute__((address_space(3))) *)(la + kb * SP * kWideRowBytes + r0 * kWideRowBytes), 16, 0, 0);
     }
   }
-  // LDS home of X^T tile t of the group
+  // LDS home of X tile t of the group
   auto xbuf = [&](int t) -> char * { return t < 2 ? lx + t * L::P_BYTES : la + (t - 2) * L::P_BYTES; };
-  // X^T output row tile tm0 + t: wave w moves rows [16 w, 16 w + 16)
+  // X tile of output row tile tm0 + t: columns [64 (tm0 + t), +64) of X rows
+  // 0 .. SP-1; wave w moves rows [w SP/4, (w+1) SP/4)
   auto dma_x = [&](int t) {
-    const char *src = Xm + (int64_t)(tm0 + t) * kSmallTile * lda_b;
+    const char *src = Xm + (int64_t)(tm0 + t) * kWideRowBytes;
     char *dst = xbuf(t);
 #pragma unroll
-    for (int kb = 0; kb < NST; ++kb)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int r0 = wave * 16 + j * 8;
-        __builtin_amdgcn_global_load_lds(
-            (const void *)(src + (int64_t)(r0 + dma_row) * lda_b + kb * kWideRowBytes + dma_chunk * 16),
-            (void __attribute__((address_space(3))) *)(dst + kb * kSmallTile * kWideRowBytes + r0 * kWideRowBytes), 16,
-            0, 0);
-      }
+    for (int j = 0; j < X_DMA; ++j) {
+      const int r0 = wave * (SP / 4) + j * 8;
+      __builtin_amdgcn_global_load_lds((const void *)(src + (int64_t)(r0 + dma_row) * lda_b + dma_chunk * 16),
+                                       (void __attribute__((address_space(3))) *)(dst + r0 * kWideRowBytes), 16, 0, 0);
+    }
   };
   dma_x(0);
   const int early = nt > 1 ? 2 : 1;
@@ -1428,14 +1435,13 @@ __global__ __launch_bounds__(kThreads) void ns_poly_update_kernel(GemmArgs args)
     if (nt > 2) dma_x(2);
     if (nt > 3) dma_x(3);
   }
-  waitcnt_vm(0);   // every X^T tile of the group has landed
+  waitcnt_vm(0);   // every X tile of the group has landed
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_barrier" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- update product and epilogue for each output row tile of the group
   constexpr int FM = 2, FN = 2;
-  const int a_frag = (wm * 32 + fr_row) * kWideRowBytes;
   const int b_frag = (wn * 32 + fr_row) * kWideRowBytes;
   const float alpha = cl.alpha, beta = cl.beta;
   FinalDesc fd{};
@@ -1447,33 +1453,51 @@ __global__ __launch_bounds__(kThreads) void ns_poly_update_kernel(GemmArgs args)
   void *C = cl.c ? (void *)((char *)cl.c + (int64_t)mat * cl.sc * 2) : nullptr;
   void *C2 = cl.c2 ? (void *)((char *)cl.c2 + (int64_t)mat * cl.sc2 * 2) : nullptr;
   // operands of a whole tile (every k step) and its X^T entries for Cin, read
-  // from LDS one tile ahead so the reads overlap the previous tile's epilogue
+  // from LDS one tile ahead so the reads overlap the previous tile's epilogue.
+  // A operand (output row m = wm 32 + 16 i + l, k = 32 ks + 8 g + 0..7, lane
+  // = 16 g + l): transposing read h covers k + 4 h .. 4 h + 3; lane 16 g + j
+  // addresses X row 32 ks + 8 g + 4 h + j / 4, columns m0 + 4 (j % 4) .. + 3.
   u32x4 fa[NKS][FM], fb[NKS][FN];
-  uint16_t cu[FM][FN][4];
+  uint2 cu[FM][FN];
+  const int tj = lane & 15, tg = lane >> 4;
+  int tr_off[2][FM];   // byte offset within a 32-k step, per half h and row block i
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int r = 8 * tg + 4 * h + (tj >> 2);      // row within the 32-k step (r & 7 = 4 h + tj / 4)
+      const int c = wm * 32 + i * 16 + 4 * (tj & 3);  // first of 4 columns
+      tr_off[h][i] = r * kWideRowBytes + (((c >> 3) ^ (r & 7)) << 4) + (c & 7) * 2;
+    }
   auto load_tile = [&](int t) {
     const char *xb = xbuf(t);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      const char *sx = xb + (ks >> 1) * kSmallTile * kWideRowBytes;
+      const char *sx = xb + ks * 32 * kWideRowBytes;
       const char *sp = lp + (ks >> 1) * kSmallTile * kWideRowBytes;
       const int ch = kchunk(ks);
 #pragma unroll
-      for (int i = 0; i < FM; ++i) fa[ks][i] = *(const u32x4 *)(sx + a_frag + i * 16 * kWideRowBytes + ch);
+      for (int i = 0; i < FM; ++i) {
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4 *)(sx + tr_off[0][i]));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4 *)(sx + tr_off[1][i]));
+        const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+        fa[ks][i] = u32x4{l2.x, l2.y, h2.x, h2.y};
+      }
 #pragma unroll
       for (int j = 0; j < FN; ++j) fb[ks][j] = *(const u32x4 *)(sp + b_frag + j * 16 * kWideRowBytes + ch);
     }
-    // the tile's own X^T entries: columns tn * 64 + jc are k stage tn
-    const char *cx = xb + tn * kSmallTile * kWideRowBytes;
+    // the tile's own X^T entries X^T[ir .. ir+3][jc] = X[tn 64 + jc][ir .. ir+3]:
+    // one 8-byte read each
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int ir = wm * 32 + i * 16 + 4 * (lane >> 4) + q;
-          const int jc = wn * 32 + j * 16 + (lane & 15);
-          cu[i][j][q] = *(const uint16_t *)(cx + ir * kWideRowBytes + (((jc >> 3) ^ (ir & 7)) << 4) + (jc & 7) * 2);
-        }
+      for (int j = 0; j < FN; ++j) {
+        const int ir = wm * 32 + i * 16 + 4 * (lane >> 4);
+        const int kr = tn * 64 + wn * 32 + j * 16 + (lane & 15);
+        cu[i][j] = *(const uint2 *)(xb + kr * kWideRowBytes + (((ir >> 3) ^ (kr & 7)) << 4) + (ir & 7) * 2);
+      }
   };
   load_tile(0);
   static_for<0, L::MAXG>([&](auto tc) {
@@ -1496,7 +1520,10 @@ __global__ __launch_bounds__(kThreads) void ns_poly_update_kernel(GemmArgs args)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) cin[i][j][q] = (float)__builtin_bit_cast(T, cu[i][j][q]);
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t w = (q < 2) ? cu[i][j].x : cu[i][j].y;
+            cin[i][j][q] = (float)__builtin_bit_cast(T, (uint16_t)((q & 1) ? (w >> 16) : (w & 0xFFFF)));
+          }
       if (t + 1 < nt) load_tile(t + 1);
       // v = alpha acc + beta X^T, staged (alternating staging tiles: the
       // previous barrier already ordered the sweeps of tile t - 2)

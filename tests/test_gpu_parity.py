@@ -29,14 +29,15 @@ def _gpu():
 
 def run_case(shapes, *, grad_dtype, ns_dtype, variant="direct", kind="quintic", ns_steps=5, mona=False, steps=1,
              divisor=1.0, restart_every=0, lr=0.02, mu=0.95, wd=0.01, beta_a=0.9, alpha=0.5, seed=0,
-             grad_kind="gaussian", gammas=None):
+             grad_kind="gaussian", gammas=None, coeffs=None):
     import newton_schulz_matrix_momentum_amd as nsm
     label = "%s %s/%s %s mona=%s" % (shapes[:3], grad_dtype, ns_dtype, variant, mona)
     print("case:", label, flush=True)
     params = make_params(shapes, grad_dtype, mona, seed, gammas=gammas)
     for p in params:
         p["ortho_out"] = torch.full(p["weight"].shape, float("nan"), dtype=torch.float32, device="cuda")
-    coeffs = oracle.coefficient_table(kind, ns_steps)
+    if coeffs is None:
+        coeffs = oracle.coefficient_table(kind, ns_steps)
     worst = (0.0, 0.0)
     ostate = oracle_state(snapshot(params))   # the oracle carries its own state
     lite_bounds = {}
@@ -106,6 +107,20 @@ def test_fused_square_update_groups(ns_dtype):
     shapes = [(192, 1408)] * 6 + [(1408, 192)] * 6 + [(150, 700)] * 10 + [(700, 150)] * 10 + \
         [(64, 320), (320, 64), (128, 200), (200, 128)]
     run_case(shapes, grad_dtype="bf16", ns_dtype=ns_dtype, grad_kind="spectral", seed=12)
+
+
+@pytest.mark.parametrize("ns_dtype,order", [("bf16", "cqcqq"), ("f16", "qcqcq")])
+def test_mixed_cubic_quintic_steps(ns_dtype, order):
+    """Per-step coefficient tables mixing cubic (c = 0) and quintic steps on
+    short sides <= 192: a quintic step runs fused and reads the iterate in
+    one layout, a cubic step runs the separate update product that also
+    reads X^T, so the layouts written before each step must follow the
+    table (X0^T only when step 1 is cubic, X'^T only ahead of a cubic step)."""
+    rows = {"c": oracle.coefficient_table("cubic", 1)[0], "q": oracle.coefficient_table("quintic", 1)[0]}
+    coeffs = np.array([rows[ch] for ch in order])
+    shapes = [(150, 700), (700, 150), (192, 192), (64, 320), (320, 64), (100, 64)]
+    run_case(shapes, grad_dtype="f32", ns_dtype=ns_dtype, grad_kind="spectral", ns_steps=len(order), coeffs=coeffs,
+             seed=14)
 
 
 @pytest.mark.parametrize("ns_dtype", ["bf16", "f16"])
