@@ -1272,13 +1272,15 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_small_kernel(GemmArgs args) 
 // written with one 8-byte LDS store.  Every X tile has landed before the
 // first global store, so the vmcnt-counted DMA waits never count stores.
 //
-// Epilogue per output tile: v = alpha acc + beta X^T (X read from LDS) is
-// staged as fp32 in a 64 x 64 tile (two staging tiles alternate, so one
-// barrier per output tile suffices); a transposed sweep stores X' (or applies
-// the fp32 weight update of a wide W) and, only where a later product reads
-// the other orientation, a row-major sweep stores X'^T (or the update of a
-// tall W), 16 bytes per access.  The next tile's operands are read from LDS
-// while the current one is staged.
+// Epilogue per output tile: v = alpha acc + beta X^T (X read from LDS).
+// When X' alone is stored, each lane writes its 4 consecutive long-side
+// entries of one X' row as one 8-byte vector, straight from the accumulator
+// layout.  Otherwise (the weight update, or X'^T also wanted ahead of a
+// cubic step) v is staged as fp32 in a 64 x 64 tile (two staging tiles
+// alternate, so one barrier per output tile suffices); a transposed sweep
+// stores X' (or applies the fp32 weight update of a wide W) and a row-major
+// sweep stores X'^T (or the update of a tall W), 16 bytes per access.  The
+// next tile's operands are read from LDS while the current one is finished.
 template <int SP>
 struct PolyLayout {
   static constexpr int A_BYTES = SP * SP * 2;
@@ -1525,100 +1527,126 @@ __global__ __launch_bounds__(kThreads) void ns_poly_update_kernel(GemmArgs args)
             cin[i][j][q] = (float)__builtin_bit_cast(T, (uint16_t)((q & 1) ? (w >> 16) : (w & 0xFFFF)));
           }
       if (t + 1 < nt) load_tile(t + 1);
-      // v = alpha acc + beta X^T, staged (alternating staging tiles: the
-      // previous barrier already ordered the sweeps of tile t - 2)
-      float *stg = (t & 1) ? (SP == 192 ? (float *)lx : (float *)(la + L::S_BYTES)) : (float *)(la + L::S0_OFF);
+      if (!cl.final_mode && !C) {
+        // X' alone: a lane's 4 accumulator rows are 4 consecutive long-side
+        // entries of one X' row, stored as one 8-byte vector (the same fp32
+        // fma and rounding as the staged path; the empty asm keeps the fma
+        // and the conversion two roundings)
+        if (C2) {
+          const int row0 = (tm0 + t) * kSmallTile, col0 = tn * kSmallTile;
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+          for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int ir = wm * 32 + i * 16 + 4 * (lane >> 4) + q;
-            const int jc = wn * 32 + j * 16 + (lane & 15);
-            stg[spos(ir, jc)] = __builtin_fmaf(beta, cin[i][j][q], alpha * acc[i][j][q]);
-          }
-      lds_barrier();
-      const int row0 = (tm0 + t) * kSmallTile;   // tile rows index the long side
-      const int col0 = tn * kSmallTile;          // tile columns index the short side
-      // row-major sweep: thread -> (tile row tid / 4, 16 columns)
-      {
-        const int r = tid >> 2, c0 = (tid & 3) * 16;
-        float v[16];
-        const float *src = stg + spos(r, c0);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float4 x = *(const float4 *)(src + 4 * e);
-          v[4 * e] = x.x; v[4 * e + 1] = x.y; v[4 * e + 2] = x.z; v[4 * e + 3] = x.w;
-        }
-        if (!cl.final_mode) {
-          if (C) {
-            T *dst = (T *)C + (int64_t)(row0 + r) * cl.ldc + col0 + c0;
-            Pack<T>::copy(dst, (const float4 *)v);
-            Pack<T>::copy(dst + 8, (const float4 *)(v + 8));
-          }
-        } else if (!fd.wide && row0 + r < fd.rows) {
-          const int i = row0 + r, j0 = col0 + c0;
-          const float lr = cl.lr, wd = cl.wd, gm = fd.gamma;
-          float *wrow = fd.weight + (int64_t)i * fd.cols;
-          float *orow = fd.ortho_out ? fd.ortho_out + (int64_t)i * fd.cols : nullptr;
-          if (fvec && j0 + 16 <= fd.cols) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              float4 w = *(const float4 *)(wrow + j0 + 4 * e);
-              w.x = w.x - lr * (gm * v[4 * e] + wd * w.x);
-              w.y = w.y - lr * (gm * v[4 * e + 1] + wd * w.y);
-              w.z = w.z - lr * (gm * v[4 * e + 2] + wd * w.z);
-              w.w = w.w - lr * (gm * v[4 * e + 3] + wd * w.w);
-              *(float4 *)(wrow + j0 + 4 * e) = w;
-              if (orow) *(float4 *)(orow + j0 + 4 * e) = make_float4(v[4 * e], v[4 * e + 1], v[4 * e + 2], v[4 * e + 3]);
+            for (int j = 0; j < FN; ++j) {
+              const int ir = wm * 32 + i * 16 + 4 * (lane >> 4);
+              const int jc = wn * 32 + j * 16 + (lane & 15);
+              float v0 = __builtin_fmaf(beta, cin[i][j][0], alpha * acc[i][j][0]);
+              float v1 = __builtin_fmaf(beta, cin[i][j][1], alpha * acc[i][j][1]);
+              float v2 = __builtin_fmaf(beta, cin[i][j][2], alpha * acc[i][j][2]);
+              float v3 = __builtin_fmaf(beta, cin[i][j][3], alpha * acc[i][j][3]);
+              asm volatile("" : "+v"(v0), "+v"(v1), "+v"(v2), "+v"(v3));
+              uint2 u;
+              u.x = Pack16<T>::pair(v0, v1);
+              u.y = Pack16<T>::pair(v2, v3);
+              *(uint2 *)((T *)C2 + (int64_t)(col0 + jc) * cl.ldc2 + row0 + ir) = u;
             }
-          } else {
+        }
+      } else {
+        // v = alpha acc + beta X^T, staged (alternating staging tiles: the
+        // previous barrier already ordered the sweeps of tile t - 2)
+        float *stg = (t & 1) ? (SP == 192 ? (float *)lx : (float *)(la + L::S_BYTES)) : (float *)(la + L::S0_OFF);
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-              if (j0 + e < fd.cols) {
-                const float w = wrow[j0 + e];
-                wrow[j0 + e] = w - lr * (gm * v[e] + wd * w);
-                if (orow) orow[j0 + e] = v[e];
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int ir = wm * 32 + i * 16 + 4 * (lane >> 4) + q;
+              const int jc = wn * 32 + j * 16 + (lane & 15);
+              stg[spos(ir, jc)] = __builtin_fmaf(beta, cin[i][j][q], alpha * acc[i][j][q]);
+            }
+        lds_barrier();
+        const int row0 = (tm0 + t) * kSmallTile;   // tile rows index the long side
+        const int col0 = tn * kSmallTile;          // tile columns index the short side
+        // row-major sweep: thread -> (tile row tid / 4, 16 columns)
+        {
+          const int r = tid >> 2, c0 = (tid & 3) * 16;
+          float v[16];
+          const float *src = stg + spos(r, c0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float4 x = *(const float4 *)(src + 4 * e);
+            v[4 * e] = x.x; v[4 * e + 1] = x.y; v[4 * e + 2] = x.z; v[4 * e + 3] = x.w;
+          }
+          if (!cl.final_mode) {
+            if (C) {
+              T *dst = (T *)C + (int64_t)(row0 + r) * cl.ldc + col0 + c0;
+              Pack<T>::copy(dst, (const float4 *)v);
+              Pack<T>::copy(dst + 8, (const float4 *)(v + 8));
+            }
+          } else if (!fd.wide && row0 + r < fd.rows) {
+            const int i = row0 + r, j0 = col0 + c0;
+            const float lr = cl.lr, wd = cl.wd, gm = fd.gamma;
+            float *wrow = fd.weight + (int64_t)i * fd.cols;
+            float *orow = fd.ortho_out ? fd.ortho_out + (int64_t)i * fd.cols : nullptr;
+            if (fvec && j0 + 16 <= fd.cols) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                float4 w = *(const float4 *)(wrow + j0 + 4 * e);
+                w.x = w.x - lr * (gm * v[4 * e] + wd * w.x);
+                w.y = w.y - lr * (gm * v[4 * e + 1] + wd * w.y);
+                w.z = w.z - lr * (gm * v[4 * e + 2] + wd * w.z);
+                w.w = w.w - lr * (gm * v[4 * e + 3] + wd * w.w);
+                *(float4 *)(wrow + j0 + 4 * e) = w;
+                if (orow) *(float4 *)(orow + j0 + 4 * e) = make_float4(v[4 * e], v[4 * e + 1], v[4 * e + 2], v[4 * e + 3]);
+              }
+            } else {
+#pragma unroll
+              for (int e = 0; e < 16; ++e) {
+                if (j0 + e < fd.cols) {
+                  const float w = wrow[j0 + e];
+                  wrow[j0 + e] = w - lr * (gm * v[e] + wd * w);
+                  if (orow) orow[j0 + e] = v[e];
+                }
               }
             }
           }
         }
-      }
-      // transposed sweep: thread -> (tile column tid / 4, 16 rows)
-      if (!cl.final_mode ? (C2 != nullptr) : (bool)fd.wide) {
-        const int c = tid >> 2, r0 = (tid & 3) * 16;
-        float v[16];
+        // transposed sweep: thread -> (tile column tid / 4, 16 rows)
+        if (!cl.final_mode ? (C2 != nullptr) : (bool)fd.wide) {
+          const int c = tid >> 2, r0 = (tid & 3) * 16;
+          float v[16];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) v[e] = stg[spos(r0 + e, c)];
-        if (!cl.final_mode) {
-          T *dst = (T *)C2 + (int64_t)(col0 + c) * cl.ldc2 + row0 + r0;
-          Pack<T>::copy(dst, (const float4 *)v);
-          Pack<T>::copy(dst + 8, (const float4 *)(v + 8));
-        } else if (col0 + c < fd.rows) {
-          // wide W: row col0 + c, columns row0 + r0 ..
-          const int i = col0 + c, j0 = row0 + r0;
-          const float lr = cl.lr, wd = cl.wd, gm = fd.gamma;
-          float *wrow = fd.weight + (int64_t)i * fd.cols;
-          float *orow = fd.ortho_out ? fd.ortho_out + (int64_t)i * fd.cols : nullptr;
-          if (fvec && j0 + 16 <= fd.cols) {
+          for (int e = 0; e < 16; ++e) v[e] = stg[spos(r0 + e, c)];
+          if (!cl.final_mode) {
+            T *dst = (T *)C2 + (int64_t)(col0 + c) * cl.ldc2 + row0 + r0;
+            Pack<T>::copy(dst, (const float4 *)v);
+            Pack<T>::copy(dst + 8, (const float4 *)(v + 8));
+          } else if (col0 + c < fd.rows) {
+            // wide W: row col0 + c, columns row0 + r0 ..
+            const int i = col0 + c, j0 = row0 + r0;
+            const float lr = cl.lr, wd = cl.wd, gm = fd.gamma;
+            float *wrow = fd.weight + (int64_t)i * fd.cols;
+            float *orow = fd.ortho_out ? fd.ortho_out + (int64_t)i * fd.cols : nullptr;
+            if (fvec && j0 + 16 <= fd.cols) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              float4 w = *(const float4 *)(wrow + j0 + 4 * e);
-              w.x = w.x - lr * (gm * v[4 * e] + wd * w.x);
-              w.y = w.y - lr * (gm * v[4 * e + 1] + wd * w.y);
-              w.z = w.z - lr * (gm * v[4 * e + 2] + wd * w.z);
-              w.w = w.w - lr * (gm * v[4 * e + 3] + wd * w.w);
-              *(float4 *)(wrow + j0 + 4 * e) = w;
-              if (orow) *(float4 *)(orow + j0 + 4 * e) = make_float4(v[4 * e], v[4 * e + 1], v[4 * e + 2], v[4 * e + 3]);
-            }
-          } else {
+              for (int e = 0; e < 4; ++e) {
+                float4 w = *(const float4 *)(wrow + j0 + 4 * e);
+                w.x = w.x - lr * (gm * v[4 * e] + wd * w.x);
+                w.y = w.y - lr * (gm * v[4 * e + 1] + wd * w.y);
+                w.z = w.z - lr * (gm * v[4 * e + 2] + wd * w.z);
+                w.w = w.w - lr * (gm * v[4 * e + 3] + wd * w.w);
+                *(float4 *)(wrow + j0 + 4 * e) = w;
+                if (orow) *(float4 *)(orow + j0 + 4 * e) = make_float4(v[4 * e], v[4 * e + 1], v[4 * e + 2], v[4 * e + 3]);
+              }
+            } else {
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-              if (j0 + e < fd.cols) {
-                const float w = wrow[j0 + e];
-                wrow[j0 + e] = w - lr * (gm * v[e] + wd * w);
-                if (orow) orow[j0 + e] = v[e];
+              for (int e = 0; e < 16; ++e) {
+                if (j0 + e < fd.cols) {
+                  const float w = wrow[j0 + e];
+                  wrow[j0 + e] = w - lr * (gm * v[e] + wd * w);
+                  if (orow) orow[j0 + e] = v[e];
+                }
               }
             }
           }
