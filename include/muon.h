@@ -91,7 +91,7 @@ typedef struct muon_param {
 typedef enum muon_stage {
   MUON_STAGE_E1 = 0,     /* MONA + momentum + Frobenius partials              */
   MUON_STAGE_NORM = 1,   /* per-matrix normalisation scale                     */
-  MUON_STAGE_E2 = 2,     /* X0 in the Newton-Schulz dtype, both orientations   */
+  MUON_STAGE_E2 = 2,     /* X0 in the Newton-Schulz dtype, layouts the NS reads */
   MUON_STAGE_GEMM = 3,   /* one grouped Newton-Schulz matrix product           */
   MUON_STAGE_E3 = 4,     /* decoupled weight-decay update                      */
   MUON_STAGE_ADAMW = 5   /* AdamW over vector parameters (muon_adamw_step)     */
