@@ -4,8 +4,10 @@
 // stored row-major along k ("NT"): the Gram X X^T, the square A A of a
 // symmetric matrix (A A = A A^T), and the update X^T B with B symmetric
 // (Gram Newton-Schulz post: the Gram matrix and its polynomials are
-// symmetric).  Both orientations of the iterate are kept in HBM, so no
-// operand is ever transposed on the fly.
+// symmetric).  Both orientations of the iterate are kept in HBM, so these
+// products never transpose an operand; the fused update of short sides
+// reads the iterate in its wide layout through gfx950's transposing LDS
+// reads instead, and keeps that one layout.
 //
 // One launch covers every matrix of a step that shares a tile shape ("grouped
 // launch"): blockIdx selects (class, matrix, tile) from the kernel-argument
@@ -17,11 +19,12 @@
 // X' = a X + B X, plus the storage scale of fp16 buffers.
 //
 // Operands: fp16 / bf16 use v_mfma_f32_16x16x32_{f16,bf16}; fp32 uses
-// v_mfma_f32_16x16x4_f32.  Accumulation is always fp32.  Three block tiles:
-// 64 x 64 (latency-bound small products, 16-bit), 128 x 128 (register-staged
-// loads; also every fp32 product) and 256 x 256 (global -> LDS DMA, 16-bit);
-// and for direct steps with short sides up to 192, one kernel that forms the
-// square A A inside the update product (ns_poly_update_kernel).  All
+// v_mfma_f32_16x16x4_f32.  Accumulation is always fp32.  16-bit block
+// tiles: 64 x 64 (latency-bound small products), 128 x 128 and 256 x 256
+// (global -> LDS DMA); fp32 products use register-staged 64 x 64 and
+// 128 x 128 tiles; and for direct steps with short sides up to 192, one
+// kernel forms the square A A inside the update product
+// (ns_poly_update_kernel).  All
 // workspace buffers are zero-padded to tile multiples, so the main loops have
 // no bounds checks.
 #include "muon_kernels.h"
