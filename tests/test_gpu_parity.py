@@ -109,6 +109,18 @@ def test_fused_square_update_groups(ns_dtype):
     run_case(shapes, grad_dtype="bf16", ns_dtype=ns_dtype, grad_kind="spectral", seed=12)
 
 
+@pytest.mark.parametrize("ns_dtype", ["bf16", "f16"])
+def test_fused_update_launch_split(ns_dtype):
+    """Ten classes whose short side pads to 192 (s = 130 .. 184) in one
+    call: the fused update's launch takes at most 8 classes, so the step
+    runs it as two launches (8 + 2 classes); both orientations."""
+    shapes = []
+    for i in range(10):
+        s, l = 130 + 6 * i, 150 + 37 * i
+        shapes.append((s, l) if i % 2 == 0 else (l, s))
+    run_case(shapes, grad_dtype="bf16", ns_dtype=ns_dtype, grad_kind="spectral", seed=15)
+
+
 @pytest.mark.parametrize("ns_dtype,order", [("bf16", "cqcqq"), ("f16", "qcqcq")])
 def test_mixed_cubic_quintic_steps(ns_dtype, order):
     """Per-step coefficient tables mixing cubic (c = 0) and quintic steps on
