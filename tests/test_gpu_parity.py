@@ -109,6 +109,15 @@ def test_fused_square_update_groups(ns_dtype):
     run_case(shapes, grad_dtype="bf16", ns_dtype=ns_dtype, grad_kind="spectral", seed=12)
 
 
+@pytest.mark.parametrize("ns_dtype", ["f32", "bf16"])
+def test_long_thin_matrices(ns_dtype):
+    """Extreme aspect ratios: long sides of 9000 to 70001 with short sides 1
+    to 17 (over a thousand 64-row tiles per matrix on the fused path, norms
+    over several E1 blocks, ragged long-side tails), both orientations."""
+    shapes = [(1, 70001), (40003, 3), (17, 9000), (9001, 5)]
+    run_case(shapes, grad_dtype="f32", ns_dtype=ns_dtype, grad_kind="gaussian", seed=16)
+
+
 @pytest.mark.parametrize("ns_dtype", ["bf16", "f16"])
 def test_fused_update_launch_split(ns_dtype):
     """Ten classes whose short side pads to 192 (s = 130 .. 184) in one
