@@ -360,7 +360,8 @@ struct StageBuilder {
       reset();
       double flops = 0.0;
       auto go = [&]() -> hipError_t {
-        const GemmArgs a = args;
+        GemmArgs a = args;
+        a.xcd_group = tile == 128 ? 0 : kXcdGroup;
         const int dt = plan.set.ns_dtype;
         return tr.run(MUON_STAGE_GEMM, flops, [&]() { return launch_gemm(a, dt, tile, tr.s); });
       };
@@ -550,7 +551,8 @@ hipError_t launch_poly_stage(const Plan &plan, Tracer &tr, const std::vector<Gem
       work = 0.0;
     };
     auto go = [&]() -> hipError_t {
-      const GemmArgs a = args;
+      GemmArgs a = args;
+      a.xcd_group = kXcdGroup;
       const int dt = plan.set.ns_dtype;
       return tr.run(MUON_STAGE_GEMM, work, [&]() { return launch_poly_update(a, dt, sp, tr.s); });
     };

@@ -184,9 +184,17 @@ struct GemmClass {
 struct GemmArgs {
   int32_t nclass;
   int32_t total_tiles;
+  // Workgroup -> tile order over the 8 XCDs: 0 = each XCD walks one
+  // contiguous run of the launch's tiles; G > 0 = runs of G tiles dealt to
+  // the XCDs in turn (every class of the launch spread over all XCDs).
+  int32_t xcd_group;
   int32_t tile_begin[kGemmMaxClasses];   // first tile of each class; unused = INT32_MAX
   GemmClass cls[kGemmMaxClasses];
 };
+// Measured choice: runs of 16 for the 64 and 256 tiles and the fused update
+// (mixed-K launches stay balanced across XCDs), one run per XCD for the 128
+// tile (operand reuse in each XCD's L2).
+constexpr int kXcdGroup = 16;
 
 // ------------------------------------------------------------------ AdamW
 // Decoupled AdamW over a list of fp32 tensors (vector-shaped parameters).

@@ -123,14 +123,25 @@ struct TileRef {
 };
 
 // Locate (class, matrix, tile) of this workgroup; uniform across the block.
-// Workgroups are dealt round-robin to the 8 XCDs (each with its own L2):
-// remap so that each XCD walks a contiguous run of tiles, which share
-// operand panels.
+// Workgroups are dealt round-robin to the 8 XCDs (each with its own L2), in
+// blockIdx order.  xcd_group == 0: remap so that each XCD walks one
+// contiguous run of tiles, which share operand panels.  xcd_group = G > 0:
+// every 8 G workgroups take 8 G consecutive tiles, G contiguous ones per XCD,
+// so each class of the launch is spread over all XCDs (a launch mixing long-
+// and short-K classes stays balanced); a last partial round keeps the
+// identity order.  Both maps are bijections of [0, nb).
 __device__ __forceinline__ TileRef locate_tile(const GemmArgs &args) {
   const int nb = (int)gridDim.x;
   const int b = (int)blockIdx.x;
-  const int per_xcd = nb / 8, rem = nb % 8, xcd = b % 8, slot = b / 8;
-  const int tile = (xcd < rem ? xcd * (per_xcd + 1) : rem * (per_xcd + 1) + (xcd - rem) * per_xcd) + slot;
+  int tile;
+  if (args.xcd_group > 0) {
+    const int G = args.xcd_group, chunk = 8 * G;
+    const int q = b / chunk, u = b - q * chunk;
+    tile = (b < nb / chunk * chunk) ? q * chunk + (u & 7) * G + (u >> 3) : b;
+  } else {
+    const int per_xcd = nb / 8, rem = nb % 8, xcd = b % 8, slot = b / 8;
+    tile = (xcd < rem ? xcd * (per_xcd + 1) : rem * (per_xcd + 1) + (xcd - rem) * per_xcd) + slot;
+  }
   // tile_begin[] is ascending with INT32_MAX past the last class: the class
   // index is the count of later entries <= tile (independent scalar loads)
   int ci = 0;
