@@ -361,7 +361,7 @@ struct StageBuilder {
       double flops = 0.0;
       auto go = [&]() -> hipError_t {
         GemmArgs a = args;
-        a.xcd_group = tile == 128 ? 0 : kXcdGroup;
+        a.xcd_group = tile == 256 ? kXcdGroup : 0;
         const int dt = plan.set.ns_dtype;
         return tr.run(MUON_STAGE_GEMM, flops, [&]() { return launch_gemm(a, dt, tile, tr.s); });
       };
@@ -551,8 +551,7 @@ hipError_t launch_poly_stage(const Plan &plan, Tracer &tr, const std::vector<Gem
       work = 0.0;
     };
     auto go = [&]() -> hipError_t {
-      GemmArgs a = args;
-      a.xcd_group = kXcdGroup;
+      const GemmArgs a = args;   // xcd_group 0: one contiguous run per XCD
       const int dt = plan.set.ns_dtype;
       return tr.run(MUON_STAGE_GEMM, work, [&]() { return launch_poly_update(a, dt, sp, tr.s); });
     };

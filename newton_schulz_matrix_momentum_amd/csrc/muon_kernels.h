@@ -191,9 +191,10 @@ struct GemmArgs {
   int32_t tile_begin[kGemmMaxClasses];   // first tile of each class; unused = INT32_MAX
   GemmClass cls[kGemmMaxClasses];
 };
-// Measured choice: runs of 16 for the 64 and 256 tiles and the fused update
-// (mixed-K launches stay balanced across XCDs), one run per XCD for the 128
-// tile (operand reuse in each XCD's L2).
+// Measured choice: runs of 16 for the 256 tile (mixed-K launches stay
+// balanced across XCDs, and the large operands are shared through the
+// device-wide cache), one run per XCD for the 64 and 128 tiles and the fused
+// update (operand reuse in each XCD's L2).
 constexpr int kXcdGroup = 16;
 
 // ------------------------------------------------------------------ AdamW
