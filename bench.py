@@ -48,14 +48,15 @@ def parse():
 
 
 def kernel_source_hash():
-    """sha256 of the NS product kernels' code (ns_gemm.hip and the argument
-    blocks in muon_kernels.h, with comments and whitespace removed):
+    """sha256 of the NS product kernels' code and of the host code that
+    configures their launches (ns_gemm.hip, the argument blocks in
+    muon_kernels.h, muon_host.cpp; comments and whitespace removed):
     HBM-traffic figures in profiles/ apply only to the code they were
     measured on, and an edit of a comment does not change that code."""
     import hashlib
     import re
     h = hashlib.sha256()
-    for name in ("ns_gemm.hip", "muon_kernels.h"):
+    for name in ("ns_gemm.hip", "muon_kernels.h", "muon_host.cpp"):
         path = os.path.join(ROOT, "newton_schulz_matrix_momentum_amd", "csrc", name)
         with open(path) as f:
             src = f.read()
