@@ -335,6 +335,16 @@ struct Tracer {
   }
 };
 
+// Workgroup -> tile order of a launch (GemmArgs::xcd_group), measured with
+// the bench on each workload: 256-tile launches deal every class over all
+// XCDs (an eighth of each class per XCD when the launch holds several
+// classes, runs of 16 tiles when it holds one); the 64 and 128 tiles and the
+// fused update (tile 0 here) keep one contiguous run per XCD.
+void set_order(GemmArgs &a, int tile) {
+  a.xcd_group = tile != 256 ? 0 : (a.nclass > 1 ? kXcdByClass : kXcdGroup);
+  if (a.xcd_group == kXcdByClass) set_xcd_order(a);
+}
+
 // One NS product for every class: built per class, launched grouped by tile.
 // per_flops[c] is the algorithmic FLOP count of one matrix of class c (true,
 // unpadded sizes; a half product counts only its upper triangle).
@@ -361,7 +371,7 @@ struct StageBuilder {
       double flops = 0.0;
       auto go = [&]() -> hipError_t {
         GemmArgs a = args;
-        a.xcd_group = tile == 256 ? kXcdGroup : 0;
+        set_order(a, tile);
         const int dt = plan.set.ns_dtype;
         return tr.run(MUON_STAGE_GEMM, flops, [&]() { return launch_gemm(a, dt, tile, tr.s); });
       };
@@ -551,7 +561,8 @@ hipError_t launch_poly_stage(const Plan &plan, Tracer &tr, const std::vector<Gem
       work = 0.0;
     };
     auto go = [&]() -> hipError_t {
-      const GemmArgs a = args;   // xcd_group 0: one contiguous run per XCD
+      GemmArgs a = args;
+      set_order(a, 0);
       const int dt = plan.set.ns_dtype;
       return tr.run(MUON_STAGE_GEMM, work, [&]() { return launch_poly_update(a, dt, sp, tr.s); });
     };

@@ -186,11 +186,27 @@ struct GemmArgs {
   int32_t total_tiles;
   // Workgroup -> tile order over the 8 XCDs: 0 = each XCD walks one
   // contiguous run of the launch's tiles; G > 0 = runs of G tiles dealt to
-  // the XCDs in turn (every class of the launch spread over all XCDs).
+  // the XCDs in turn (every class of the launch spread over all XCDs);
+  // kXcdByClass = each XCD walks a contiguous eighth of every class
+  // (xcd_lo / xcd_start, filled by set_xcd_order).
   int32_t xcd_group;
   int32_t tile_begin[kGemmMaxClasses];   // first tile of each class; unused = INT32_MAX
+  int32_t xcd_lo[kGemmMaxClasses][9];    // class c's eighth x: tiles [xcd_lo[c][x], xcd_lo[c][x+1]) of the class
+  int32_t xcd_start[9];                  // sum over classes of xcd_lo[c][x]
   GemmClass cls[kGemmMaxClasses];
 };
+constexpr int kXcdByClass = -1;
+// Fill xcd_lo / xcd_start from nclass, tile_begin and total_tiles.
+inline void set_xcd_order(GemmArgs &a) {
+  for (int x = 0; x <= 8; ++x) a.xcd_start[x] = 0;
+  for (int c = 0; c < kGemmMaxClasses; ++c) {
+    const int64_t t = c < a.nclass ? (int64_t)((c + 1 < a.nclass ? a.tile_begin[c + 1] : a.total_tiles) - a.tile_begin[c]) : 0;
+    for (int x = 0; x <= 8; ++x) {
+      a.xcd_lo[c][x] = (int32_t)(t * x / 8);
+      a.xcd_start[x] += a.xcd_lo[c][x];
+    }
+  }
+}
 // Measured choice: runs of 16 for the 256 tile (mixed-K launches stay
 // balanced across XCDs, and the large operands are shared through the
 // device-wide cache), one run per XCD for the 64 and 128 tiles and the fused

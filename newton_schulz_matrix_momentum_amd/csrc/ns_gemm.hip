@@ -141,6 +141,27 @@ __device__ __forceinline__ TileRef locate_tile(const GemmArgs &args) {
   } else {
     const int per_xcd = nb / 8, rem = nb % 8, xcd = b % 8, slot = b / 8;
     tile = (xcd < rem ? xcd * (per_xcd + 1) : rem * (per_xcd + 1) + (xcd - rem) * per_xcd) + slot;
+    if (args.xcd_group == kXcdByClass) {
+      // position `tile` of an order that lists eighth 0 of every class, then
+      // eighth 1 of every class, ...: each XCD's contiguous run covers about
+      // one eighth of each class
+      const int v = tile;
+      int x = 0;
+#pragma unroll
+      for (int i = 1; i < 8; ++i) x += (args.xcd_start[i] <= v) ? 1 : 0;
+      int r = v - args.xcd_start[x];
+      tile = 0;
+      bool found = false;
+#pragma unroll
+      for (int c = 0; c < kGemmMaxClasses; ++c) {
+        const int lo = args.xcd_lo[c][x], n = args.xcd_lo[c][x + 1] - lo;
+        if (!found && r < n) {
+          tile = args.tile_begin[c] + lo + r;
+          found = true;
+        }
+        if (!found) r -= n;
+      }
+    }
   }
   // tile_begin[] is ascending with INT32_MAX past the last class: the class
   // index is the count of later entries <= tile (independent scalar loads)
