@@ -109,6 +109,16 @@ def test_fused_square_update_groups(ns_dtype):
     run_case(shapes, grad_dtype="bf16", ns_dtype=ns_dtype, grad_kind="spectral", seed=12)
 
 
+@pytest.mark.parametrize("ns_dtype,variant", [("bf16", "direct"), ("f16", "gram")])
+def test_256_tile_classes_mixed_k(ns_dtype, variant):
+    """Three classes on the 256 tile whose Gram products run over different
+    K (700, 900, 1300) in one launch: the launch deals each XCD a contiguous
+    eighth of every class; both orientations."""
+    shapes = [(512, 700), (700, 512), (768, 900), (1300, 512)]
+    run_case(shapes, grad_dtype="bf16", ns_dtype=ns_dtype, variant=variant, grad_kind="spectral", seed=17,
+             divisor=1.03 if variant == "gram" else 1.0, restart_every=3 if variant == "gram" else 0)
+
+
 @pytest.mark.parametrize("ns_dtype", ["f32", "bf16"])
 def test_long_thin_matrices(ns_dtype):
     """Extreme aspect ratios: long sides of 9000 to 70001 with short sides 1
