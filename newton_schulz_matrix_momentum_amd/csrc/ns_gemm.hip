@@ -122,6 +122,10 @@ struct TileRef {
   int ci, mat, tm, tn;
 };
 
+// Tile rows per super-row in the order of a full (non-symmetric) product's
+// tiles (4: measured against 1 and 8).
+constexpr int kRowGroup = 4;
+
 // Locate (class, matrix, tile) of this workgroup; uniform across the block.
 // Workgroups are dealt round-robin to the 8 XCDs (each with its own L2), in
 // blockIdx order.  xcd_group == 0: remap so that each XCD walks one
@@ -181,8 +185,13 @@ __device__ __forceinline__ TileRef locate_tile(const GemmArgs &args) {
     r.tm = tm;
     r.tn = tm + t;
   } else {
-    r.tm = t / cl.tiles_n;
-    r.tn = t - r.tm * cl.tiles_n;
+    // super-rows of kRowGroup tile rows, walked column by column: the tiles
+    // a workgroup's neighbours take share both A and B panels in L2
+    const int per_group = kRowGroup * cl.tiles_n;
+    const int g = t / per_group, u = t - g * per_group;
+    const int rows = min(kRowGroup, cl.tiles_m - g * kRowGroup);
+    r.tm = g * kRowGroup + u % rows;
+    r.tn = u / rows;
   }
   return r;
 }
