@@ -119,6 +119,15 @@ def test_256_tile_classes_mixed_k(ns_dtype, variant):
              divisor=1.03 if variant == "gram" else 1.0, restart_every=3 if variant == "gram" else 0)
 
 
+def test_256_tile_many_small_classes():
+    """Nine one-matrix classes on the 256 tile (short side 512, long sides
+    512 .. 900): 3 to 8 tiles per class and product, so most XCDs get an
+    empty eighth of a class, and the ninth class opens a second launch."""
+    longs = [512, 530, 560, 600, 640, 700, 760, 800, 900]
+    shapes = [(512, l) if i % 2 == 0 else (l, 512) for i, l in enumerate(longs)]
+    run_case(shapes, grad_dtype="bf16", ns_dtype="bf16", grad_kind="spectral", seed=18)
+
+
 @pytest.mark.parametrize("ns_dtype", ["f32", "bf16"])
 def test_long_thin_matrices(ns_dtype):
     """Extreme aspect ratios: long sides of 9000 to 70001 with short sides 1
