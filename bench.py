@@ -24,6 +24,7 @@ if ROOT not in sys.path:
 METRIC = "Muon step ms per model + NS TFLOP/s (% MFMA peak), elementwise GB/s"
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}   # MI355X dense MFMA
 PEAK_HBM_GBPS = 8000.0
+SCLK_NOMINAL_MHZ = 2400.0   # shader clock of the MFMA peak figures
 
 
 def parse():
@@ -201,6 +202,53 @@ def coeff_table(w):
     return [list(base)] * w.ns_steps
 
 
+def sample_sclk(run, step_ms, seconds=1.0):
+    """Shader clock (MHz) while `run` (one step of about `step_ms`) is
+    replayed back to back for about `seconds` (about 50 ms of steps queued
+    between synchronisations, so the device never idles): the median over
+    samples of the mean of the per-XCD GFX clocks that `amd-smi metric
+    --clock --json` reports.  None where amd-smi is missing or reports
+    nothing."""
+    import shutil
+    import statistics
+    import subprocess
+    import threading
+    import torch
+    exe = shutil.which("amd-smi")
+    if exe is None:
+        return None
+    samples = []
+    stop = threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            try:
+                out = subprocess.run([exe, "metric", "--clock", "--json"], capture_output=True, text=True,
+                                     timeout=10).stdout
+                gpu = json.loads(out)["gpu_data"][0]["clock"]
+                clks = [v["clk"]["value"] for k, v in gpu.items() if k.startswith("gfx_")]
+                clks = [float(c) for c in clks if isinstance(c, (int, float))]
+                if clks:
+                    samples.append(sum(clks) / len(clks))
+            except Exception:
+                return
+            time.sleep(0.05)
+
+    batch = max(1, min(1024, int(50.0 / max(step_ms, 1e-3))))
+    for _ in range(batch):   # the queue is busy before the first sample
+        run()
+    th = threading.Thread(target=poll, daemon=True)
+    t_end = time.perf_counter() + seconds
+    th.start()
+    while time.perf_counter() < t_end:
+        for _ in range(batch):
+            run()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=15)
+    return statistics.median(samples) if samples else None
+
+
 def gpu_timing(args, w, variant):
     import torch
     import newton_schulz_matrix_momentum_amd as nsm
@@ -258,6 +306,8 @@ def gpu_timing(args, w, variant):
     torch.cuda.synchronize()
     dist = sorted(a.elapsed_time(b) for a, b in evs)
     spread = [dist[int(q * (n_dist - 1) + 0.5)] for q in (0.1, 0.5, 0.9)]
+    # shader clock under the same load (outside the timed region)
+    sclk = sample_sclk(run, ms_per_step)
 
     # MONA workloads: the first step (D = 0: no previous gradient is read)
     # timed on its own graph
@@ -316,7 +366,7 @@ def gpu_timing(args, w, variant):
         d["ms"] /= tsteps
         d["work"] /= tsteps
         d["launches"] /= tsteps
-    return params, ms_per_step, wall, per_stage, launches_per_step, graph is not None, spread, first_ms
+    return params, ms_per_step, wall, per_stage, launches_per_step, graph is not None, spread, first_ms, sclk
 
 
 def cpu_baseline(args, w, variant, params, single_thread=False, seconds=None):
@@ -387,7 +437,7 @@ def main():
     variant = args.variant or w.variants[0]
     print("bench: workload %s variant %s, %d matrices, %d warmup + %d timed steps" %
           (w.name, variant, len(w.shapes), args.warmup, args.steps), file=sys.stderr, flush=True)
-    params, ms, wall, per_stage, launches, graphed, spread, first_ms = gpu_timing(args, w, variant)
+    params, ms, wall, per_stage, launches, graphed, spread, first_ms, sclk = gpu_timing(args, w, variant)
     print("bench: gpu timing done (%.4f ms/step)" % ms, file=sys.stderr, flush=True)
 
     gemm = per_stage.get("gemm", {"ms": 0.0, "work": 0.0, "launches": 0})
@@ -414,6 +464,11 @@ def main():
                 "peak": PEAK_HBM_GBPS, "unit": "GB/s", "avg_launch_us": per_launch_ms * 1e3,
                 "work_per_launch": per_launch_work, "traffic": None}
     roof["frac"] = roof["achieved"] / roof["peak"]
+    if roof["bound"] == "mfma":
+        # the MFMA peak scales with the shader clock: also quote the fraction
+        # of the peak at the clock measured under this load (2.4 GHz nominal)
+        roof["sclk_mhz"] = sclk
+        roof["frac_at_sclk"] = roof["frac"] * SCLK_NOMINAL_MHZ / sclk if sclk else None
 
     cpu = cpu1 = None
     if not args.no_cpu_baseline:
