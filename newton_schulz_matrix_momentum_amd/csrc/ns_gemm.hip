@@ -133,7 +133,9 @@ constexpr int kRowGroup = 4;
 // every 8 G workgroups take 8 G consecutive tiles, G contiguous ones per XCD,
 // so each class of the launch is spread over all XCDs (a launch mixing long-
 // and short-K classes stays balanced); a last partial round keeps the
-// identity order.  Both maps are bijections of [0, nb).
+// identity order.  xcd_group == kXcdByClass: the contiguous runs walk an
+// order that lists one eighth of every class per XCD (balanced and still
+// contiguous within each class).  All three maps are bijections of [0, nb).
 __device__ __forceinline__ TileRef locate_tile(const GemmArgs &args) {
   const int nb = (int)gridDim.x;
   const int b = (int)blockIdx.x;
