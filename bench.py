@@ -32,7 +32,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="nanochat_6l_d192")
+    ap.add_argument("--workload", default="gram_tall_32x4096x16384")
     ap.add_argument("--variant", default=None, help="direct | gram (default: the workload's first)")
     ap.add_argument("--no-graph", action="store_true", help="launch kernels directly instead of a HIP graph")
     ap.add_argument("--mona-lite", action="store_true",
@@ -202,37 +202,63 @@ def coeff_table(w):
     return [list(base)] * w.ns_steps
 
 
+def _sysfs_device_dir(dev_index=0):
+    """The sysfs directory of the PCI device behind torch's device
+    ``dev_index`` (matched by PCI domain/bus/device), or None."""
+    import torch
+    props = torch.cuda.get_device_properties(dev_index)
+    bus = getattr(props, "pci_bus_id", None)
+    if bus is None:
+        return None
+    dom = getattr(props, "pci_domain_id", 0) or 0
+    devn = getattr(props, "pci_device_id", 0) or 0
+    path = "/sys/bus/pci/devices/%04x:%02x:%02x.0" % (dom, bus, devn)
+    return path if os.path.isdir(path) else None
+
+
+def _read_sclk_mhz(path):
+    """Current shader clock from the kernel driver's pp_dpm_sclk table (the
+    level marked with '*'), read in this process (no child program)."""
+    with open(path) as f:
+        for line in f:
+            if "*" in line:
+                digits = "".join(ch for ch in line.split(":", 1)[-1] if ch.isdigit() or ch == ".")
+                return float(digits) if digits else None
+    return None
+
+
 def sample_sclk(run, step_ms, seconds=1.0):
     """Shader clock (MHz) while `run` (one step of about `step_ms`) is
     replayed back to back for about `seconds` (about 50 ms of steps queued
-    between synchronisations, so the device never idles): the median over
-    samples of the mean of the per-XCD GFX clocks that `amd-smi metric
-    --clock --json` reports.  None where amd-smi is missing or reports
-    nothing."""
-    import shutil
+    between synchronisations, so the device never idles): the median of the
+    driver's current-level readings from sysfs (pp_dpm_sclk), polled by a
+    thread of this process.  Returns (MHz or None, reason when None)."""
     import statistics
-    import subprocess
     import threading
     import torch
-    exe = shutil.which("amd-smi")
-    if exe is None:
-        return None
+    try:
+        d = _sysfs_device_dir(torch.cuda.current_device())
+    except Exception as e:  # pragma: no cover - depends on the box
+        return None, "no PCI address for the device (%s)" % e
+    path = os.path.join(d, "pp_dpm_sclk") if d else None
+    if path is None or not os.path.exists(path):
+        return None, "pp_dpm_sclk not found in sysfs for this device"
+    try:
+        _read_sclk_mhz(path)
+    except OSError as e:
+        return None, "pp_dpm_sclk not readable (%s)" % e
     samples = []
     stop = threading.Event()
 
     def poll():
         while not stop.is_set():
             try:
-                out = subprocess.run([exe, "metric", "--clock", "--json"], capture_output=True, text=True,
-                                     timeout=10).stdout
-                gpu = json.loads(out)["gpu_data"][0]["clock"]
-                clks = [v["clk"]["value"] for k, v in gpu.items() if k.startswith("gfx_")]
-                clks = [float(c) for c in clks if isinstance(c, (int, float))]
-                if clks:
-                    samples.append(sum(clks) / len(clks))
-            except Exception:
+                v = _read_sclk_mhz(path)
+                if v:
+                    samples.append(v)
+            except OSError:
                 return
-            time.sleep(0.05)
+            time.sleep(0.01)
 
     batch = max(1, min(1024, int(50.0 / max(step_ms, 1e-3))))
     for _ in range(batch):   # the queue is busy before the first sample
@@ -246,7 +272,9 @@ def sample_sclk(run, step_ms, seconds=1.0):
         torch.cuda.synchronize()
     stop.set()
     th.join(timeout=15)
-    return statistics.median(samples) if samples else None
+    if not samples:
+        return None, "pp_dpm_sclk marked no current level"
+    return statistics.median(samples), None
 
 
 def gpu_timing(args, w, variant):
@@ -371,49 +399,49 @@ def gpu_timing(args, w, variant):
 
 def cpu_baseline(args, w, variant, params, single_thread=False, seconds=None):
     """The oracle as it stands, on this host's cores (or one BLAS thread), on
-    a bounded sample: one matrix of each shape class, each repeated until its
-    share of the time budget is spent; the per-step time is extrapolated by
-    matrix counts."""
-    if single_thread:
-        from threadpoolctl import threadpool_limits
-        with threadpool_limits(limits=1, user_api="blas"):
-            r = cpu_baseline(args, w, variant, params, seconds=seconds)
-        r["cores"] = 1
-        return r
+    a bounded sample: one matrix of each shape class (for the tall-matrix
+    Gram set: one per orientation), each repeated until its share of the time
+    budget is spent; the per-step time is extrapolated by matrix counts.
+    The host BLAS runs one thread per core of this process's affinity mask
+    (``cores``)."""
     import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([t.get("num_threads", 1) for t in threadpool_info() if t.get("user_api") == "blas"] or [1])
-    except Exception:  # pragma: no cover
-        cores = 1
-    divisor, restart = w.settings_for(variant)
-    coeffs = oracle.coefficient_table(w.coeffs, w.ns_steps)
-    classes = {}
-    for i, (r, c) in enumerate(w.shapes):
-        classes.setdefault((r, c), []).append(i)
-    budget = (args.cpu_seconds if seconds is None else seconds) / max(len(classes), 1)
-    total_ms = 0.0
-    sample = []
-    for (r, c), idx in classes.items():
-        p = params[idx[0]]
-        snap = {k: v.detach().cpu().double().numpy() for k, v in p.items() if hasattr(v, "detach")}
-        reps, spent = 0, 0.0
-        while spent < budget or reps == 0:
-            t0 = time.perf_counter()
-            oracle.muon_step_matrix(snap["weight"], snap["grad"], snap["momentum"], lr=w.lr, mu=w.mu,
-                                    weight_decay=w.weight_decay, coeffs=coeffs, variant=variant, divisor=divisor,
-                                    restart_every=restart, accel=snap.get("accel"), prev_grad=snap.get("prev_grad"),
-                                    lite_state=snap.get("mona_lite"), beta_a=w.beta_a, alpha=w.alpha,
-                                    step=1 if w.mona else 0)
-            spent += time.perf_counter() - t0
-            reps += 1
-        per = spent / reps
-        total_ms += 1e3 * per * len(idx)
-        sample.append("%dx%d x%d reps (of %d)" % (r, c, reps, len(idx)))
-    return {"value": total_ms, "unit": "ms", "cores": int(cores), "kind": "oracle",
-            "sample": "fp64 numpy oracle, one matrix per shape class: " + "; ".join(sample) +
-                      "; per-step time extrapolated by matrix count"}
+    affinity = len(os.sched_getaffinity(0))
+    threads = 1 if single_thread else affinity
+    with threadpool_limits(limits=threads, user_api="blas"):
+        blas = max([t.get("num_threads", 1) for t in threadpool_info() if t.get("user_api") == "blas"] or [1])
+        divisor, restart = w.settings_for(variant)
+        coeffs = oracle.coefficient_table(w.coeffs, w.ns_steps)
+        classes = {}
+        for i, (r, c) in enumerate(w.shapes):
+            classes.setdefault((r, c), []).append(i)
+        budget = (args.cpu_seconds if seconds is None else seconds) / max(len(classes), 1)
+        total_ms = 0.0
+        sample = []
+        extrapolated = False
+        for (r, c), idx in classes.items():
+            p = params[idx[0]]
+            snap = {k: v.detach().cpu().double().numpy() for k, v in p.items() if hasattr(v, "detach")}
+            reps, spent = 0, 0.0
+            while spent < budget or reps == 0:
+                t0 = time.perf_counter()
+                oracle.muon_step_matrix(snap["weight"], snap["grad"], snap["momentum"], lr=w.lr, mu=w.mu,
+                                        weight_decay=w.weight_decay, coeffs=coeffs, variant=variant,
+                                        divisor=divisor, restart_every=restart, accel=snap.get("accel"),
+                                        prev_grad=snap.get("prev_grad"), lite_state=snap.get("mona_lite"),
+                                        beta_a=w.beta_a, alpha=w.alpha, step=1 if w.mona else 0)
+                spent += time.perf_counter() - t0
+                reps += 1
+            per = spent / reps
+            total_ms += 1e3 * per * len(idx)
+            extrapolated = extrapolated or len(idx) > 1
+            sample.append("%dx%d: 1 matrix x %d reps, %.2f s each, x%d matrices" % (r, c, reps, per, len(idx)))
+            del snap
+    return {"value": total_ms, "unit": "ms", "cores": int(threads), "kind": "oracle",
+            "affinity_cores": affinity, "blas_threads": int(blas), "extrapolated": extrapolated,
+            "sample": "fp64 numpy oracle (full products, no symmetric halving) on one matrix per shape class: " +
+                      "; ".join(sample) + ("; per-step time extrapolated by matrix count" if extrapolated else "")}
 
 
 def main():
@@ -452,7 +480,8 @@ def main():
     if dom == "gemm":
         per_launch_work = gemm["work"] / gemm["launches"]
         per_launch_ms = gemm["ms"] / gemm["launches"]
-        roof = {"kernel": "ns_gemm (all Newton-Schulz product launches, %s)" % w.ns_dtype, "bound": "mfma",
+        roof = {"kernel": "Newton-Schulz products (%s; all %g product launches of a step, averaged)"
+                          % (w.ns_dtype, gemm["launches"]), "bound": "mfma",
                 "achieved": per_launch_work / (per_launch_ms * 1e-3) / 1e12, "peak": peak, "unit": "TFLOP/s",
                 "avg_launch_us": per_launch_ms * 1e3, "work_per_launch": per_launch_work,
                 "traffic": recorded_traffic(w.name)}
@@ -467,8 +496,11 @@ def main():
     if roof["bound"] == "mfma":
         # the MFMA peak scales with the shader clock: also quote the fraction
         # of the peak at the clock measured under this load (2.4 GHz nominal)
-        roof["sclk_mhz"] = sclk
-        roof["frac_at_sclk"] = roof["frac"] * SCLK_NOMINAL_MHZ / sclk if sclk else None
+        mhz, why = sclk
+        roof["sclk_mhz"] = mhz
+        roof["frac_at_sclk"] = roof["frac"] * SCLK_NOMINAL_MHZ / mhz if mhz else None
+        if mhz is None:
+            roof["sclk_unavailable"] = why
 
     cpu = cpu1 = None
     if not args.no_cpu_baseline:

@@ -11,8 +11,9 @@ import ctypes
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-# LIBMUON_PATH selects another build of the library (e.g. a tuning variant)
-LIB_PATH = os.environ.get("LIBMUON_PATH") or os.path.join(_PKG, "libmuon.so")
+# the in-tree build; another build (a tuning variant) is loaded only by an
+# explicit load(path) call, never through the environment
+LIB_PATH = os.path.join(_PKG, "libmuon.so")
 
 MUON_OK = 0
 MUON_ERR_INVALID_ARG = 1

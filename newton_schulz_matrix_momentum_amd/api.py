@@ -137,6 +137,11 @@ class Workspace:
         return self.buf
 
 
+# Default workspaces, one per (device, stream): a workspace is written by the
+# kernels of the stream it is used on, so two streams never share one, and the
+# caching allocator (which hands a freed block only to allocations on the
+# stream it was allocated on) cannot give a grown-out buffer to another
+# stream while kernels of its own stream still use it.
 _default_ws: Dict = {}
 
 
@@ -162,13 +167,19 @@ def muon_step(params: Sequence[Dict], *, lr: float, mu: float, beta_a: float = 0
     need = lib.muon_workspace_size(arr, n, int(ns_steps), _VARIANTS[variant], ctypes.byref(opts))
     if need == 0:
         raise _lib.MuonError(_lib.MUON_ERR_INVALID_ARG, _lib.last_error())
+    cur = torch.cuda.current_stream(device)
     if workspace is None:
-        ws = _default_ws.setdefault(device, Workspace()).get(need, device)
+        ws = _default_ws.setdefault((device, cur.cuda_stream), Workspace()).get(need, device)
     else:
         if workspace.device != device or workspace.dtype != torch.uint8:
             raise ValueError("workspace must be a uint8 tensor on %s" % device)
         ws = workspace
-    stream = torch.cuda.current_stream(device).cuda_stream
+        # a caller's workspace allocated on another stream stays reserved
+        # until this stream's kernels are done with it (outside captures: a
+        # captured graph's memory lives as long as the graph)
+        if not Workspace._capturing(device):
+            ws.record_stream(cur)
+    stream = cur.cuda_stream
     _lib.check(lib.muon_step(arr, n, float(lr), float(mu), float(beta_a), float(alpha), float(weight_decay),
                              int(ns_steps), _VARIANTS[variant], ctypes.byref(opts), ctypes.c_void_p(ws.data_ptr()),
                              ws.numel(), ctypes.c_void_p(stream)))

@@ -1,7 +1,9 @@
 """Full-size parity: every synthetic workload at its real size, stepped exactly
 as bench.py steps it (all matrices in one call), checked against the fp64
-oracle on one sampled matrix per shape class (every stage: momentum,
-acceleration, previous gradient, O and dW), plus finiteness of every matrix.
+oracle on the first and the last matrix of every shape class (the last one
+sits at the class's highest workspace offset) -- every stage: momentum,
+acceleration, previous gradient, O and dW, the last two per matrix and per
+64 x 64 block -- plus finiteness of every matrix.
 
 The oracle computes full products in fp64 on the host, so only sampled
 matrices are re-derived; the elementwise state of every other matrix is
@@ -12,7 +14,7 @@ import pytest
 import torch
 
 import oracle
-from helpers import rel_fro, to64, tol_for, TOL_STATE
+from helpers import check_close, rel_fro, to64, tol_for, TOL_STATE
 from workloads import WORKLOADS, make_grads, make_state
 
 pytestmark = pytest.mark.gpu
@@ -28,13 +30,12 @@ def _setup(w, device, lite=False):
 
 
 def _sample_indices(w):
-    """First matrix of every shape class."""
-    seen, idx = set(), []
+    """First and last matrix of every shape class."""
+    first, last = {}, {}
     for i, s in enumerate(w.shapes):
-        if s not in seen:
-            seen.add(s)
-            idx.append(i)
-    return idx
+        first.setdefault(s, i)
+        last[s] = i
+    return sorted(set(first.values()) | set(last.values()))
 
 
 def _run_workload(name, variant, lite=False):
@@ -102,11 +103,12 @@ def _run_workload(name, variant, lite=False):
             assert rel_fro(to64(p["momentum"]), ref["momentum"]) <= TOL_STATE
             if "accel" in p:
                 assert rel_fro(to64(p["accel"]), ref["accel"]) <= TOL_STATE
-            o_err = rel_fro(to64(p["ortho_out"]), ref["ortho"])
-            dw_err = rel_fro(to64(p["weight"]) - w_gpu_before[i], ref["weight"] - s["weight"])
-            print("  step %d matrix %d %s: O err %.3g, dW err %.3g (tol %.0e)"
-                  % (step, i, w.shapes[i], o_err, dw_err, tol), flush=True)
-            assert o_err <= tol and dw_err <= tol
+            what = "step %d matrix %d %s" % (step, i, w.shapes[i])
+            print("  %s: O err %.3g, dW err %.3g (tol %.0e)"
+                  % (what, rel_fro(to64(p["ortho_out"]), ref["ortho"]),
+                     rel_fro(to64(p["weight"]) - w_gpu_before[i], ref["weight"] - s["weight"]), tol), flush=True)
+            check_close(to64(p["ortho_out"]), ref["ortho"], tol, what + ": O")
+            check_close(to64(p["weight"]) - w_gpu_before[i], ref["weight"] - s["weight"], tol, what + ": dW")
             # carry the oracle's own state forward (never the GPU's)
             s["weight"], s["momentum"] = ref["weight"], ref["momentum"]
             if "prev_grad" in ref:

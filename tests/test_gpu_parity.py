@@ -1,12 +1,13 @@
-"""HIP path vs the fp64 oracle, element by element, on seeded inputs.
+"""HIP path vs the fp64 oracle on seeded inputs.
 
 Sizes span several tiles and ragged tails (64-wide tiles for short sides up to
 256, 128-wide above), both orientations, every dtype combination, both
 Newton-Schulz variants, MONA on and off, and two consecutive steps.
-Tolerances (relative Frobenius per matrix, on O and on dW = W_new - W_old):
+Tolerances on O and on dW = W_new - W_old: relative Frobenius per matrix
 1e-5 with fp32 Newton-Schulz operands, 2e-2 with fp16 / bf16 operands and fp32
-accumulation; momentum and acceleration 1e-6; the stored previous gradient is
-bitwise the gradient.
+accumulation, and every 64 x 64 block's rms error within 3x that in units of
+the matrix's rms value (helpers.check_close); momentum and acceleration 1e-6;
+the stored previous gradient is bitwise the gradient.
 """
 import numpy as np
 import pytest
@@ -14,7 +15,7 @@ import torch
 
 import oracle
 from helpers import (advance_oracle_state, compare, draw_grads, make_params, oracle_state, oracle_step, snapshot,
-                     to64, rel_fro, TOL_STATE, TOL_STATE_LITE)
+                     to64, rel_fro, check_close, TOL_STATE, TOL_STATE_LITE)
 
 pytestmark = pytest.mark.gpu
 
@@ -326,7 +327,7 @@ def test_symmetric_input_gram_f32():
     nsm.muon_step(params, lr=0.02, mu=0.95, weight_decay=0.0, ns_dtype="f32", variant="gram")
     torch.cuda.synchronize()
     ref = oracle.newton_schulz_gram(oracle.frobenius_normalize(to64(g)), oracle.coefficient_table("quintic", 5))
-    assert rel_fro(to64(params[0]["ortho_out"]), ref) < 1e-5
+    check_close(to64(params[0]["ortho_out"]), ref, 1e-5, "symmetric fp32 Gram: O")
 
 
 # ---------------------------------------------------------------- launch timing
@@ -498,7 +499,7 @@ def test_optimizer_routes_vectors_to_adamw():
     torch.cuda.synchronize()
     r = oracle.muon_step_matrix(to64(w0), to64(w.grad), np.zeros((96, 160)), lr=f32(0.02), mu=f32(0.95),
                                 weight_decay=f32(0.01), coeffs=oracle.coefficient_table("quintic", 5))
-    assert rel_fro(to64(w) - to64(w0), r["weight"] - to64(w0)) < 2e-2
+    check_close(to64(w) - to64(w0), r["weight"] - to64(w0), 2e-2, "optimizer wrapper: dW")
     pb, _, _ = oracle.adamw_step(to64(b0), to64(b.grad), np.zeros(96), np.zeros(96), step=0, lr=f32(1e-3),
                                  beta1=f32(0.9), beta2=f32(0.95), eps=f32(1e-8), weight_decay=f32(0.05))
     np.testing.assert_allclose(to64(b), pb, rtol=1e-6, atol=1e-7)
