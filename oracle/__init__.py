@@ -18,6 +18,7 @@ from .muon_oracle import (  # noqa: F401
     newton_schulz_direct,
     newton_schulz_gram,
     newton_schulz,
+    limuon_orthogonalize,
     decoupled_update,
     muon_step_matrix,
     muon_step,

@@ -29,6 +29,14 @@ Sources (the pages this follows):
   Matrices", 2008, section 8.3): the cubic map X <- (3X - X X^T X)/2, which
   needs sigma_max(X) < sqrt(3); Frobenius normalisation guarantees
   sigma_max <= 1.
+* "LiMuon: Light and Fast Muon Optimizer for Large Models" (digest,
+  arxiv.sitesynth.xyz 2509.14562v1), section "Метод": momentum as in Muon,
+  with the orthogonalisation done through a randomized SVD of the momentum.
+  The randomized SVD is the textbook one (N. Halko, P.-G. Martinsson,
+  J. A. Tropp, "Finding structure with randomness", SIAM Review 53(2),
+  2011): Algorithm 4.4 (randomized subspace iteration: a Gaussian test
+  matrix, power iterations with re-orthonormalisation) followed by
+  Algorithm 5.1 (direct SVD of the small projected matrix).
 
 Readings of points the pages leave open (each is listed with its reason in the
 design notes):
@@ -51,6 +59,13 @@ design notes):
   arithmetic and G_{k-1} is never stored; C is rounded to bfloat16 (nearest,
   ties to even) each time it is stored.
 * gamma (the scale on O in the update) is a per-matrix number, default 1.
+* LiMuon (the digest names the method only): O = U_k V_k^T built from the
+  rank-k randomized SVD of the momentum, sketching the long side (the wide
+  orientation X, s x l, s <= l: Y = X Omega with a Gaussian test matrix
+  Omega of l x (k + p), drawn by the caller and passed in), q power
+  iterations, and directions whose sketched singular value is at most
+  rcond * sigma_1 dropped (a null direction maps to zero, as p(0) = 0 does
+  for Newton-Schulz).  Rank k, oversampling p, q and rcond are arguments.
 
 Everything is computed in float64 from inputs upcast exactly from their stored
 dtype.  There is no blocking, fusion or reordering beyond what the steps
@@ -232,6 +247,44 @@ def newton_schulz(x0, coeffs, variant: str = "direct", divisor: float = 1.0, res
     raise ValueError("unknown variant %r" % (variant,))
 
 
+def limuon_orthogonalize(m, omega, rank: int, power_iters: int = 1, rcond: float = 1e-4):
+    """LiMuon's orthogonaliser (LiMuon digest, "Метод": a randomized SVD of
+    the momentum in place of Newton-Schulz), as the textbook randomized SVD
+    (Halko, Martinsson & Tropp 2011, Algorithms 4.4 and 5.1):
+
+      X = M in its wide orientation (s x l, s <= l; a tall M is transposed
+          in and the result transposed back), Omega: l x (k + p) Gaussian
+      Y = X Omega,  Q = qr(Y)                       range finder
+      q times:  Q~ = qr(X^T Q),  Q = qr(X Q~)       power iterations
+      B = Q^T X = U~ S V^T                          SVD of the small matrix
+      O = sum over i < k with S_i > rcond S_1 of (Q U~)_i V_i^T
+
+    O is scale-invariant in M (the rcond cutoff is relative) and depends on
+    Omega only through the range of X Omega.  M = 0 gives O = 0.
+    """
+    m = np.asarray(m, dtype=np.float64)
+    om = np.asarray(omega, dtype=np.float64)
+    tall = m.shape[0] > m.shape[1]
+    x = m.T if tall else m
+    s, l = x.shape
+    if om.shape[0] != l:
+        raise ValueError("omega has %d rows, the long side is %d" % (om.shape[0], l))
+    if rank < 1 or rank > om.shape[1]:
+        raise ValueError("rank must lie in [1, columns of omega]")
+    q, _ = np.linalg.qr(x @ om)
+    for _ in range(power_iters):
+        qt, _ = np.linalg.qr(x.T @ q)
+        q, _ = np.linalg.qr(x @ qt)
+    b = q.T @ x
+    ub, sv, vt = np.linalg.svd(b, full_matrices=False)
+    out = np.zeros_like(x)
+    if sv.size and sv[0] > 0.0:
+        keep = [i for i in range(min(rank, sv.size)) if sv[i] > rcond * sv[0]]
+        if keep:
+            out = (q @ ub[:, keep]) @ vt[keep, :]
+    return out.T if tall else out
+
+
 def decoupled_update(weight, ortho, lr: float, weight_decay: float, gamma: float = 1.0):
     """W_{k+1} = W_k - eta (gamma O_k + lambda W_k) (MONA summary, step 4)."""
     w = np.asarray(weight, dtype=np.float64)
@@ -240,11 +293,14 @@ def decoupled_update(weight, ortho, lr: float, weight_decay: float, gamma: float
 
 def muon_step_matrix(weight, grad, momentum, *, lr, mu, weight_decay, coeffs,
                      variant="direct", divisor=1.0, restart_every=0, gamma=1.0,
-                     accel=None, prev_grad=None, beta_a=0.0, alpha=0.0, step=0, lite_state=None):
+                     accel=None, prev_grad=None, beta_a=0.0, alpha=0.0, step=0, lite_state=None,
+                     omega=None, rank=None, power_iters=1, rcond=1e-4):
     """One optimizer step for one weight matrix, in the pages' order.
 
     MONA (if ``accel`` is given) or MONA-Lite (if ``lite_state`` is given) ->
-    momentum -> normalise -> Newton-Schulz -> decoupled update.  The
+    momentum -> normalise -> Newton-Schulz (``variant`` "direct" or "gram")
+    or LiMuon's randomized SVD (``variant`` "limuon": ``omega``, ``rank``,
+    ``power_iters``, ``rcond``; ``coeffs`` unused) -> decoupled update.  The
     acceleration enters before orthogonalisation (MONA summary,
     "Ontwerprichtlijnen").  Returns a dict with every stage's output, all
     float64.
@@ -262,7 +318,10 @@ def muon_step_matrix(weight, grad, momentum, *, lr, mu, weight_decay, coeffs,
         g_tilde = np.asarray(grad, dtype=np.float64)
     m_new = momentum_update(momentum, g_tilde, mu)
     x0 = frobenius_normalize(m_new, divisor)
-    o = newton_schulz(x0, coeffs, variant, divisor, restart_every)
+    if variant == "limuon":
+        o = limuon_orthogonalize(m_new, omega, rank, power_iters, rcond)
+    else:
+        o = newton_schulz(x0, coeffs, variant, divisor, restart_every)
     out["momentum"] = m_new
     out["x0"] = x0
     out["ortho"] = o
