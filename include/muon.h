@@ -167,6 +167,29 @@ muon_status muon_step(const muon_param *params, int n,
                       int ns_steps, muon_variant variant, const muon_options *opts,
                       void *workspace, size_t workspace_bytes, void *stream);
 
+/* Bytes of the static workspace muon_step_static uses on each GPU (64 MiB). */
+#define MUON_STATIC_WORKSPACE_BYTES (64u << 20)
+
+/* muon_step without a caller-owned workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same arguments, computation and
+ * results as muon_step, with the workspace taken from a static device array
+ * of MUON_STATIC_WORKSPACE_BYTES that the library holds on every GPU it runs
+ * on until the process ends.  The array belongs to the CURRENT device: the
+ * stream must belong to it.  The call allocates and frees nothing (the
+ * array's device address is looked up once per device, on the first call
+ * there).  Every call on one GPU shares that GPU's array and leaves its
+ * contents behind, so calls that overlap on one GPU (on two streams, or from
+ * two threads without ordering) race; order them on one stream.
+ * Errors: as muon_step, plus MUON_ERR_WORKSPACE_TOO_SMALL (before anything is
+ * enqueued) when muon_workspace_size(...) of the call exceeds
+ * MUON_STATIC_WORKSPACE_BYTES, MUON_ERR_INVALID_ARG when the stream belongs
+ * to another device, MUON_ERR_HIP when the array cannot be located. */
+muon_status muon_step_static(const muon_param *params, int n,
+                             float lr, float mu, float beta_a, float alpha, float lambda,
+                             int ns_steps, muon_variant variant, const muon_options *opts,
+                             void *stream);
+
 /* One vector-shaped parameter (bias, norm weight, embedding: anything the
  * caller keeps out of Muon) and its AdamW state.  Every buffer holds numel
  * contiguous elements on the device; none may overlap another. */

@@ -25,8 +25,10 @@ MUON_F32, MUON_F16, MUON_BF16 = 0, 1, 2
 MUON_NS_DIRECT, MUON_NS_GRAM = 0, 1
 
 # every entry point declared in include/muon.h
-EXPORTS = ("muon_options_init", "muon_workspace_size", "muon_step", "muon_adamw_step", "muon_status_string",
-           "muon_last_error", "muon_version")
+EXPORTS = ("muon_options_init", "muon_workspace_size", "muon_step", "muon_step_static", "muon_adamw_step",
+           "muon_status_string", "muon_last_error", "muon_version")
+# bytes of the static workspace of muon_step_static (MUON_STATIC_WORKSPACE_BYTES)
+STATIC_WORKSPACE_BYTES = 64 << 20
 
 
 class MuonParam(ctypes.Structure):
@@ -113,6 +115,10 @@ def load(path: str = LIB_PATH):
                               ctypes.c_int, ctypes.c_int, ctypes.POINTER(MuonOptions),
                               ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.muon_step.restype = ctypes.c_int
+    lib.muon_step_static.argtypes = [ctypes.POINTER(MuonParam), ctypes.c_int,
+                                     ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                                     ctypes.c_int, ctypes.c_int, ctypes.POINTER(MuonOptions), ctypes.c_void_p]
+    lib.muon_step_static.restype = ctypes.c_int
     lib.muon_adamw_step.argtypes = [ctypes.POINTER(MuonAdamwParam), ctypes.c_int, ctypes.c_int,
                                     ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_float,
                                     ctypes.c_int64, ctypes.POINTER(MuonTrace), ctypes.c_void_p]

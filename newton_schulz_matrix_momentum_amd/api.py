@@ -185,6 +185,21 @@ def muon_step(params: Sequence[Dict], *, lr: float, mu: float, beta_a: float = 0
                              ws.numel(), ctypes.c_void_p(stream)))
 
 
+def muon_step_static(params: Sequence[Dict], *, lr: float, mu: float, beta_a: float = 0.0, alpha: float = 0.0,
+                     weight_decay: float = 0.0, ns_steps: int = 5, variant: str = "direct", ns_dtype=None,
+                     coeffs=None, divisor: float = 1.0, restart_every: int = 0, step: int = 0, trace=None) -> None:
+    """``muon_step`` through ``muon_step_static``: the same step with the
+    library's static per-GPU workspace (64 MiB) instead of an allocated one,
+    for callers that cannot allocate.  Calls on one GPU share that workspace:
+    order them on one stream.  Raises when the call needs a larger workspace."""
+    arr, n, opts, keep, device = _marshal(params, ns_dtype, coeffs, divisor, restart_every, step, trace)
+    lib = _lib.load()
+    stream = torch.cuda.current_stream(device).cuda_stream if device is not None else None
+    _lib.check(lib.muon_step_static(arr, n, float(lr), float(mu), float(beta_a), float(alpha), float(weight_decay),
+                                    int(ns_steps), _VARIANTS[variant], ctypes.byref(opts),
+                                    ctypes.c_void_p(stream) if stream else None))
+
+
 def adamw_step(params: Sequence[Dict], *, lr: float, betas=(0.9, 0.999), eps: float = 1e-8,
                weight_decay: float = 0.0, step: int = 0, trace=None) -> None:
     """One decoupled AdamW step (``muon_adamw_step``) over ``params``: dicts of

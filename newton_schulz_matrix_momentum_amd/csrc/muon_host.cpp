@@ -816,6 +816,11 @@ muon_status run_gram(const Plan &plan, char *ws, Tracer &st, double sx0, float l
 
 }  // namespace
 
+muon_status muon::record_error(muon_status s, const char *msg) {
+  g_last_error = msg ? msg : "";
+  return s;
+}
+
 extern "C" {
 
 void muon_options_init(muon_options *o) {

@@ -10,6 +10,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "muon.h"
+
 #include <climits>
 
 namespace muon {
@@ -239,6 +241,9 @@ struct AdamArgs {
   int32_t begin[kAdamMaxTensors];   // first block of each tensor (see E1Args)
   AdamTensor t[kAdamMaxTensors];
 };
+
+// Record `msg` as the calling thread's muon_last_error() and return `s`.
+muon_status record_error(muon_status s, const char *msg);
 
 // Launchers (return the launch status).
 hipError_t launch_e1(const E1Args &args, int blocks, hipStream_t s);

@@ -280,3 +280,18 @@ def test_workspace_keeps_buffers_used_under_graph_capture(monkeypatch):
     c = ws.get(10000, torch.device("cpu"))                 # grows again: b must survive
     assert c is not b and len(ws.retired) == 1 and ws.retired[0] is b
     assert ws.get(20000, torch.device("cpu")) is not c and len(ws.retired) == 1   # c never captured
+
+
+def test_static_entry_point_rejects_oversized_call_before_any_device_call(lib):
+    """muon_step_static sizes the call on the host first: a request beyond
+    its static workspace fails without touching the device (so this runs
+    without a GPU)."""
+    big = param(0, 4096, 4096)
+    o = opts(lib, ns_dtype=_lib.MUON_BF16)
+    need = lib.muon_workspace_size(arr(big), 1, 5, 0, ctypes.byref(o))
+    assert need > _lib.STATIC_WORKSPACE_BYTES
+    st = lib.muon_step_static(arr(big), 1, 0.02, 0.95, 0.0, 0.0, 0.0, 5, 0, ctypes.byref(o), None)
+    assert st == _lib.MUON_ERR_WORKSPACE_TOO_SMALL
+    assert "static workspace" in _lib.last_error()
+    assert lib.muon_step_static(arr(param(0, rows=0)), 1, 0.02, 0.95, 0.0, 0.0, 0.0, 5, 0, None, None) \
+        == _lib.MUON_ERR_INVALID_ARG
