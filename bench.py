@@ -190,11 +190,16 @@ def setup(w, variant, device, mona_lite=False):
     return params
 
 
-def step_kwargs(w, variant):
+def step_kwargs(w, variant, device="cpu"):
     divisor, restart = w.settings_for(variant)
-    return dict(lr=w.lr, mu=w.mu, beta_a=w.beta_a, alpha=w.alpha, weight_decay=w.weight_decay,
-                ns_steps=w.ns_steps, variant=variant, ns_dtype=w.ns_dtype, divisor=divisor,
-                restart_every=restart)
+    kw = dict(lr=w.lr, mu=w.mu, beta_a=w.beta_a, alpha=w.alpha, weight_decay=w.weight_decay,
+              ns_steps=w.ns_steps, variant=variant, ns_dtype=w.ns_dtype_for(variant), divisor=divisor,
+              restart_every=restart)
+    if variant == "limuon":
+        from workloads import workload_sketch
+        kw.update(w.limuon_settings())
+        kw["sketch"] = workload_sketch(w, 1, device=device)
+    return kw
 
 
 def coeff_table(w):
@@ -286,6 +291,8 @@ def gpu_timing(args, w, variant):
     torch.cuda.set_device(dev)
     params = setup(w, variant, dev, args.mona_lite)
     kw = step_kwargs(w, variant)
+    if "sketch" in kw:
+        kw["sketch"] = kw["sketch"].to(dev)
     coeffs = coeff_table(w)
     # MONA workloads time steps after the first (D = G - G_prev is live)
     step_idx = 1 if w.mona else 0
@@ -413,6 +420,11 @@ def cpu_baseline(args, w, variant, params, single_thread=False, seconds=None):
         blas = max([t.get("num_threads", 1) for t in threadpool_info() if t.get("user_api") == "blas"] or [1])
         divisor, restart = w.settings_for(variant)
         coeffs = oracle.coefficient_table(w.coeffs, w.ns_steps)
+        lm = {}
+        if variant == "limuon":
+            kw = step_kwargs(w, variant)
+            lm = dict(rank=kw["rank"], power_iters=kw["power_iters"])
+            sketch = kw["sketch"].double().numpy()
         classes = {}
         for i, (r, c) in enumerate(w.shapes):
             classes.setdefault((r, c), []).append(i)
@@ -423,6 +435,8 @@ def cpu_baseline(args, w, variant, params, single_thread=False, seconds=None):
         for (r, c), idx in classes.items():
             p = params[idx[0]]
             snap = {k: v.detach().cpu().double().numpy() for k, v in p.items() if hasattr(v, "detach")}
+            if lm:
+                lm["omega"] = sketch[:, :max(r, c)].T
             reps, spent = 0, 0.0
             while spent < budget or reps == 0:
                 t0 = time.perf_counter()
@@ -430,7 +444,7 @@ def cpu_baseline(args, w, variant, params, single_thread=False, seconds=None):
                                         weight_decay=w.weight_decay, coeffs=coeffs, variant=variant,
                                         divisor=divisor, restart_every=restart, accel=snap.get("accel"),
                                         prev_grad=snap.get("prev_grad"), lite_state=snap.get("mona_lite"),
-                                        beta_a=w.beta_a, alpha=w.alpha, step=1 if w.mona else 0)
+                                        beta_a=w.beta_a, alpha=w.alpha, step=1 if w.mona else 0, **lm)
                 spent += time.perf_counter() - t0
                 reps += 1
             per = spent / reps
@@ -474,17 +488,18 @@ def main():
     ew_bytes = sum(d["work"] for d in ew)
     ns_tflops = gemm["work"] / (gemm["ms"] * 1e-3) / 1e12 if gemm["ms"] > 0 else 0.0
     ew_gbps = ew_bytes / (ew_ms * 1e-3) / 1e9 if ew_ms > 0 else 0.0
-    peak = PEAK_TFLOPS[w.ns_dtype]
+    ns_dtype = w.ns_dtype_for(variant)
+    peak = PEAK_TFLOPS[ns_dtype]
     # dominant kernel by time per step
     dom = max(per_stage.items(), key=lambda kv: kv[1]["ms"])[0]
     if dom == "gemm":
         per_launch_work = gemm["work"] / gemm["launches"]
         per_launch_ms = gemm["ms"] / gemm["launches"]
         roof = {"kernel": "Newton-Schulz products (%s; all %g product launches of a step, averaged)"
-                          % (w.ns_dtype, gemm["launches"]), "bound": "mfma",
+                          % (ns_dtype, gemm["launches"]), "bound": "mfma",
                 "achieved": per_launch_work / (per_launch_ms * 1e-3) / 1e12, "peak": peak, "unit": "TFLOP/s",
                 "avg_launch_us": per_launch_ms * 1e3, "work_per_launch": per_launch_work,
-                "traffic": recorded_traffic(w.name)}
+                "traffic": recorded_traffic(w.name if variant == w.variants[0] else "%s_%s" % (w.name, variant))}
     else:
         d = per_stage[dom]
         per_launch_work = d["work"] / d["launches"]
@@ -521,11 +536,11 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.ns_dtype,
+        "dtype": ns_dtype,
         "data": "synthetic",
         "config": {"workload": w.name + ("+mona_lite" if args.mona_lite and w.mona else ""), "matrices": len(w.shapes),
                    "params": w.numel, "variant": variant,
-                   "ns_steps": w.ns_steps, "coeffs": w.coeffs, "grad_dtype": w.grad_dtype, "ns_dtype": w.ns_dtype,
+                   "ns_steps": w.ns_steps, "coeffs": w.coeffs, "grad_dtype": w.grad_dtype, "ns_dtype": ns_dtype,
                    "mona": ("lite" if args.mona_lite else True) if w.mona else False, "hip_graph": graphed, "parallelism": "single_gpu"},
         "ns_tflops": ns_tflops,
         "ns_frac_of_peak": ns_tflops / peak,

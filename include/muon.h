@@ -68,7 +68,9 @@ typedef enum muon_dtype {
 
 typedef enum muon_variant {
   MUON_NS_DIRECT = 0,   /* Newton-Schulz on X itself                             */
-  MUON_NS_GRAM = 1      /* Newton-Schulz on the smaller Gram matrix, with restarts */
+  MUON_NS_GRAM = 1,     /* Newton-Schulz on the smaller Gram matrix, with restarts */
+  MUON_LIMUON = 2       /* randomized SVD of the momentum instead of Newton-Schulz
+                           (LiMuon digest, "Метод"; see muon_options.sketch)      */
 } muon_variant;
 
 /* One weight matrix and its optimizer state.  Every buffer holds rows*cols
@@ -94,7 +96,9 @@ typedef enum muon_stage {
   MUON_STAGE_E2 = 2,     /* X0 in the Newton-Schulz dtype, layouts the NS reads */
   MUON_STAGE_GEMM = 3,   /* one grouped Newton-Schulz matrix product           */
   MUON_STAGE_E3 = 4,     /* decoupled weight-decay update                      */
-  MUON_STAGE_ADAMW = 5   /* AdamW over vector parameters (muon_adamw_step)     */
+  MUON_STAGE_ADAMW = 5,  /* AdamW over vector parameters (muon_adamw_step)     */
+  MUON_STAGE_SMALL = 6   /* LiMuon's (k+p)-wide stages: Gram partials, eigen-
+                            decompositions, test-matrix copy                   */
 } muon_stage;
 
 /* Optional launch timing.  When muon_options.trace is non-NULL the library
@@ -133,6 +137,26 @@ typedef struct muon_options {
   int32_t restart_every;   /* restart period r >= 0 (0 = never).      default 0         */
   int64_t step;            /* 0-based optimizer step; 0 => MONA's D is zero.  default 0 */
   muon_trace *trace;       /* optional launch timing (see muon_trace).  default NULL */
+  /* MUON_LIMUON only (ignored otherwise).  LiMuon digest ("LiMuon: Light and
+   * Fast Muon Optimizer for Large Models", section "Метод"): momentum, then a
+   * randomized SVD of it in place of Newton-Schulz -- the textbook randomized
+   * SVD (Halko, Martinsson & Tropp 2011, Algorithms 4.4 and 5.1).  Per matrix,
+   * with X the momentum in its wide orientation (s x l, s <= l; a tall matrix
+   * is transposed in and out) and Omega = the first l columns of `sketch`,
+   * transposed (l x (rank + oversample)):
+   *     Y = X Omega, Q = orth(Y); power_iters times: Q = orth(X orth(X^T Q));
+   *     B = Q^T X = U~ S V^T;  O = sum over the `rank` largest S_i that exceed
+   *     rcond * S_1 of (Q U~)_i V_i^T
+   * O is scale-invariant, so ns_steps, coeffs, divisor and restart_every are
+   * ignored.  The products run with fp32 operands: ns_dtype must be F32. */
+  const float *sketch;     /* DEVICE fp32 [(rank + oversample) x sketch_ld] Gaussian
+                              test matrix, row-major, drawn by the caller (row j =
+                              test vector j); read only.        default NULL       */
+  int64_t sketch_ld;       /* row stride of sketch, >= every matrix's long side   */
+  int32_t rank;            /* k >= 1.                                 default 0 (unset) */
+  int32_t oversample;      /* p >= 0, k + p <= 64.                    default 8         */
+  int32_t power_iters;     /* q in [0, 16].                           default 1         */
+  float rcond;             /* relative singular-value cutoff in [0, 1). default 1e-4    */
 } muon_options;
 
 /* Fill `o` with the defaults listed above. */
@@ -160,7 +184,11 @@ size_t muon_workspace_size(const muon_param *params, int n, int ns_steps,
  * given without the other, mona_lite together with accel, rows or cols < 1,
  * ns_steps out of range,
  * non-finite scalars, divisor < 1, restart_every < 0, buffers that overlap;
- * MUON_ERR_UNSUPPORTED for an unknown dtype; MUON_ERR_WORKSPACE_TOO_SMALL;
+ * for MUON_LIMUON also a NULL sketch, rank < 1, oversample < 0,
+ * rank + oversample > 64, power_iters outside [0, 16], rcond outside [0, 1),
+ * sketch_ld below a long side, a sketch overlapping another buffer;
+ * MUON_ERR_UNSUPPORTED for an unknown dtype (and for MUON_LIMUON with a
+ * 16-bit ns_dtype); MUON_ERR_WORKSPACE_TOO_SMALL;
  * MUON_ERR_HIP when a launch fails. */
 muon_status muon_step(const muon_param *params, int n,
                       float lr, float mu, float beta_a, float alpha, float lambda,

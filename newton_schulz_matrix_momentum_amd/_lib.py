@@ -22,7 +22,7 @@ MUON_ERR_WORKSPACE_TOO_SMALL = 3
 MUON_ERR_HIP = 4
 
 MUON_F32, MUON_F16, MUON_BF16 = 0, 1, 2
-MUON_NS_DIRECT, MUON_NS_GRAM = 0, 1
+MUON_NS_DIRECT, MUON_NS_GRAM, MUON_LIMUON = 0, 1, 2
 
 # every entry point declared in include/muon.h
 EXPORTS = ("muon_options_init", "muon_workspace_size", "muon_step", "muon_step_static", "muon_adamw_step",
@@ -58,8 +58,9 @@ class MuonTrace(ctypes.Structure):
     ]
 
 
-MUON_STAGE_E1, MUON_STAGE_NORM, MUON_STAGE_E2, MUON_STAGE_GEMM, MUON_STAGE_E3, MUON_STAGE_ADAMW = range(6)
-STAGE_NAMES = {0: "e1", 1: "norm", 2: "e2", 3: "gemm", 4: "e3", 5: "adamw"}
+MUON_STAGE_E1, MUON_STAGE_NORM, MUON_STAGE_E2, MUON_STAGE_GEMM, MUON_STAGE_E3, MUON_STAGE_ADAMW, \
+    MUON_STAGE_SMALL = range(7)
+STAGE_NAMES = {0: "e1", 1: "norm", 2: "e2", 3: "gemm", 4: "e3", 5: "adamw", 6: "small"}
 
 
 class MuonOptions(ctypes.Structure):
@@ -71,6 +72,12 @@ class MuonOptions(ctypes.Structure):
         ("restart_every", ctypes.c_int32),
         ("step", ctypes.c_int64),
         ("trace", ctypes.POINTER(MuonTrace)),
+        ("sketch", ctypes.c_void_p),
+        ("sketch_ld", ctypes.c_int64),
+        ("rank", ctypes.c_int32),
+        ("oversample", ctypes.c_int32),
+        ("power_iters", ctypes.c_int32),
+        ("rcond", ctypes.c_float),
     ]
 
 

@@ -18,7 +18,7 @@ _DT = {torch.float32: _lib.MUON_F32, torch.float16: _lib.MUON_F16, torch.bfloat1
 _DT_NAMES = {"f32": _lib.MUON_F32, "fp32": _lib.MUON_F32, "float32": _lib.MUON_F32,
              "f16": _lib.MUON_F16, "fp16": _lib.MUON_F16, "float16": _lib.MUON_F16,
              "bf16": _lib.MUON_BF16, "bfloat16": _lib.MUON_BF16}
-_VARIANTS = {"direct": _lib.MUON_NS_DIRECT, "gram": _lib.MUON_NS_GRAM}
+_VARIANTS = {"direct": _lib.MUON_NS_DIRECT, "gram": _lib.MUON_NS_GRAM, "limuon": _lib.MUON_LIMUON}
 
 
 def _ptr(t: Optional[torch.Tensor], name: str, dtype=None, shape=None):
@@ -45,7 +45,7 @@ def _dtype_code(x):
     return _DT_NAMES[str(x).lower()]
 
 
-def _marshal(params: Sequence[Dict], ns_dtype, coeffs, divisor, restart_every, step, trace=None):
+def _marshal(params: Sequence[Dict], ns_dtype, coeffs, divisor, restart_every, step, trace=None, limuon=None):
     n = len(params)
     arr = (_lib.MuonParam * max(n, 1))()
     grad_dtype = None
@@ -92,12 +92,34 @@ def _marshal(params: Sequence[Dict], ns_dtype, coeffs, divisor, restart_every, s
     opts.step = int(step)
     if trace is not None:
         opts.trace = ctypes.pointer(trace)
+    if limuon:
+        sk = limuon.get("sketch")
+        if sk is not None:
+            if sk.dim() != 2:
+                raise ValueError("sketch must be 2-D: (rank + oversample) x sketch_ld")
+            if device is not None and sk.device != device:
+                raise ValueError("sketch is on %s, the weights on %s" % (sk.device, device))
+            opts.sketch = _ptr(sk, "sketch", torch.float32)
+            opts.sketch_ld = int(sk.shape[1])
+            if "oversample" not in limuon and limuon.get("rank") is not None:
+                opts.oversample = int(sk.shape[0]) - int(limuon["rank"])
+        for key in ("rank", "oversample", "power_iters"):
+            if limuon.get(key) is not None:
+                setattr(opts, key, int(limuon[key]))
+        if limuon.get("rcond") is not None:
+            opts.rcond = float(limuon["rcond"])
+        if sk is not None and int(sk.shape[0]) != opts.rank + opts.oversample:
+            raise ValueError("sketch has %d rows, rank + oversample is %d" % (sk.shape[0], opts.rank + opts.oversample))
     return arr, n, opts, keep, device
 
 
 def muon_workspace_size(params: Sequence[Dict], *, ns_steps: int = 5, variant: str = "direct", ns_dtype=None,
-                        coeffs=None, divisor: float = 1.0, restart_every: int = 0, step: int = 0) -> int:
-    arr, n, opts, keep, _ = _marshal(params, ns_dtype, coeffs, divisor, restart_every, step)
+                        coeffs=None, divisor: float = 1.0, restart_every: int = 0, step: int = 0,
+                        sketch=None, rank=None, oversample=None, power_iters=None, rcond=None) -> int:
+    lm = dict(sketch=sketch, rank=rank, power_iters=power_iters, rcond=rcond)
+    if oversample is not None:
+        lm["oversample"] = oversample
+    arr, n, opts, keep, _ = _marshal(params, ns_dtype, coeffs, divisor, restart_every, step, limuon=lm)
     size = _lib.load().muon_workspace_size(arr, n, int(ns_steps), _VARIANTS[variant], ctypes.byref(opts))
     if size == 0 and n > 0:
         raise _lib.MuonError(_lib.MUON_ERR_INVALID_ARG, _lib.last_error())
@@ -148,7 +170,8 @@ _default_ws: Dict = {}
 def muon_step(params: Sequence[Dict], *, lr: float, mu: float, beta_a: float = 0.0, alpha: float = 0.0,
               weight_decay: float = 0.0, ns_steps: int = 5, variant: str = "direct", ns_dtype=None, coeffs=None,
               divisor: float = 1.0, restart_every: int = 0, step: int = 0,
-              workspace: Optional[torch.Tensor] = None, trace=None) -> None:
+              workspace: Optional[torch.Tensor] = None, trace=None, sketch=None, rank=None, oversample=None,
+              power_iters=None, rcond=None) -> None:
     """One Muon / MONA step over ``params`` (list of dicts of tensors).
 
     Each dict holds ``weight`` (fp32, updated), ``grad``, ``momentum`` (fp32,
@@ -157,8 +180,17 @@ def muon_step(params: Sequence[Dict], *, lr: float, mu: float, beta_a: float = 0
     ``ortho_out`` (fp32, receives O).  Enqueued on the
     current stream; returns without synchronising.  ``trace`` is an optional
     ``_lib.MuonTrace`` for per-launch HIP-event timing.
+
+    ``variant="limuon"`` orthogonalises by a randomized SVD instead of
+    Newton-Schulz: ``sketch`` is the Gaussian test matrix, a float32 GPU
+    tensor of (rank + oversample) x L (L >= every matrix's long side), with
+    ``rank``, ``power_iters`` (default 1) and ``rcond`` (default 1e-4);
+    ``ns_dtype`` must be f32.
     """
-    arr, n, opts, keep, device = _marshal(params, ns_dtype, coeffs, divisor, restart_every, step, trace)
+    lm = dict(sketch=sketch, rank=rank, power_iters=power_iters, rcond=rcond)
+    if oversample is not None:
+        lm["oversample"] = oversample
+    arr, n, opts, keep, device = _marshal(params, ns_dtype, coeffs, divisor, restart_every, step, trace, lm)
     lib = _lib.load()
     if n == 0:
         _lib.check(lib.muon_step(arr, 0, lr, mu, beta_a, alpha, weight_decay, int(ns_steps), _VARIANTS[variant],
@@ -187,12 +219,16 @@ def muon_step(params: Sequence[Dict], *, lr: float, mu: float, beta_a: float = 0
 
 def muon_step_static(params: Sequence[Dict], *, lr: float, mu: float, beta_a: float = 0.0, alpha: float = 0.0,
                      weight_decay: float = 0.0, ns_steps: int = 5, variant: str = "direct", ns_dtype=None,
-                     coeffs=None, divisor: float = 1.0, restart_every: int = 0, step: int = 0, trace=None) -> None:
+                     coeffs=None, divisor: float = 1.0, restart_every: int = 0, step: int = 0, trace=None,
+                     sketch=None, rank=None, oversample=None, power_iters=None, rcond=None) -> None:
     """``muon_step`` through ``muon_step_static``: the same step with the
     library's static per-GPU workspace (64 MiB) instead of an allocated one,
     for callers that cannot allocate.  Calls on one GPU share that workspace:
     order them on one stream.  Raises when the call needs a larger workspace."""
-    arr, n, opts, keep, device = _marshal(params, ns_dtype, coeffs, divisor, restart_every, step, trace)
+    lm = dict(sketch=sketch, rank=rank, power_iters=power_iters, rcond=rcond)
+    if oversample is not None:
+        lm["oversample"] = oversample
+    arr, n, opts, keep, device = _marshal(params, ns_dtype, coeffs, divisor, restart_every, step, trace, lm)
     lib = _lib.load()
     stream = torch.cuda.current_stream(device).cuda_stream if device is not None else None
     _lib.check(lib.muon_step_static(arr, n, float(lr), float(mu), float(beta_a), float(alpha), float(weight_decay),

@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmuon.so")
-SOURCES = ["muon_host.cpp", "elementwise.hip", "ns_gemm.hip", "muon_static.hip"]
+SOURCES = ["muon_host.cpp", "elementwise.hip", "ns_gemm.hip", "limuon.hip", "muon_static.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU ops are disabled for all device code.

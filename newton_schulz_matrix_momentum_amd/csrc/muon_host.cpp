@@ -62,7 +62,16 @@ struct Settings {
   double divisor = 1.0;
   int restart_every = 0;
   int64_t step = 0;
+  // LiMuon
+  const float *sketch = nullptr;
+  int64_t sketch_ld = 0;
+  int rank = 0, oversample = 0, power_iters = 0;
+  double rcond = 0.0;
 };
+
+// LiMuon buffers of a class (indices into ClassInfo::lm): the padded test
+// matrix (shared by the class) and the (k + p)-wide panels of each matrix.
+enum LmBuf { kLmOmt = 0, kLmY, kLmQ, kLmQ2, kLmQt, kLmZ, kLmZ2, kLmZ2t, kLmW, kLmT, kLmP, kLmBufs };
 
 struct ClassInfo {
   int64_t s = 0, l = 0;
@@ -72,6 +81,9 @@ struct ClassInfo {
   std::vector<int> members;
   size_t X[2] = {0, 0}, XT[2] = {0, 0};
   size_t sq[5] = {0, 0, 0, 0, 0};   // direct: A, B ; gram: R, T, P, Q, Qspare
+  size_t lm[kLmBufs] = {};         // LiMuon panels
+  int lm_part_base = 0;            // first fp64 Gram partial slot (LiMuon)
+  int lm_chunks_s = 0, lm_chunks_l = 0;   // partial chunks of an s-row / l-row panel
 };
 
 struct Plan {
@@ -83,7 +95,13 @@ struct Plan {
   std::vector<int> cls_of, idx_in_cls;
   std::vector<int> e1_blocks, partial_off;
   size_t off_partials = 0, off_scales = 0, off_desc = 0, total = 0;
+  size_t off_lm_parts = 0;         // LiMuon fp64 Gram partials
 };
+
+bool is_limuon(const Plan &plan) { return plan.variant == MUON_LIMUON; }
+// The step ends in an orthogonalisation product that applies the update
+// (otherwise E3 applies it to X0).
+bool has_products(const Plan &plan) { return is_limuon(plan) || plan.K > 0; }
 
 bool is_finite(double v) { return std::isfinite(v); }
 
@@ -102,7 +120,7 @@ int pick_tile(int64_t s, int64_t l, int ns_dtype) {
   return 64;
 }
 
-muon_status read_options(const muon_options *o, int ns_steps, Settings &s) {
+muon_status read_options(const muon_options *o, int ns_steps, muon_variant v, Settings &s) {
   s = Settings();
   muon_options d;
   muon_options_init(&d);
@@ -120,6 +138,25 @@ muon_status read_options(const muon_options *o, int ns_steps, Settings &s) {
   s.divisor = o->divisor;
   s.restart_every = o->restart_every;
   s.step = o->step;
+  if (v == MUON_LIMUON) {
+    if (s.ns_dtype != kF32)
+      return fail(MUON_ERR_UNSUPPORTED, "LiMuon runs its products with fp32 operands: ns_dtype must be MUON_F32");
+    if (!o->sketch) return fail(MUON_ERR_INVALID_ARG, "LiMuon needs a sketch (Gaussian test matrix)");
+    if (o->rank < 1) return fail(MUON_ERR_INVALID_ARG, "LiMuon rank must be >= 1 (got %d)", (int)o->rank);
+    if (o->oversample < 0) return fail(MUON_ERR_INVALID_ARG, "LiMuon oversample must be >= 0");
+    if ((int64_t)o->rank + o->oversample > kLmKP)
+      return fail(MUON_ERR_INVALID_ARG, "LiMuon rank + oversample must be <= %d (got %d)", kLmKP,
+                  (int)(o->rank + o->oversample));
+    if (o->power_iters < 0 || o->power_iters > 16) return fail(MUON_ERR_INVALID_ARG, "LiMuon power_iters must lie in [0, 16]");
+    if (!is_finite(o->rcond) || o->rcond < 0.0f || o->rcond >= 1.0f)
+      return fail(MUON_ERR_INVALID_ARG, "LiMuon rcond must lie in [0, 1)");
+    s.sketch = o->sketch;
+    s.sketch_ld = o->sketch_ld;
+    s.rank = o->rank;
+    s.oversample = o->oversample;
+    s.power_iters = o->power_iters;
+    s.rcond = o->rcond;
+  }
   s.coeffs.resize(3 * (size_t)ns_steps);
   for (int k = 0; k < ns_steps; ++k) {
     for (int j = 0; j < 3; ++j) {
@@ -145,7 +182,17 @@ struct Range {
 
 muon_status check_params(const muon_param *p, int n, const Settings &set) {
   std::vector<Range> ranges;
-  ranges.reserve((size_t)n * 6);
+  ranges.reserve((size_t)n * 6 + 1);
+  if (set.sketch) {
+    int64_t lmax = 0;
+    for (int i = 0; i < n; ++i) lmax = std::max(lmax, std::max(p[i].rows, p[i].cols));
+    if (set.sketch_ld < std::max<int64_t>(lmax, 1))
+      return fail(MUON_ERR_INVALID_ARG, "sketch_ld %lld is below the longest side %lld", (long long)set.sketch_ld,
+                  (long long)lmax);
+    if (set.sketch_ld > kMaxDim) return fail(MUON_ERR_UNSUPPORTED, "sketch_ld exceeds the supported size");
+    const uint64_t kp = (uint64_t)(set.rank + set.oversample);
+    ranges.push_back({(uintptr_t)set.sketch, (uintptr_t)set.sketch + kp * (uint64_t)set.sketch_ld * 4, -1, "sketch"});
+  }
   for (int i = 0; i < n; ++i) {
     const muon_param &q = p[i];
     if (!q.weight || !q.grad || !q.momentum) return fail(MUON_ERR_INVALID_ARG, "param %d: weight, grad and momentum must be non-NULL", i);
@@ -183,8 +230,9 @@ muon_status build_plan(const muon_param *p, int n, int ns_steps, muon_variant v,
   if (n < 0) return fail(MUON_ERR_INVALID_ARG, "n must be >= 0");
   if (n > 0 && !p) return fail(MUON_ERR_INVALID_ARG, "params is NULL");
   if (ns_steps < 0 || ns_steps > kMaxSteps) return fail(MUON_ERR_INVALID_ARG, "ns_steps must be in [0, %d]", kMaxSteps);
-  if (v != MUON_NS_DIRECT && v != MUON_NS_GRAM) return fail(MUON_ERR_INVALID_ARG, "unknown variant %d", (int)v);
-  muon_status st = read_options(o, ns_steps, plan.set);
+  if (v != MUON_NS_DIRECT && v != MUON_NS_GRAM && v != MUON_LIMUON)
+    return fail(MUON_ERR_INVALID_ARG, "unknown variant %d", (int)v);
+  muon_status st = read_options(o, ns_steps, v, plan.set);
   if (st != MUON_OK) return st;
   st = check_params(p, n, plan.set);
   if (st != MUON_OK) return st;
@@ -205,7 +253,8 @@ muon_status build_plan(const muon_param *p, int n, int ns_steps, muon_variant v,
       ClassInfo ci;
       ci.s = s;
       ci.l = l;
-      ci.tile = pick_tile(s, l, plan.set.ns_dtype);
+      // LiMuon's panels are kLmKP wide: every product uses the 64 tile
+      ci.tile = (v == MUON_LIMUON) ? 64 : pick_tile(s, l, plan.set.ns_dtype);
       ci.Sp = round_up(s, ci.tile);
       ci.Lp = round_up(l, ci.tile);
       plan.classes.push_back(ci);
@@ -234,16 +283,46 @@ muon_status build_plan(const muon_param *p, int n, int ns_steps, muon_variant v,
     }
   }
   const size_t es = (size_t)elem_size(plan.set.ns_dtype);
-  for (ClassInfo &c : plan.classes) {
-    const size_t cnt = c.members.size();
-    const size_t rect = (size_t)c.Sp * (size_t)c.Lp * es * cnt;
-    const size_t sqb = (size_t)c.Sp * (size_t)c.Sp * es * cnt;
-    for (int j = 0; j < 2; ++j) {
-      c.X[j] = off; off = align256(off + rect);
-      c.XT[j] = off; off = align256(off + rect);
+  if (v == MUON_LIMUON) {
+    // X0 in both orientations, the class's padded test matrix, the panels,
+    // and the fp64 Gram partials (one set per matrix, enough chunks for an
+    // l-row panel)
+    int slots = 0;
+    for (ClassInfo &c : plan.classes) {
+      const size_t cnt = c.members.size();
+      const size_t rect = (size_t)c.Sp * (size_t)c.Lp * es * cnt;
+      c.X[0] = off; off = align256(off + rect);
+      c.XT[0] = off; off = align256(off + rect);
+      c.X[1] = c.X[0];
+      c.XT[1] = c.XT[0];
+      const size_t kp = (size_t)kLmKP;
+      const size_t sizes[kLmBufs] = {kp * (size_t)c.Lp * 4,                                     // omt (shared)
+                                     (size_t)c.Sp * kp * 4 * cnt, (size_t)c.Sp * kp * 4 * cnt,   // y, q
+                                     (size_t)c.Sp * kp * 4 * cnt, (size_t)c.Sp * kp * 4 * cnt,   // q2, qt
+                                     (size_t)c.Lp * kp * 4 * cnt, (size_t)c.Lp * kp * 4 * cnt,   // z, z2
+                                     (size_t)c.Lp * kp * 4 * cnt,                                // z2t
+                                     kp * kp * 4 * cnt, kp * kp * 4 * cnt,                       // w, t
+                                     (size_t)c.Sp * kp * 4 * cnt};                               // p
+      for (int j = 0; j < kLmBufs; ++j) { c.lm[j] = off; off = align256(off + sizes[j]); }
+      c.lm_chunks_s = (int)((c.s + kLmChunk - 1) / kLmChunk);
+      c.lm_chunks_l = (int)((c.l + kLmChunk - 1) / kLmChunk);
+      c.lm_part_base = slots;
+      slots += (int)cnt * c.lm_chunks_l;
     }
-    const int nsq = (v == MUON_NS_DIRECT) ? 2 : 5;
-    for (int j = 0; j < nsq; ++j) { c.sq[j] = off; off = align256(off + sqb); }
+    plan.off_lm_parts = off;
+    off = align256(off + (size_t)slots * kLmSlot * sizeof(double));
+  } else {
+    for (ClassInfo &c : plan.classes) {
+      const size_t cnt = c.members.size();
+      const size_t rect = (size_t)c.Sp * (size_t)c.Lp * es * cnt;
+      const size_t sqb = (size_t)c.Sp * (size_t)c.Sp * es * cnt;
+      for (int j = 0; j < 2; ++j) {
+        c.X[j] = off; off = align256(off + rect);
+        c.XT[j] = off; off = align256(off + rect);
+      }
+      const int nsq = (v == MUON_NS_DIRECT) ? 2 : 5;
+      for (int j = 0; j < nsq; ++j) { c.sq[j] = off; off = align256(off + sqb); }
+    }
   }
   plan.total = std::max<size_t>(off, 256);
   return MUON_OK;
@@ -814,6 +893,233 @@ muon_status run_gram(const Plan &plan, char *ws, Tracer &st, double sx0, float l
   return MUON_OK;
 }
 
+// ---------------------------------------------------------------- LiMuon
+// Randomized SVD of X (X0 in its wide orientation, s x l) in place of
+// Newton-Schulz (LiMuon digest, "Метод"; Halko, Martinsson & Tropp 2011,
+// Algorithms 4.4 and 5.1), with kp = k + p test vectors padded to kLmKP:
+//   Y = X Omega ; Q = orth(Y)
+//   q times: Z = orth(X^T Q) ; Q = orth(X Z)     (the last Q orthonormalised twice)
+//   B^T = X^T Q ; H = B B^T = V D V^T ; T = V_k D_k^{-1/2} V_k^T
+//   O^T = B^T (Q T)^T   (= V_k U_k^T ... in the tall orientation), fused with
+//                        the weight update
+// orth(P) = P W with W = V_r D_r^{-1/2} from the fp64 Jacobi eigen-
+// decomposition of P^T P (directions at most 1e-12 of the largest
+// eigenvalue dropped).  Every product is a grouped fp32 GEMM on 64 tiles;
+// the Gram partials and eigen-decompositions are the lm_* kernels.
+muon_status run_limuon(const Plan &plan, char *ws, Tracer &st, float lr, float wd) {
+  const int kp = plan.set.rank + plan.set.oversample;
+  const int KP = kLmKP;
+  double *parts = (double *)(ws + plan.off_lm_parts);
+  const size_t es = 4;
+  const size_t pan_s = 0, pan_l = 1;   // panel kinds: s rows or l rows
+
+  // pad the caller's test matrix into each class's [KP x Lp] buffer
+  {
+    LmPadArgs a;
+    std::memset(&a, 0, sizeof(a));
+    for (int j = 0; j < kLmMaxClasses; ++j) a.begin[j] = INT32_MAX;
+    a.src = plan.set.sketch;
+    a.ld = plan.set.sketch_ld;
+    a.kp = kp;
+    int blocks = 0;
+    double bytes = 0.0;
+    auto go = [&]() -> muon_status {
+      if (a.nclass == 0) return MUON_OK;
+      HIP_TRY(st.run(MUON_STAGE_SMALL, bytes, [&]() { return launch_lm_pad(a, blocks, st.s); }));
+      a.nclass = 0;
+      blocks = 0;
+      bytes = 0.0;
+      for (int j = 0; j < kLmMaxClasses; ++j) a.begin[j] = INT32_MAX;
+      return MUON_OK;
+    };
+    for (const ClassInfo &cl : plan.classes) {
+      if (a.nclass == kLmMaxClasses) {
+        muon_status e = go();
+        if (e != MUON_OK) return e;
+      }
+      LmPadClass &c = a.cls[a.nclass];
+      c.dst = (float *)(ws + cl.lm[kLmOmt]);
+      c.l = (int32_t)cl.l;
+      c.lp = (int32_t)cl.Lp;
+      c.blocks = (int32_t)(((int64_t)KP * cl.Lp + kLmPadElems - 1) / kLmPadElems);
+      a.begin[a.nclass++] = blocks;
+      blocks += c.blocks;
+      bytes += (double)kp * (double)cl.l * 4.0 + (double)KP * (double)cl.Lp * 4.0;
+    }
+    muon_status e = go();
+    if (e != MUON_OK) return e;
+  }
+
+  // fp64 Gram partials of one panel per matrix, then the eigen stage
+  auto gram_eig = [&](int buf, size_t kind, int mode, int out_buf) -> muon_status {
+    {
+      LmGramArgs a;
+      std::memset(&a, 0, sizeof(a));
+      for (int j = 0; j < kLmMaxClasses; ++j) a.block_begin[j] = INT32_MAX;
+      a.n = kp;
+      a.partials = parts;
+      int blocks = 0;
+      double bytes = 0.0;
+      auto go = [&]() -> muon_status {
+        if (a.nclass == 0) return MUON_OK;
+        HIP_TRY(st.run(MUON_STAGE_SMALL, bytes, [&]() { return launch_lm_gram(a, blocks, st.s); }));
+        a.nclass = 0;
+        blocks = 0;
+        bytes = 0.0;
+        for (int j = 0; j < kLmMaxClasses; ++j) a.block_begin[j] = INT32_MAX;
+        return MUON_OK;
+      };
+      for (const ClassInfo &cl : plan.classes) {
+        if (a.nclass == kLmMaxClasses) {
+          muon_status e = go();
+          if (e != MUON_OK) return e;
+        }
+        const int64_t rows = kind == pan_s ? cl.s : cl.l;
+        const int64_t prows = kind == pan_s ? cl.Sp : cl.Lp;
+        LmGramClass &c = a.cls[a.nclass];
+        c.panel = (const float *)(ws + cl.lm[buf]);
+        c.stride = prows * KP;
+        c.rows = (int32_t)rows;
+        c.nchunks = kind == pan_s ? cl.lm_chunks_s : cl.lm_chunks_l;
+        c.count = (int32_t)cl.members.size();
+        c.part_base = cl.lm_part_base;
+        a.block_begin[a.nclass++] = blocks;
+        blocks += c.count * c.nchunks;
+        bytes += (double)rows * kp * 4.0 * c.count;
+      }
+      muon_status e = go();
+      if (e != MUON_OK) return e;
+    }
+    {
+      LmEigArgs a;
+      std::memset(&a, 0, sizeof(a));
+      for (int j = 0; j < kLmMaxClasses; ++j) a.begin[j] = INT32_MAX;
+      a.n = kp;
+      a.mode = mode;
+      a.rank = plan.set.rank;
+      a.cutoff = mode == kLmOrth ? 1e-12 : plan.set.rcond * plan.set.rcond;
+      a.partials = parts;
+      int blocks = 0;
+      auto go = [&]() -> muon_status {
+        if (a.nclass == 0) return MUON_OK;
+        HIP_TRY(st.run(MUON_STAGE_SMALL, 0.0, [&]() { return launch_lm_eig(a, blocks, st.s); }));
+        a.nclass = 0;
+        blocks = 0;
+        for (int j = 0; j < kLmMaxClasses; ++j) a.begin[j] = INT32_MAX;
+        return MUON_OK;
+      };
+      for (const ClassInfo &cl : plan.classes) {
+        if (a.nclass == kLmMaxClasses) {
+          muon_status e = go();
+          if (e != MUON_OK) return e;
+        }
+        LmEigClass &c = a.cls[a.nclass];
+        c.out = (float *)(ws + cl.lm[out_buf]);
+        c.out_stride = (int64_t)KP * KP;
+        c.count = (int32_t)cl.members.size();
+        c.nchunks = kind == pan_s ? cl.lm_chunks_s : cl.lm_chunks_l;
+        c.part_base = cl.lm_part_base;
+        a.begin[a.nclass++] = blocks;
+        blocks += c.count;
+      }
+      muon_status e = go();
+      if (e != MUON_OK) return e;
+    }
+    return MUON_OK;
+  };
+
+  // C (m x KP or l x KP) = panel (rows x KP) W, and optionally C^T
+  auto apply_w = [&](int in_buf, size_t kind, int w_buf, int out_buf, int out_t_buf) -> muon_status {
+    StageBuilder sb(plan, ws, st);
+    for (size_t ci = 0; ci < plan.classes.size(); ++ci) {
+      const ClassInfo &cl = plan.classes[ci];
+      const int64_t prows = kind == pan_s ? cl.Sp : cl.Lp;
+      GemmClass g = make_gemm(cl, es, ws, cl.lm[in_buf], prows, KP, cl.lm[w_buf], KP, KP, KP, false);
+      set_out(g, ws, cl.lm[out_buf], prows, KP, true);
+      if (out_t_buf >= 0) set_out2(g, ws, cl.lm[out_t_buf], KP, prows);
+      sb.per_class[ci] = g;
+      sb.per_flops[ci] = 2.0 * (double)(kind == pan_s ? cl.s : cl.l) * kp * kp;
+    }
+    HIP_TRY(sb.launch());
+    return MUON_OK;
+  };
+  auto orth = [&](int in_buf, size_t kind, int out_buf, int out_t_buf) -> muon_status {
+    muon_status e = gram_eig(in_buf, kind, kLmOrth, kLmW);
+    if (e != MUON_OK) return e;
+    return apply_w(in_buf, kind, kLmW, out_buf, out_t_buf);
+  };
+  // X-panel products: long = X (s x l) times an l-row panel stored
+  // transposed [KP x Lp]; short = X^T (l x s) times an s-row panel stored
+  // transposed [KP x Sp]
+  auto x_times = [&](int bt_buf, bool shared_b, int out_buf) -> muon_status {
+    StageBuilder sb(plan, ws, st);
+    for (size_t ci = 0; ci < plan.classes.size(); ++ci) {
+      const ClassInfo &cl = plan.classes[ci];
+      GemmClass g = make_gemm(cl, es, ws, cl.X[0], cl.Sp, cl.Lp, cl.lm[bt_buf], KP, cl.Lp, cl.Lp, false);
+      if (shared_b) g.sb = 0;
+      set_out(g, ws, cl.lm[out_buf], cl.Sp, KP, true);
+      sb.per_class[ci] = g;
+      sb.per_flops[ci] = 2.0 * (double)cl.s * (double)cl.l * kp;
+    }
+    HIP_TRY(sb.launch());
+    return MUON_OK;
+  };
+  auto xt_times = [&](int bt_buf, int out_buf) -> muon_status {
+    StageBuilder sb(plan, ws, st);
+    for (size_t ci = 0; ci < plan.classes.size(); ++ci) {
+      const ClassInfo &cl = plan.classes[ci];
+      GemmClass g = make_gemm(cl, es, ws, cl.XT[0], cl.Lp, cl.Sp, cl.lm[bt_buf], KP, cl.Sp, cl.Sp, false);
+      set_out(g, ws, cl.lm[out_buf], cl.Lp, KP, true);
+      sb.per_class[ci] = g;
+      sb.per_flops[ci] = 2.0 * (double)cl.s * (double)cl.l * kp;
+    }
+    HIP_TRY(sb.launch());
+    return MUON_OK;
+  };
+
+  muon_status e;
+  // Y = X Omega ; Q = orth(Y)   (twice when no power iteration follows)
+  if ((e = x_times(kLmOmt, true, kLmY)) != MUON_OK) return e;
+  const int q = plan.set.power_iters;
+  if (q == 0) {
+    if ((e = orth(kLmY, pan_s, kLmQ2, -1)) != MUON_OK) return e;
+    if ((e = orth(kLmQ2, pan_s, kLmQ, kLmQt)) != MUON_OK) return e;
+  } else {
+    if ((e = orth(kLmY, pan_s, kLmQ, kLmQt)) != MUON_OK) return e;
+  }
+  for (int it = 0; it < q; ++it) {
+    // Z = orth(X^T Q), Y = X Z, Q = orth(Y) (orthonormalised twice at the end)
+    if ((e = xt_times(kLmQt, kLmZ)) != MUON_OK) return e;
+    if ((e = orth(kLmZ, pan_l, kLmZ2, kLmZ2t)) != MUON_OK) return e;
+    if ((e = x_times(kLmZ2t, false, kLmY)) != MUON_OK) return e;
+    if (it + 1 < q) {
+      if ((e = orth(kLmY, pan_s, kLmQ, kLmQt)) != MUON_OK) return e;
+    } else {
+      if ((e = orth(kLmY, pan_s, kLmQ2, -1)) != MUON_OK) return e;
+      if ((e = orth(kLmQ2, pan_s, kLmQ, kLmQt)) != MUON_OK) return e;
+    }
+  }
+  // B^T = X^T Q (into Z) ; T from B B^T
+  if ((e = xt_times(kLmQt, kLmZ)) != MUON_OK) return e;
+  if ((e = gram_eig(kLmZ, pan_l, kLmTrunc, kLmT)) != MUON_OK) return e;
+  // P = Q T
+  if ((e = apply_w(kLmQ, pan_s, kLmT, kLmP, -1)) != MUON_OK) return e;
+  // O^T = B^T P^T (tall orientation), fused with the weight update
+  {
+    StageBuilder sb(plan, ws, st);
+    for (size_t ci = 0; ci < plan.classes.size(); ++ci) {
+      const ClassInfo &cl = plan.classes[ci];
+      GemmClass g = make_gemm(cl, es, ws, cl.lm[kLmZ], cl.Lp, KP, cl.lm[kLmP], cl.Sp, KP, KP, false);
+      set_final(g, plan, cl, ws, lr, wd);
+      g.alpha = 1.0f;
+      sb.per_class[ci] = g;
+      sb.per_flops[ci] = 2.0 * (double)cl.s * (double)cl.l * kp;
+    }
+    HIP_TRY(sb.launch());
+  }
+  return MUON_OK;
+}
+
 }  // namespace
 
 muon_status muon::record_error(muon_status s, const char *msg) {
@@ -832,6 +1138,12 @@ void muon_options_init(muon_options *o) {
   o->restart_every = 0;
   o->step = 0;
   o->trace = nullptr;
+  o->sketch = nullptr;
+  o->sketch_ld = 0;
+  o->rank = 0;
+  o->oversample = 8;
+  o->power_iters = 1;
+  o->rcond = 1e-4f;
 }
 
 size_t muon_workspace_size(const muon_param *params, int n, int ns_steps, muon_variant variant,
@@ -916,7 +1228,7 @@ muon_status muon_step(const muon_param *params, int n, float lr, float mu, float
       m.rows = (int32_t)params[i].rows;
       m.cols = (int32_t)params[i].cols;
       m.gamma = params[i].gamma;
-      m.desc_idx = plan.K > 0 ? plan.classes[plan.cls_of[i]].desc_base + plan.idx_in_cls[i] : -1;
+      m.desc_idx = has_products(plan) ? plan.classes[plan.cls_of[i]].desc_base + plan.idx_in_cls[i] : -1;
       blocks += plan.e1_blocks[i];
       {
         // G read, M read+write; MONA: A read+write, G_prev written (and read
@@ -1009,9 +1321,13 @@ muon_status muon_step(const muon_param *params, int n, float lr, float mu, float
     HIP_TRY(tr.close());
   }
 
-  // ---- Newton-Schulz
+  // ---- Newton-Schulz (or LiMuon's randomized SVD)
   NsResult res{0, sx0};
-  if (plan.K > 0) {
+  if (is_limuon(plan)) {
+    st = run_limuon(plan, ws, tr, lr, lambda);
+    if (st != MUON_OK) return st;
+    HIP_TRY(tr.close());
+  } else if (plan.K > 0) {
     st = (variant == MUON_NS_DIRECT) ? run_direct(plan, ws, tr, sx0, lr, lambda, res)
                                      : run_gram(plan, ws, tr, sx0, lr, lambda, res);
     if (st != MUON_OK) return st;
@@ -1020,7 +1336,7 @@ muon_status muon_step(const muon_param *params, int n, float lr, float mu, float
 
   // ---- E3: only without Newton-Schulz steps (O = X0); otherwise the last
   // product applied the update in its epilogue
-  if (plan.K == 0) {
+  if (!has_products(plan)) {
     E3Args a;
     std::memset(&a, 0, sizeof(a));
     for (int j = 0; j < kE3MaxMats; ++j) a.begin[j] = INT32_MAX;

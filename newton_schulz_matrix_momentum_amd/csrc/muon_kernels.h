@@ -242,6 +242,80 @@ struct AdamArgs {
   AdamTensor t[kAdamMaxTensors];
 };
 
+// ------------------------------------------------------------------ LiMuon
+// Small-matrix stages of the randomized-SVD orthogonaliser: the sketch
+// width k + p is padded to kLmKP; panels are fp32 [rows x kLmKP] row-major.
+constexpr int kLmKP = 64;             // padded sketch width (k + p <= 64)
+constexpr int kLmChunk = 256;         // panel rows per Gram partial
+constexpr int kLmMaxClasses = 8;
+constexpr int kLmSlot = kLmKP * kLmKP;   // doubles per partial / per small matrix
+
+// Gram partials G_c = sum over rows of chunk c of p_row^T p_row (fp64),
+// first n columns only; one block per (matrix, chunk).
+struct LmGramClass {
+  const float *panel;      // first matrix's panel
+  int64_t stride;          // elements between matrices' panels
+  int32_t rows;            // rows summed (the true rows of the panel)
+  int32_t nchunks;         // ceil(rows / kLmChunk)
+  int32_t count;           // matrices
+  int32_t part_base;       // first partial slot of the class
+};
+struct LmGramArgs {
+  int32_t nclass;
+  int32_t n;                             // columns used (k + p)
+  int32_t block_begin[kLmMaxClasses];    // first block of each class; unused = INT32_MAX
+  double *partials;                      // workspace, kLmSlot doubles per slot
+  LmGramClass cls[kLmMaxClasses];
+};
+
+// Symmetric eigen-decomposition (fp64 Jacobi) of the sum of a matrix's Gram
+// partials, one block per matrix, writing a kLmKP x kLmKP fp32 result:
+//   kLmOrth:  W^T with W = V_r D_r^{-1/2} over eigenvalues > cutoff * d_max
+//             (P W has orthonormal columns spanning the panel's range)
+//   kLmTrunc: T = V_k D_k^{-1/2} V_k^T over the `rank` largest eigenvalues
+//             that exceed cutoff * d_max
+enum LmEigMode : int32_t { kLmOrth = 0, kLmTrunc = 1 };
+struct LmEigClass {
+  float *out;              // first matrix's kLmKP x kLmKP result
+  int64_t out_stride;      // elements between matrices' results
+  int32_t count;
+  int32_t nchunks;
+  int32_t part_base;
+  int32_t pad;
+};
+struct LmEigArgs {
+  int32_t nclass;
+  int32_t n;
+  int32_t mode;
+  int32_t rank;
+  double cutoff;                         // relative to the largest eigenvalue
+  int32_t begin[kLmMaxClasses];          // first block (matrix) of each class
+  const double *partials;
+  LmEigClass cls[kLmMaxClasses];
+};
+
+// Copy the caller's test matrix (kp rows of the long-side length, row
+// stride ld) into each class's zero-padded [kLmKP x lp] buffer.
+struct LmPadClass {
+  float *dst;
+  int32_t l, lp;           // true and padded long side
+  int32_t blocks;          // blocks of this class
+  int32_t pad;
+};
+struct LmPadArgs {
+  const float *src;
+  int64_t ld;
+  int32_t kp;
+  int32_t nclass;
+  int32_t begin[kLmMaxClasses];
+  LmPadClass cls[kLmMaxClasses];
+};
+constexpr int kLmPadElems = 4096;     // padded elements per pad block
+
+hipError_t launch_lm_gram(const LmGramArgs &args, int blocks, hipStream_t s);
+hipError_t launch_lm_eig(const LmEigArgs &args, int blocks, hipStream_t s);
+hipError_t launch_lm_pad(const LmPadArgs &args, int blocks, hipStream_t s);
+
 // Record `msg` as the calling thread's muon_last_error() and return `s`.
 muon_status record_error(muon_status s, const char *msg);
 

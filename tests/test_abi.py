@@ -49,6 +49,9 @@ int main(void) {
          offsetof(muon_options, divisor), offsetof(muon_options, step), offsetof(muon_options, trace),
          sizeof(muon_trace), offsetof(muon_trace, capacity), offsetof(muon_trace, group),
          offsetof(muon_trace, launches), offsetof(muon_param, mona_lite));
+  printf("%zu %zu %zu %zu %zu %zu\n", offsetof(muon_options, sketch), offsetof(muon_options, sketch_ld),
+         offsetof(muon_options, rank), offsetof(muon_options, oversample), offsetof(muon_options, power_iters),
+         offsetof(muon_options, rcond));
   return 0;
 }
 ''')
@@ -59,7 +62,9 @@ int main(void) {
     want = [ctypes.sizeof(P), P.grad.offset, P.prev_grad.offset, P.rows.offset, P.gamma.offset, P.ortho_out.offset,
             ctypes.sizeof(O), O.coeffs.offset, O.divisor.offset, O.step.offset, O.trace.offset,
             ctypes.sizeof(_lib.MuonTrace), _lib.MuonTrace.capacity.offset, _lib.MuonTrace.group.offset,
-            _lib.MuonTrace.launches.offset, P.mona_lite.offset]
+            _lib.MuonTrace.launches.offset, P.mona_lite.offset,
+            O.sketch.offset, O.sketch_ld.offset, O.rank.offset, O.oversample.offset, O.power_iters.offset,
+            O.rcond.offset]
     assert got == want
 
 
@@ -173,6 +178,34 @@ def test_overlap_rejected(lib):
     b.grad = a.grad                  # two params sharing a gradient
     assert step(lib, [a, b]) == E
     assert "overlap" in _lib.last_error()
+
+
+def test_limuon_argument_checks(lib):
+    """MUON_LIMUON: every setting is checked before anything would run."""
+    E, U = _lib.MUON_ERR_INVALID_ARG, _lib.MUON_ERR_UNSUPPORTED
+    L = _lib.MUON_LIMUON
+    sk = BASE * 3
+    good = dict(sketch=sk, sketch_ld=16, rank=4, oversample=4)
+    ws = lib.muon_workspace_size(arr(param(0)), 1, 5, L, ctypes.byref(opts(lib, **good)))
+    assert ws > 0, _lib.last_error()
+    assert lib.muon_workspace_size(arr(param(0)), 1, 5, L, ctypes.byref(opts(lib, **dict(good, rank=0)))) == 0
+    assert step(lib, [param(0)], variant=L, o=opts(lib, **dict(good, sketch=None))) == E
+    assert "sketch" in _lib.last_error()
+    assert step(lib, [param(0)], variant=L, o=opts(lib, **dict(good, rank=0))) == E
+    assert step(lib, [param(0)], variant=L, o=opts(lib, **dict(good, oversample=-1))) == E
+    assert step(lib, [param(0)], variant=L, o=opts(lib, **dict(good, rank=40, oversample=25))) == E
+    assert "64" in _lib.last_error()
+    assert step(lib, [param(0)], variant=L, o=opts(lib, **dict(good, power_iters=17))) == E
+    assert step(lib, [param(0)], variant=L, o=opts(lib, **dict(good, rcond=1.0))) == E
+    assert step(lib, [param(0)], variant=L, o=opts(lib, **dict(good, rcond=float("nan")))) == E
+    assert step(lib, [param(0)], variant=L, o=opts(lib, **dict(good, sketch_ld=15))) == E   # long side 16
+    assert "sketch_ld" in _lib.last_error()
+    p = param(0)
+    assert step(lib, [p], variant=L, o=opts(lib, **dict(good, sketch=p.weight + 64))) == E   # inside W
+    assert "overlap" in _lib.last_error()
+    assert step(lib, [param(0)], variant=L, o=opts(lib, **dict(good, ns_dtype=_lib.MUON_BF16))) == U
+    # the LiMuon settings are ignored by the Newton-Schulz variants
+    assert lib.muon_workspace_size(arr(param(0)), 1, 5, 0, ctypes.byref(opts(lib, rank=0, sketch=None))) > 0
 
 
 def test_workspace_size_and_too_small(lib):

@@ -14,8 +14,8 @@ import pytest
 import torch
 
 import oracle
-from helpers import check_close, rel_fro, to64, tol_for, TOL_STATE
-from workloads import WORKLOADS, make_grads, make_state
+from helpers import check_close, dw_discounted, rel_fro, sketch_for, to64, tol_for, TOL_STATE
+from workloads import WORKLOADS, make_grads, make_state, workload_sketch
 
 pytestmark = pytest.mark.gpu
 
@@ -49,7 +49,8 @@ def _run_workload(name, variant, lite=False):
         params[i]["ortho_out"] = torch.empty_like(params[i]["weight"])
     divisor, restart = w.settings_for(variant)
     coeffs = oracle.coefficient_table(w.coeffs, w.ns_steps)
-    tol = tol_for(w.ns_dtype)
+    ns_dtype = w.ns_dtype_for(variant)
+    tol = tol_for(ns_dtype)
     snaps = {i: {k: to64(v) for k, v in params[i].items() if k != "ortho_out"} for i in sample}
     rng = np.random.default_rng(7)
     for step in range(w.steps):
@@ -64,9 +65,14 @@ def _run_workload(name, variant, lite=False):
             probes.append((i, pos, {k: p[k].flatten()[pos].double().cpu().numpy()
                                     for k in ("grad", "momentum", "accel", "prev_grad", "mona_lite") if k in p}))
         w_gpu_before = {i: to64(params[i]["weight"]) for i in sample}
+        lm, lm_ref = {}, {}
+        if variant == "limuon":
+            sketch = workload_sketch(w, step).to(dev)
+            lm = dict(sketch=sketch, **w.limuon_settings())
+            lm_ref = dict(rank=lm["rank"], power_iters=lm["power_iters"], rcond=float(np.float32(1e-4)))
         nsm.muon_step(params, lr=w.lr, mu=w.mu, beta_a=w.beta_a, alpha=w.alpha, weight_decay=w.weight_decay,
-                      ns_steps=w.ns_steps, variant=variant, ns_dtype=w.ns_dtype, coeffs=coeffs.tolist(),
-                      divisor=divisor, restart_every=restart, step=step)
+                      ns_steps=w.ns_steps, variant=variant, ns_dtype=ns_dtype, coeffs=coeffs.tolist(),
+                      divisor=divisor, restart_every=restart, step=step, **lm)
         torch.cuda.synchronize()
         for i, pos, before in probes:
             p = params[i]
@@ -94,11 +100,13 @@ def _run_workload(name, variant, lite=False):
         for i in sample:
             s = snaps[i]
             g = to64(params[i]["grad"])
+            if variant == "limuon":
+                lm_ref["omega"] = sketch_for(lm["sketch"], w.shapes[i])
             ref = oracle.muon_step_matrix(s["weight"], g, s["momentum"], lr=w.lr, mu=w.mu,
                                           weight_decay=w.weight_decay, coeffs=coeffs, variant=variant,
                                           divisor=divisor, restart_every=restart, accel=s.get("accel"),
                                           prev_grad=s.get("prev_grad"), lite_state=s.get("mona_lite"),
-                                          beta_a=w.beta_a, alpha=w.alpha, step=step)
+                                          beta_a=w.beta_a, alpha=w.alpha, step=step, **lm_ref)
             p = params[i]
             assert rel_fro(to64(p["momentum"]), ref["momentum"]) <= TOL_STATE
             if "accel" in p:
@@ -108,7 +116,9 @@ def _run_workload(name, variant, lite=False):
                   % (what, rel_fro(to64(p["ortho_out"]), ref["ortho"]),
                      rel_fro(to64(p["weight"]) - w_gpu_before[i], ref["weight"] - s["weight"]), tol), flush=True)
             check_close(to64(p["ortho_out"]), ref["ortho"], tol, what + ": O")
-            check_close(to64(p["weight"]) - w_gpu_before[i], ref["weight"] - s["weight"], tol, what + ": dW")
+            dw_ref = ref["weight"] - s["weight"]
+            check_close(dw_discounted(to64(p["weight"]) - w_gpu_before[i], dw_ref, ref["weight"]), dw_ref, tol,
+                        what + ": dW")
             # carry the oracle's own state forward (never the GPU's)
             s["weight"], s["momentum"] = ref["weight"], ref["momentum"]
             if "prev_grad" in ref:
@@ -127,6 +137,10 @@ def test_full_nanochat_6l_d192():
 
 def test_full_llama430m_24l_d1024():
     _run_workload("llama430m_24l_d1024", "direct")
+
+
+def test_full_llama430m_24l_d1024_limuon():
+    _run_workload("llama430m_24l_d1024", "limuon")
 
 
 def test_full_llama430m_24l_d1024_mona_lite():

@@ -3,7 +3,7 @@ localized error that the per-matrix relative Frobenius bound lets through."""
 import numpy as np
 import pytest
 
-from helpers import BLOCK_FACTOR, TOL_16, block_errors, check_close, rel_fro
+from helpers import BLOCK_FACTOR, TOL_16, block_errors, check_close, dw_discounted, rel_fro
 
 
 def _orthogonal(n, seed):
@@ -66,3 +66,20 @@ def test_block_errors_ragged_edges_and_units():
     assert b[1, 2] == pytest.approx(2.0)  # rms error 2 in units of rms(ref) = 1
     assert np.count_nonzero(b) == 1
     assert BLOCK_FACTOR * TOL_16 < 2.0
+
+
+def test_dw_discount_covers_only_the_fp32_store():
+    """The dW check forgives the fp32 rounding of W_new and nothing more: a
+    correctly rounded W_new passes at any update size, an update off by
+    1e-4 of itself still fails."""
+    rng = np.random.default_rng(9)
+    w_old = (0.02 * rng.standard_normal((512, 512))).astype(np.float32).astype(np.float64)
+    o = 1e-3 * rng.standard_normal((512, 512))          # tiny update (low-rank O scale)
+    w_ref = w_old - 0.02 * (o + 0.01 * w_old)           # exact (fp64)
+    w_gpu = w_ref.astype(np.float32).astype(np.float64)   # stored in fp32
+    dw_ref, dw_gpu = w_ref - w_old, w_gpu - w_old
+    assert rel_fro(dw_gpu, dw_ref) > 1e-5                 # the storage floor alone
+    check_close(dw_discounted(dw_gpu, dw_ref, w_ref), dw_ref, 1e-5, "stored W_new")
+    off = w_old + (1.0 + 1e-4) * dw_ref
+    with pytest.raises(AssertionError):
+        check_close(dw_discounted(off - w_old, dw_ref, w_ref), dw_ref, 1e-5, "wrong update")

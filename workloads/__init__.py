@@ -9,5 +9,7 @@ from .inputs import (  # noqa: F401
     Workload,
     make_state,
     make_grads,
+    make_sketch,
     seed_for,
+    workload_sketch,
 )

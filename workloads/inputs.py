@@ -63,6 +63,15 @@ class Workload:
             return self.divisor, self.restart_every
         return self.extra.get("direct_divisor", 1.0), self.extra.get("direct_restart_every", 0)
 
+    def ns_dtype_for(self, variant: str) -> str:
+        """Operand dtype of the orthogonaliser's products (LiMuon: fp32)."""
+        return "f32" if variant == "limuon" else self.ns_dtype
+
+    def limuon_settings(self) -> dict:
+        """rank, oversample and power_iters of the LiMuon variant."""
+        return {"rank": self.extra.get("limuon_rank", 8), "oversample": self.extra.get("limuon_oversample", 8),
+                "power_iters": self.extra.get("limuon_power_iters", 1)}
+
 
 def seed_for(workload_index: int, matrix_index: int, step: int) -> int:
     return 1000 * workload_index + 10 * matrix_index + step
@@ -133,6 +142,22 @@ def make_grads(w: Workload, step: int, device="cpu", shapes=None) -> List[torch.
     return out
 
 
+def make_sketch(kp: int, cols: int, seed: int, device="cpu") -> torch.Tensor:
+    """Gaussian test matrix for the LiMuon variant: kp rows of ``cols``
+    N(0, 1) values (one test vector per row), drawn in float64 and rounded
+    once to float32."""
+    g = torch.randn(kp, cols, generator=_gen(seed, device), dtype=torch.float64, device=device)
+    return g.to(torch.float32)
+
+
+def workload_sketch(w: Workload, step: int, device="cpu") -> torch.Tensor:
+    """The test matrix of optimizer step ``step`` for workload ``w``: wide
+    enough for its longest side, seeded per step."""
+    st = w.limuon_settings()
+    lmax = max(max(r, c) for r, c in w.shapes)
+    return make_sketch(st["rank"] + st["oversample"], lmax, seed_for(w.index + 700, 0, step), device)
+
+
 def make_state(w: Workload, device="cpu", shapes=None, mona=None):
     """Initial optimizer state: W ~ N(0, 0.02^2) fp32, M = 0 (fp32), and for
     MONA A = 0 (fp32) and a previous-gradient buffer (grad dtype, zeros), or
@@ -196,8 +221,10 @@ WORKLOADS = {
     "llama430m_24l_d1024": Workload(
         name="llama430m_24l_d1024", index=3, shapes=_llama_shapes(), grad_dtype="bf16", ns_dtype="bf16",
         grad_kind="spike", grad_std=1e-2, spike_rank=8, coeffs="quintic", ns_steps=5,
-        mona=True, beta_a=0.9, alpha=0.5, steps=2,
-        note="Llama-430M-style 24 layers d=1024 ff=2816; bf16 N(0,1e-2^2) + rank-8 spike; MONA, 2 steps"),
+        variants=("direct", "limuon"), mona=True, beta_a=0.9, alpha=0.5, steps=2,
+        extra={"limuon_rank": 8, "limuon_oversample": 8, "limuon_power_iters": 1},
+        note="Llama-430M-style 24 layers d=1024 ff=2816; bf16 N(0,1e-2^2) + rank-8 spike; MONA, 2 steps; "
+             "direct NS (bf16) or LiMuon (rank 8, oversampling 8, one power iteration, fp32)"),
     "gram_tall_32x4096x16384": Workload(
         name="gram_tall_32x4096x16384", index=4, shapes=[(4096, 16384)] * 16 + [(16384, 4096)] * 16,
         grad_dtype="f16", ns_dtype="f16", grad_kind="spectral", log10_sv=(-5.0, 0.0),
