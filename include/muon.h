@@ -246,6 +246,24 @@ muon_status muon_adamw_step(const muon_adamw_param *params, int n, muon_dtype gr
                             float lr, float beta1, float beta2, float eps, float weight_decay,
                             int64_t step, muon_trace *trace, void *stream);
 
+/* Where one square Newton-Schulz work buffer of param `index` lives in the
+ * workspace of the call described by the same (params, n, ns_steps,
+ * variant, opts) as muon_workspace_size -- for tests and debugging, e.g.
+ * checking that symmetric results (computed on upper-triangular tiles and
+ * mirrored: Gram Newton-Schulz post, "half the elements") are stored exactly
+ * symmetric.  which: 0..1 for MUON_NS_DIRECT (A = X X^T, B = b A + c A^2),
+ * 0..4 for MUON_NS_GRAM (the R, T, P, Q buffers, rotated between steps).
+ * After a muon_step the buffer holds the last value the schedule wrote
+ * there, stored in ns_dtype (fp16 multiplied by a power-of-two storage
+ * scale), side x side, padded to ld x ld with zeros.  Writes *offset
+ * (bytes), *ld and *side (elements).  Errors: MUON_ERR_INVALID_ARG for an
+ * invalid call, index or which (LiMuon has no square buffers), NULL
+ * outputs. */
+muon_status muon_debug_square_buffer(const muon_param *params, int n, int ns_steps,
+                                     muon_variant variant, const muon_options *opts,
+                                     int index, int which,
+                                     size_t *offset, int64_t *ld, int64_t *side);
+
 /* Static description of a status code. */
 const char *muon_status_string(muon_status s);
 

@@ -26,7 +26,7 @@ MUON_NS_DIRECT, MUON_NS_GRAM, MUON_LIMUON = 0, 1, 2
 
 # every entry point declared in include/muon.h
 EXPORTS = ("muon_options_init", "muon_workspace_size", "muon_step", "muon_step_static", "muon_adamw_step",
-           "muon_status_string", "muon_last_error", "muon_version")
+           "muon_debug_square_buffer", "muon_status_string", "muon_last_error", "muon_version")
 # bytes of the static workspace of muon_step_static (MUON_STATIC_WORKSPACE_BYTES)
 STATIC_WORKSPACE_BYTES = 64 << 20
 
@@ -130,6 +130,11 @@ def load(path: str = LIB_PATH):
                                     ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_float,
                                     ctypes.c_int64, ctypes.POINTER(MuonTrace), ctypes.c_void_p]
     lib.muon_adamw_step.restype = ctypes.c_int
+    lib.muon_debug_square_buffer.argtypes = [ctypes.POINTER(MuonParam), ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                             ctypes.POINTER(MuonOptions), ctypes.c_int, ctypes.c_int,
+                                             ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_int64),
+                                             ctypes.POINTER(ctypes.c_int64)]
+    lib.muon_debug_square_buffer.restype = ctypes.c_int
     lib.muon_status_string.argtypes = [ctypes.c_int]
     lib.muon_status_string.restype = ctypes.c_char_p
     lib.muon_last_error.argtypes = []

@@ -126,6 +126,20 @@ def muon_workspace_size(params: Sequence[Dict], *, ns_steps: int = 5, variant: s
     return int(size)
 
 
+def debug_square_buffer(params: Sequence[Dict], index: int, which: int, *, ns_steps: int = 5,
+                        variant: str = "direct", ns_dtype=None, coeffs=None, divisor: float = 1.0,
+                        restart_every: int = 0, step: int = 0):
+    """(byte offset, leading dimension, side) of square work buffer ``which``
+    of param ``index`` in the workspace of the described call
+    (``muon_debug_square_buffer``)."""
+    arr, n, opts, keep, _ = _marshal(params, ns_dtype, coeffs, divisor, restart_every, step)
+    off, ld, side = ctypes.c_size_t(), ctypes.c_int64(), ctypes.c_int64()
+    _lib.check(_lib.load().muon_debug_square_buffer(arr, n, int(ns_steps), _VARIANTS[variant], ctypes.byref(opts),
+                                                    int(index), int(which), ctypes.byref(off), ctypes.byref(ld),
+                                                    ctypes.byref(side)))
+    return off.value, ld.value, side.value
+
+
 class Workspace:
     """A reusable device byte buffer for ``muon_step`` (grows on demand).
 

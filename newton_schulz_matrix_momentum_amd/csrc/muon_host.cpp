@@ -1154,6 +1154,25 @@ size_t muon_workspace_size(const muon_param *params, int n, int ns_steps, muon_v
   return plan.total;
 }
 
+muon_status muon_debug_square_buffer(const muon_param *params, int n, int ns_steps, muon_variant variant,
+                                     const muon_options *opts, int index, int which, size_t *offset, int64_t *ld,
+                                     int64_t *side) {
+  if (!offset || !ld || !side) return fail(MUON_ERR_INVALID_ARG, "offset, ld and side must be non-NULL");
+  Plan plan;
+  muon_status st = build_plan(params, n, ns_steps, variant, opts, plan);
+  if (st != MUON_OK) return st;
+  if (index < 0 || index >= n) return fail(MUON_ERR_INVALID_ARG, "index %d out of [0, %d)", index, n);
+  const int nsq = variant == MUON_NS_DIRECT ? 2 : variant == MUON_NS_GRAM ? 5 : 0;
+  if (which < 0 || which >= nsq) return fail(MUON_ERR_INVALID_ARG, "which %d out of [0, %d)", which, nsq);
+  const ClassInfo &cl = plan.classes[plan.cls_of[index]];
+  const size_t es = (size_t)elem_size(plan.set.ns_dtype);
+  *offset = cl.sq[which] + (size_t)plan.idx_in_cls[index] * (size_t)cl.Sp * (size_t)cl.Sp * es;
+  *ld = cl.Sp;
+  *side = cl.s;
+  g_last_error.clear();
+  return MUON_OK;
+}
+
 muon_status muon_step(const muon_param *params, int n, float lr, float mu, float beta_a, float alpha, float lambda,
                       int ns_steps, muon_variant variant, const muon_options *opts, void *workspace,
                       size_t workspace_bytes, void *stream) {

@@ -98,6 +98,18 @@ def test_f16_ns(variant):
              divisor=1.03, restart_every=3)
 
 
+@pytest.mark.parametrize("variant,ns_dtype", [("direct", "bf16"), ("gram", "f16"), ("direct", "f16")])
+def test_128_tile_classes_next_to_256_tile_classes(variant, ns_dtype):
+    """Short sides that pad well to 128 tiles but not to 256 (1408 as in the
+    MoE experts, 1664, 640) next to a 256-tile class (1024): both
+    orientations, ragged long sides (1900), two matrices of one class, over
+    two MONA steps."""
+    shapes = [(1408, 2048), (2048, 1408), (1664, 1900), (1900, 1664), (1024, 1024), (640, 1280), (1408, 2048)]
+    run_case(shapes, grad_dtype="bf16", ns_dtype=ns_dtype, variant=variant, grad_kind="spectral", seed=17,
+             mona=True, steps=2, divisor=1.03 if variant == "gram" else 1.0,
+             restart_every=3 if variant == "gram" else 0)
+
+
 @pytest.mark.parametrize("ns_dtype", ["bf16", "f16"])
 def test_fused_square_update_groups(ns_dtype):
     """Short sides <= 192 form B = b A + c A^2 inside the update launch, each
