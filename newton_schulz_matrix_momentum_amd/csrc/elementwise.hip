@@ -71,6 +71,41 @@ template <int DT> struct Vec4Half {
 template <> struct Vec4<kBF16> : Vec4Half<kBF16> {};
 template <> struct Vec4<kF16> : Vec4Half<kF16> {};
 
+// Streaming accesses (`nt`: non-temporal loads and stores) for calls whose
+// state is far larger than the caches: measured on MI355X, a non-temporal
+// read stream sustains about 7.1 TB/s against 6.4 for a plain one, and E1
+// runs 7-11% faster on the Llama-shaped and tall-matrix sets; a call whose
+// momentum fits in the caches keeps plain accesses (E2 re-reads M from
+// cache there).  The choice is a template parameter of the kernels.
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+// Loads and stores of clang vector types (the non-temporal builtins keep
+// their hint on these; through HIP's float4 / uint2 structs it was lost).
+template <bool NT, typename V> __device__ __forceinline__ V ld(const void *p) {
+  if (NT) return __builtin_nontemporal_load((const V *)p);
+  return *(const V *)p;
+}
+template <bool NT, typename V> __device__ __forceinline__ void st(void *p, V v) {
+  if (NT) __builtin_nontemporal_store(v, (V *)p);
+  else *(V *)p = v;
+}
+// four gradient (or previous-gradient) elements: 16 bytes of fp32 or 8 bytes
+// of a 16-bit dtype
+template <int DT> struct GV {
+  typedef u32x2v type;
+  static __device__ __forceinline__ void unpack(type v, float o[4]) {
+    o[0] = Elem<DT>::to_f32((uint16_t)(v.x & 0xffffu));
+    o[1] = Elem<DT>::to_f32((uint16_t)(v.x >> 16));
+    o[2] = Elem<DT>::to_f32((uint16_t)(v.y & 0xffffu));
+    o[3] = Elem<DT>::to_f32((uint16_t)(v.y >> 16));
+  }
+};
+template <> struct GV<kF32> {
+  typedef f32x4v type;
+  static __device__ __forceinline__ void unpack(type v, float o[4]) { o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w; }
+};
+
 __device__ __forceinline__ double wave_sum(double v) {
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
   return v;
@@ -105,7 +140,7 @@ __device__ __forceinline__ void e1_elem(float g, float &m, float &s, float prev,
   m = args.mu * m + g;
 }
 
-template <int GDT, int MODE>
+template <int GDT, int MODE, bool NT>
 __global__ __launch_bounds__(kE1Threads) void e1_kernel(E1Args args) {
   typedef typename Elem<GDT>::raw graw;
   typedef typename Vec4<GDT>::type gvec;
@@ -138,20 +173,21 @@ __global__ __launch_bounds__(kE1Threads) void e1_kernel(E1Args args) {
   if (vec_ok) {
     // Groups of 4 elements, predicated on lying inside the matrix; every load
     // of the thread is issued before the first use (no serial tail loop).
-    gvec gv[G], pv[G];
-    float4 mv[G], av[G];
-    uint2 lv[G];
+    typedef typename GV<GDT>::type gx;
+    gx gv[G], pv[G];
+    f32x4v mv[G], av[G];
+    u32x2v lv[G];
 #pragma unroll
     for (int it = 0; it < G; ++it) {
       const int64_t e = base + ((int64_t)it * kE1Threads + threadIdx.x) * 4;
       if (e + 4 <= numel) {
-        gv[it] = *(const gvec *)(grad + e);
-        mv[it] = *(const float4 *)(mom + e);
+        gv[it] = ld<NT, gx>(grad + e);
+        mv[it] = ld<NT, f32x4v>(mom + e);
         if (MONA) {
-          av[it] = *(const float4 *)(acc + e);
-          if (!args.first_step) pv[it] = *(const gvec *)(prev + e);
+          av[it] = ld<NT, f32x4v>(acc + e);
+          if (!args.first_step) pv[it] = ld<NT, gx>(prev + e);
         }
-        if (LITE && !args.first_step) lv[it] = *(const uint2 *)(lite + e);
+        if (LITE && !args.first_step) lv[it] = ld<NT, u32x2v>(lite + e);
       }
     }
 #pragma unroll
@@ -159,23 +195,23 @@ __global__ __launch_bounds__(kE1Threads) void e1_kernel(E1Args args) {
       const int64_t e = base + ((int64_t)it * kE1Threads + threadIdx.x) * 4;
       if (e + 4 <= numel) {
         float g[4], m[4] = {mv[it].x, mv[it].y, mv[it].z, mv[it].w}, a[4] = {0, 0, 0, 0}, p[4] = {0, 0, 0, 0};
-        Vec4<GDT>::unpack(gv[it], g);
+        GV<GDT>::unpack(gv[it], g);
         if (MONA) {
           a[0] = av[it].x; a[1] = av[it].y; a[2] = av[it].z; a[3] = av[it].w;
-          if (!args.first_step) Vec4<GDT>::unpack(pv[it], p);
+          if (!args.first_step) GV<GDT>::unpack(pv[it], p);
         }
-        if (LITE && !args.first_step) Vec4<kBF16>::unpack(lv[it], a);
+        if (LITE && !args.first_step) GV<kBF16>::unpack(lv[it], a);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           e1_elem<MODE>(g[q], m[q], a[q], p[q], args);
           sq += m[q] * m[q];
         }
-        *(float4 *)(mom + e) = make_float4(m[0], m[1], m[2], m[3]);
+        st<NT, f32x4v>(mom + e, f32x4v{m[0], m[1], m[2], m[3]});
         if (MONA) {
-          *(float4 *)(acc + e) = make_float4(a[0], a[1], a[2], a[3]);
-          *(gvec *)(prev + e) = gv[it];  // exact copy of the stored gradient
+          st<NT, f32x4v>(acc + e, f32x4v{a[0], a[1], a[2], a[3]});
+          st<NT, gx>(prev + e, gv[it]);  // exact copy of the stored gradient
         }
-        if (LITE) *(uint2 *)(lite + e) = Vec4<kBF16>::pack(a);
+        if (LITE) st<NT, u32x2v>(lite + e, __builtin_bit_cast(u32x2v, Vec4<kBF16>::pack(a)));
       } else if (e < numel) {
         // the matrix's last numel % 4 elements
         for (int64_t j = e; j < numel; ++j) {
@@ -250,6 +286,36 @@ __global__ __launch_bounds__(256) void norm_kernel(NormArgs args) {
 }
 
 // ------------------------------------------------------------------ E2
+// Per-matrix scale: reduced here from few partials (the same fixed order in
+// every block of the matrix: one partial per lane, fp64 butterfly), else
+// read from norm_kernel's output.
+__device__ __forceinline__ float e2_scale(const E2Args &args, const E2Mat &mt) {
+  if (mt.nparts > 0) {
+    __shared__ float sh_scale;
+    if (threadIdx.x < 64) {
+      double p = ((int)threadIdx.x < mt.nparts) ? args.partials[mt.partial_off + threadIdx.x] : 0.0;
+      p = wave_sum(p);
+      if (threadIdx.x == 0) {
+        // zero matrix => X0 = 0 (no epsilon); Inf/NaN propagate
+        const double sc = (p == 0.0) ? 0.0 : (double)args.inv_sqrt_d / sqrt(p);
+        sh_scale = (float)(sc * (double)args.store_scale);
+      }
+    }
+    __syncthreads();
+    return sh_scale;
+  }
+  return args.scales[mt.scale_idx];
+}
+
+// fp32 X0: 64 x 64 tiles, each thread 4 rows x 4 columns (16-byte loads and
+// stores in both orientations).
+// E2's loads of M stay plain by default: measured on the large sets,
+// non-temporal loads made E2 15-20% slower (M was just written by E1).  X0's
+// stores stay plain too: the first product reads X0 right away.
+#ifndef MUON_E2_NT_LOADS
+#define MUON_E2_NT_LOADS 0
+#endif
+
 template <int NDT>
 __global__ __launch_bounds__(256) void e2_kernel(E2Args args) {
   typedef typename Elem<NDT>::raw nraw;
@@ -284,25 +350,7 @@ __global__ __launch_bounds__(256) void e2_kernel(E2Args args) {
       }
     }
   }
-  float scale;
-  if (mt.nparts > 0) {
-    // few partials: reduce them here, in the same fixed order in every block
-    // of the matrix (one partial per lane, fp64 butterfly)
-    __shared__ float sh_scale;
-    if (threadIdx.x < 64) {
-      double p = ((int)threadIdx.x < mt.nparts) ? args.partials[mt.partial_off + threadIdx.x] : 0.0;
-      p = wave_sum(p);
-      if (threadIdx.x == 0) {
-        // zero matrix => X0 = 0 (no epsilon); Inf/NaN propagate
-        const double sc = (p == 0.0) ? 0.0 : (double)args.inv_sqrt_d / sqrt(p);
-        sh_scale = (float)(sc * (double)args.store_scale);
-      }
-    }
-    __syncthreads();
-    scale = sh_scale;
-  } else {
-    scale = args.scales[mt.scale_idx];
-  }
+  const float scale = e2_scale(args, mt);
   nraw *nat = (nraw *)mt.nat;
   nraw *trn = (nraw *)mt.trn;
 #pragma unroll
@@ -327,6 +375,72 @@ __global__ __launch_bounds__(256) void e2_kernel(E2Args args) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) o[q] = tile[cg + q][tcol];
     *(nvec *)(trn + (int64_t)(c0 + tcol) * mt.ld_trn + r0 + cg) = Vec4<NDT>::pack(o);
+  }
+}
+
+
+// 16-bit X0: 64 x 64 tiles.  Each thread loads 4 rows x 4 columns of M (16
+// threads cover a row's 256 bytes), rounds them once and leaves them in LDS;
+// then both layouts are written from LDS as 16-byte vectors of 8 values, 8
+// threads per 128-byte line: rows of X0 (row-major) and rows of X0^T
+// (columns of the tile).
+__device__ __forceinline__ void store16(void *p, u32x4v v) { *(u32x4v *)p = v; }
+
+template <int NDT, bool NT>
+__global__ __launch_bounds__(256) void e2_kernel16(E2Args args) {
+  __shared__ float tile[kE2Tile][kE2Tile + 1];
+  const int b = blockIdx.x;
+  const int mi = find_mat(args.begin, b);
+  const E2Mat &mt = args.mats[mi];
+  const int t = b - args.begin[mi];
+  const int tr = t / mt.tiles_c, tc = t - tr * mt.tiles_c;
+  const int r0 = tr * kE2Tile, c0 = tc * kE2Tile;
+  const int cg = (threadIdx.x & 15) * 4;   // column group within the tile
+  const int rr = threadIdx.x >> 4;         // 0..15
+  const bool vec_ok = ((mt.cols & 3) == 0) && ((((uintptr_t)mt.mom) & 15) == 0);
+  float v[4][4];
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int r = r0 + rr + 16 * it;
+    const int c = c0 + cg;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[it][q] = 0.f;
+    if (r < mt.rows) {
+      const float *src = mt.mom + (int64_t)r * mt.cols;
+      if (vec_ok && c + 4 <= mt.cols) {
+        const f32x4v x = ld<NT && MUON_E2_NT_LOADS, f32x4v>(src + c);
+        v[it][0] = x.x; v[it][1] = x.y; v[it][2] = x.z; v[it][3] = x.w;
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (c + q < mt.cols) v[it][q] = src[c + q];
+      }
+    }
+  }
+  const float scale = e2_scale(args, mt);
+#pragma unroll
+  for (int it = 0; it < 4; ++it)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)   // round once to the storage dtype; LDS holds the rounded value
+      tile[rr + 16 * it][cg + q] = Elem<NDT>::to_f32(Elem<NDT>::from_f32(v[it][q] * scale));
+  __syncthreads();
+  uint16_t *nat = (uint16_t *)mt.nat;
+  uint16_t *trn = (uint16_t *)mt.trn;
+  const int l8 = threadIdx.x >> 3;          // 0..31: a row (or column) of the tile, per pass
+  const int e8 = (threadIdx.x & 7) * 8;     // first of the 8 values this thread stores
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int line = l8 + 32 * h;
+    uint32_t pn[4], pt[4];
+#pragma unroll
+    for (int q = 0; q < 8; q += 2) {
+      pn[q / 2] = (uint32_t)Elem<NDT>::from_f32(tile[line][e8 + q]) |
+                  ((uint32_t)Elem<NDT>::from_f32(tile[line][e8 + q + 1]) << 16);
+      pt[q / 2] = (uint32_t)Elem<NDT>::from_f32(tile[e8 + q][line]) |
+                  ((uint32_t)Elem<NDT>::from_f32(tile[e8 + q + 1][line]) << 16);
+    }
+    if (nat) store16(nat + (int64_t)(r0 + line) * mt.ld_nat + c0 + e8, u32x4v{pn[0], pn[1], pn[2], pn[3]});
+    if (trn) store16(trn + (int64_t)(c0 + line) * mt.ld_trn + r0 + e8, u32x4v{pt[0], pt[1], pt[2], pt[3]});
   }
 }
 
@@ -455,7 +569,10 @@ __global__ __launch_bounds__(kAdamThreads) void adamw_kernel(AdamArgs args) {
 
 hipError_t launch_e1(const E1Args &args, int blocks, hipStream_t s) {
   const dim3 g(blocks), b(kE1Threads);
-#define MUON_E1(GDT, MODE) hipLaunchKernelGGL((e1_kernel<GDT, MODE>), g, b, 0, s, args); break;
+#define MUON_E1(GDT, MODE)                                                                \
+  if (args.stream) hipLaunchKernelGGL((e1_kernel<GDT, MODE, true>), g, b, 0, s, args);   \
+  else hipLaunchKernelGGL((e1_kernel<GDT, MODE, false>), g, b, 0, s, args);              \
+  break;
   switch (args.grad_dtype * 3 + args.mode) {
     case kF32 * 3 + kE1Plain: MUON_E1(kF32, kE1Plain)
     case kF32 * 3 + kE1Mona: MUON_E1(kF32, kE1Mona)
@@ -480,8 +597,14 @@ hipError_t launch_norm(const NormArgs &args, hipStream_t s) {
 hipError_t launch_e2(const E2Args &args, int blocks, hipStream_t s) {
   switch (args.ns_dtype) {
     case kF32: hipLaunchKernelGGL(e2_kernel<kF32>, dim3(blocks), dim3(256), 0, s, args); break;
-    case kF16: hipLaunchKernelGGL(e2_kernel<kF16>, dim3(blocks), dim3(256), 0, s, args); break;
-    case kBF16: hipLaunchKernelGGL(e2_kernel<kBF16>, dim3(blocks), dim3(256), 0, s, args); break;
+    case kF16:
+      if (args.stream) hipLaunchKernelGGL((e2_kernel16<kF16, true>), dim3(blocks), dim3(256), 0, s, args);
+      else hipLaunchKernelGGL((e2_kernel16<kF16, false>), dim3(blocks), dim3(256), 0, s, args);
+      break;
+    case kBF16:
+      if (args.stream) hipLaunchKernelGGL((e2_kernel16<kBF16, true>), dim3(blocks), dim3(256), 0, s, args);
+      else hipLaunchKernelGGL((e2_kernel16<kBF16, false>), dim3(blocks), dim3(256), 0, s, args);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -1200,6 +1200,11 @@ muon_status muon_step(const muon_param *params, int n, float lr, float mu, float
   Tracer tr{trace, hs};
   const Settings &set = plan.set;
   double *partials = (double *)(ws + plan.off_partials);
+  // Streaming (non-temporal) accesses in E1 / E2 when the call's momentum is
+  // far larger than the device's caches (256 MB of last-level cache).
+  int64_t total_elems = 0;
+  for (int i = 0; i < n; ++i) total_elems += params[i].rows * params[i].cols;
+  const int32_t stream_ew = total_elems * 4 > (int64_t(512) << 20) ? 1 : 0;
   float *scales = (float *)(ws + plan.off_scales);
 
   // ---- E1, launched separately for plain, MONA and MONA-Lite matrices
@@ -1213,6 +1218,7 @@ muon_status muon_step(const muon_param *params, int n, float lr, float mu, float
     a.mu = mu;
     a.beta_a = beta_a;
     a.alpha = alpha;
+    a.stream = stream_ew;
     a.partials = partials;
     a.desc = (FinalDesc *)(ws + plan.off_desc);
     int blocks = 0;
@@ -1300,6 +1306,7 @@ muon_status muon_step(const muon_param *params, int n, float lr, float mu, float
     a.partials = partials;
     a.inv_sqrt_d = (float)(1.0 / std::sqrt(set.divisor));
     a.store_scale = (float)sx0;
+    a.stream = stream_ew;
     int blocks = 0;
     double bytes = 0.0;
     for (int i = 0; i < n; ++i) {

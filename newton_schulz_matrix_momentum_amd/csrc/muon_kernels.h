@@ -57,7 +57,8 @@ struct E1Args {
   int32_t grad_dtype;
   int32_t first_step;    // MONA / MONA-Lite: D = 0
   int32_t mode;          // E1Mode of every matrix of the launch
-  float mu, beta_a, alpha, pad1;
+  float mu, beta_a, alpha;
+  int32_t stream;        // non-temporal loads and stores (state far larger than the caches)
   double *partials;      // workspace
   FinalDesc *desc;       // workspace
   int32_t begin[kE1MaxMats];
@@ -118,6 +119,8 @@ struct E2Args {
   int32_t ns_dtype;
   float inv_sqrt_d;          // inline norm: 1/sqrt(divisor)
   float store_scale;         // inline norm: storage scale of X0
+  int32_t stream;            // non-temporal loads of M (see E1Args::stream)
+  int32_t pad;
   const float *scales;
   const double *partials;
   int32_t begin[kE2MaxMats];   // first tile of each matrix (see E1Args)
