@@ -2,13 +2,13 @@
 //
 // LiMuon (digest "LiMuon: Light and Fast Muon Optimizer for Large Models",
 // section "Метод") replaces Newton-Schulz by a randomized SVD of the
-// momentum.  The large products of that SVD (the sketch X Omega, the power
-// iterations X^T Q and X Z, the projection X^T Q and the final product) run
-// in the grouped MFMA GEMM kernels; what remains are operations on the
-// (k + p)-wide panels, implemented here:
+// momentum.  Its products against (k + p)-wide panels (the sketch X Omega,
+// the power iterations X^T Q and X Z, the projection X^T Q, and the
+// orthonormalising factors) and the small-matrix stages are implemented
+// here; the final product (the weight update) runs in the grouped GEMM:
 //
-//   lm_gram_kernel  fp64 partial Gram matrices P^T P of tall fp32 panels,
-//                   one block per (matrix, chunk of rows)
+//   lm_thin_kernel  the products against a (k + p)-wide panel, with the
+//                   fp64 Gram partials of the result fused in
 //   lm_eig_kernel   one block per matrix: fixed-order sum of its partials,
 //                   cyclic Jacobi eigen-decomposition in fp64 (parallel
 //                   round-robin pair order), then either the orthonormalising
@@ -35,55 +35,133 @@ __device__ __forceinline__ int class_of(const int32_t (&begin)[kLmMaxClasses], i
   return ci;
 }
 
-// ------------------------------------------------------------------ Gram
-constexpr int kGramRows = 64;   // panel rows staged in LDS at a time
+// s_waitcnt vmcnt(n), leaving expcnt and lgkmcnt alone (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14]); n >= 32 waits for everything.
+#define LM_VMCNT(n) (0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
+#define LM_VMCASE(n) case n: __builtin_amdgcn_s_waitcnt(LM_VMCNT(n)); break;
+__device__ __forceinline__ void lm_waitcnt_vm(int n) {
+  switch (n) {
+    LM_VMCASE(1) LM_VMCASE(2) LM_VMCASE(3) LM_VMCASE(4) LM_VMCASE(5) LM_VMCASE(6) LM_VMCASE(7) LM_VMCASE(8)
+    LM_VMCASE(9) LM_VMCASE(10) LM_VMCASE(11) LM_VMCASE(12) LM_VMCASE(13) LM_VMCASE(14) LM_VMCASE(15)
+    LM_VMCASE(16) LM_VMCASE(17) LM_VMCASE(18) LM_VMCASE(19) LM_VMCASE(20) LM_VMCASE(21) LM_VMCASE(22)
+    LM_VMCASE(23) LM_VMCASE(24) LM_VMCASE(25) LM_VMCASE(26) LM_VMCASE(27) LM_VMCASE(28) LM_VMCASE(29)
+    LM_VMCASE(30) LM_VMCASE(31)
+    default: __builtin_amdgcn_s_waitcnt(LM_VMCNT(0)); break;
+  }
+}
 
-__global__ __launch_bounds__(256) void lm_gram_kernel(LmGramArgs args) {
-  __shared__ float rows[kGramRows][kLmKP + 1];
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ------------------------------------------------------------------ thin products
+// C (64 rows of one matrix x NB) = A B^T, fp32.  The products of the
+// randomized SVD read the whole of X (or X^T) against a narrow panel, so
+// they are bound by streaming X: operands move global -> LDS by DMA in
+// stages of 32 k (one 128-byte line per row: the block's 64 rows of A, then
+// NB rows of B) through a ring of kThinRing stages (kThinRing - 1 stages in
+// flight).  16-byte chunk c of row r is stored at chunk c ^ (r & 7).  Wave w
+// computes rows 16 w .. 16 w + 15 against all NB columns with
+// v_mfma_f32_16x16x4_f32 (a lane's 16-byte fragment holds 4 consecutive k,
+// consumed by four MFMAs).  The epilogue writes C, optionally C^T, and
+// optionally the fp64 Gram matrix of the block's rows of C (the next
+// orthonormalisation's input), so no Gram pass re-reads the panel.
+// Six stages: two blocks fit a CU at NB = 32 (72 KB each), so the second
+// block's waves hide each stage's LDS and barrier latency.
+constexpr int kThinRing = 6;
+
+template <int NB>
+__global__ __launch_bounds__(256, NB == 32 ? 2 : 1) void lm_thin_kernel(LmThinArgs args) {
+  constexpr int ROWS = kThinRows + NB;      // rows per stage: A then B
+  constexpr int CHUNKS = ROWS / 8;          // 1 KB DMA instructions per stage
+  constexpr int STAGE = ROWS * 128;         // bytes per stage
+  constexpr int FN = NB / 16;
+  static_assert(kThinRing * STAGE <= (NB == 32 ? 80 : 128) * 1024, "LDS");
+  __shared__ __attribute__((aligned(1024))) char lds[kThinRing * STAGE];
   const int b = (int)blockIdx.x;
-  const int ci = class_of(args.block_begin, b);
-  const LmGramClass &cl = args.cls[ci];
-  const int local = b - args.block_begin[ci];
-  const int mat = local / cl.nchunks, chunk = local - mat * cl.nchunks;
-  const float *P = cl.panel + (int64_t)mat * cl.stride;
+  const int ci = class_of(args.begin, b);
+  const LmThinClass &cl = args.cls[ci];
+  const int local = b - args.begin[ci];
+  const int mat = local / cl.tiles, tile = local - mat * cl.tiles;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const char *A = (const char *)(cl.a + (int64_t)mat * cl.sa + (int64_t)tile * kThinRows * cl.lda);
+  const char *B = (const char *)(cl.b + (int64_t)mat * cl.sb);
+  const int64_t lda_b = (int64_t)cl.lda * 4, ldb_b = (int64_t)cl.ldb * 4;
+  const int nk = cl.K / 32;
+  const int my_chunks = (CHUNKS - wave + 3) / 4;   // DMA instructions of this wave per stage
+  auto dma = [&](int kb) {
+    char *dst = lds + (kb % kThinRing) * STAGE;
+    for (int c = wave; c < CHUNKS; c += 4) {
+      const int row = 8 * c + (lane >> 3);
+      const int lch = (lane & 7) ^ (lane >> 3);          // logical chunk held at physical chunk lane & 7
+      const char *src = row < kThinRows ? A + (int64_t)row * lda_b : B + (int64_t)(row - kThinRows) * ldb_b;
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)(src + (int64_t)kb * 128 + lch * 16),
+                                       (void __attribute__((address_space(3))) *)(dst + c * 1024), 16, 0, 0);
+    }
+  };
+  f32x4 acc[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int pre = min(kThinRing - 1, nk);
+  for (int kb = 0; kb < pre; ++kb) dma(kb);
+  const int fr = lane & 15;
+  const int arow = 16 * wave + fr;
+  for (int kb = 0; kb < nk; ++kb) {
+    const int issued = min(nk, kb + kThinRing - 1);
+    lm_waitcnt_vm((issued - kb - 1) * my_chunks);
+    __syncthreads();   // every wave's part of stage kb has landed; stage kb - 1's slot is free
+    if (kb + kThinRing - 1 < nk) dma(kb + kThinRing - 1);
+    const char *slot = lds + (kb % kThinRing) * STAGE;
+    // every fragment of the stage first, then the MFMAs
+    u32x4 a[2], bv[2][FN];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int lch = 4 * ks + (lane >> 4);
+      a[ks] = *(const u32x4 *)(slot + arow * 128 + ((lch ^ (arow & 7)) * 16));
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int brow = kThinRows + 16 * j + fr;
+        bv[ks][j] = *(const u32x4 *)(slot + brow * 128 + ((lch ^ (brow & 7)) * 16));
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[ks].x), __uint_as_float(bv[ks][j].x), acc[j], 0, 0, 0);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[ks].y), __uint_as_float(bv[ks][j].y), acc[j], 0, 0, 0);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[ks].z), __uint_as_float(bv[ks][j].z), acc[j], 0, 0, 0);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[ks].w), __uint_as_float(bv[ks][j].w), acc[j], 0, 0, 0);
+      }
+  }
+  // epilogue: lane holds C[16 w + 4 (lane / 16) + r][16 j + lane % 16]
+  const int r0 = tile * kThinRows + 16 * wave + 4 * (lane >> 4);
+  if (cl.c) {
+    float *C = cl.c + (int64_t)mat * cl.sc;
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) C[(int64_t)(r0 + r) * cl.ldc + 16 * j + fr] = acc[j][r];
+  }
+  if (cl.c2) {
+    float *C2 = cl.c2 + (int64_t)mat * cl.sc2;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) *(f32x4 *)(C2 + (int64_t)(16 * j + fr) * cl.ldc2 + r0) = acc[j];
+  }
+  if (cl.part_base < 0) return;   // uniform per class
+  __syncthreads();                // every wave is done with the ring
+  float *cb = (float *)lds;       // 64 x (NB + 1) floats
+#pragma unroll
+  for (int j = 0; j < FN; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) cb[(16 * wave + 4 * (lane >> 4) + r) * (NB + 1) + 16 * j + fr] = acc[j][r];
+  __syncthreads();
   const int n = args.n, nn = n * n;
-  const int r0 = chunk * kLmChunk, r1 = min(cl.rows, r0 + kLmChunk);
-  constexpr int kPer = kLmSlot / 256;   // entries per thread at n = kLmKP
-  double acc[kPer];
-  int ei[kPer], ej[kPer];
-#pragma unroll
-  for (int m = 0; m < kPer; ++m) {
-    const int e = threadIdx.x + 256 * m;
-    acc[m] = 0.0;
-    ei[m] = e < nn ? e / n : 0;
-    ej[m] = e < nn ? e - (e / n) * n : 0;
-  }
-  for (int base = r0; base < r1; base += kGramRows) {
-    const int cnt = min(kGramRows, r1 - base);
-    __syncthreads();
-    // stage cnt rows of kLmKP floats: 16-byte loads, 16 per row
-    for (int q = threadIdx.x; q < kGramRows * (kLmKP / 4); q += 256) {
-      const int r = q / (kLmKP / 4), c4 = q - r * (kLmKP / 4);
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (r < cnt) v = *(const float4 *)(P + (int64_t)(base + r) * kLmKP + 4 * c4);
-      rows[r][4 * c4 + 0] = v.x;
-      rows[r][4 * c4 + 1] = v.y;
-      rows[r][4 * c4 + 2] = v.z;
-      rows[r][4 * c4 + 3] = v.w;
-    }
-    __syncthreads();
-    for (int r = 0; r < cnt; ++r) {
-#pragma unroll
-      for (int m = 0; m < kPer; ++m)
-        if (256 * m < nn)   // uniform: skip entry groups past n x n
-          acc[m] = fma((double)rows[r][ei[m]], (double)rows[r][ej[m]], acc[m]);
-    }
-  }
-  double *out = args.partials + (int64_t)(cl.part_base + mat * cl.nchunks + chunk) * kLmSlot;
-#pragma unroll
-  for (int m = 0; m < kPer; ++m) {
-    const int e = threadIdx.x + 256 * m;
-    if (e < nn) out[ei[m] * kLmKP + ej[m]] = acc[m];
+  double *out = args.partials + (int64_t)(cl.part_base + mat * cl.tiles + tile) * nn;
+  for (int e = threadIdx.x; e < nn; e += 256) {
+    const int i = e / n, j = e - (e / n) * n;
+    double sum = 0.0;
+    for (int r = 0; r < kThinRows; ++r) sum = fma((double)cb[r * (NB + 1) + i], (double)cb[r * (NB + 1) + j], sum);
+    out[e] = sum;
   }
 }
 
@@ -102,7 +180,7 @@ __device__ __forceinline__ void round_pair(int N, int r, int k, int &p, int &q) 
 }
 
 __global__ __launch_bounds__(256) void lm_eig_kernel(LmEigArgs args) {
-  __shared__ double a[kLmKP][kLmKP + 1];
+  __shared__ double a[2][kLmKP][kLmKP + 1];   // double-buffered: each round reads one, writes the other
   __shared__ double v[kLmKP][kLmKP + 1];
   __shared__ double rot_c[kLmKP / 2], rot_s[kLmKP / 2];
   __shared__ int rot_p[kLmKP / 2], rot_q[kLmKP / 2];
@@ -114,71 +192,93 @@ __global__ __launch_bounds__(256) void lm_eig_kernel(LmEigArgs args) {
   const int mat = b - args.begin[ci];
   const int n = args.n;
   const int N = (n + 1) & ~1;   // even size for the pair schedule (a zero row/column pads an odd n)
+  const int H = N / 2;          // pairs per round
   const int tid = threadIdx.x;
+  const int NT = (int)blockDim.x;   // 64 (one wave) for n <= 32, else 256
 
   // fixed-order sum of the matrix's partials; V = I
-  const double *part = args.partials + (int64_t)(cl.part_base + mat * cl.nchunks) * kLmSlot;
-  for (int e = tid; e < N * N; e += 256) {
+  const int nn = n * n;
+  const double *part = args.partials + (int64_t)(cl.part_base + mat * cl.nchunks) * nn;
+  for (int e = tid; e < N * N; e += NT) {
     const int i = e / N, j = e - (e / N) * N;
     double s = 0.0;
-    if (i < n && j < n)
-      for (int c = 0; c < cl.nchunks; ++c) s += part[(int64_t)c * kLmSlot + i * kLmKP + j];
-    a[i][j] = s;
+    if (i < n && j < n) {
+      // partials in chunk order; 8 loads in flight before their adds
+      const double *pe = part + i * n + j;
+      int c = 0;
+      for (; c + 8 <= cl.nchunks; c += 8) {
+        double x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = pe[(int64_t)(c + u) * nn];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s += x[u];
+      }
+      for (; c < cl.nchunks; ++c) s += pe[(int64_t)c * nn];
+    }
+    a[0][i][j] = s;
     v[i][j] = (i == j) ? 1.0 : 0.0;
   }
   __syncthreads();
 
   // cyclic Jacobi (Golub & Van Loan, "Matrix Computations", section 8.5):
-  // each rotation J in rows / columns (p, q) with J_pp = J_qq = c,
-  // J_pq = s, J_qp = -s zeroes a_pq in J^T A J; V <- V J.  A pair rotates
-  // only while |a_pq| > 1e-15 sqrt(|a_pp a_qq|) (the relative test that
-  // keeps small eigenvalues accurate); a sweep without any rotation ends the
+  // a rotation J in rows / columns (p, q) with J_pp = J_qq = c, J_pq = s,
+  // J_qp = -s zeroes a_pq in J^T A J.  A round applies N / 2 disjoint
+  // rotations at once: each 2 x 2 block of rows (p_k, q_k) and columns
+  // (p_m, q_m) becomes J_k^T A_km J_m, read from one buffer and written to
+  // the other; V <- V J column pair by column pair.  A pair rotates only
+  // while |a_pq| > 1e-15 sqrt(|a_pp a_qq|) (the relative test that keeps
+  // small eigenvalues accurate); a sweep without any rotation ends the
   // iteration (at most kMaxSweeps; NaN input runs them all).
+  int cur = 0;
   for (int sweep = 0; sweep < kMaxSweeps; ++sweep) {
     if (tid == 0) rotated = 0;
     __syncthreads();
     for (int r = 0; r < N - 1; ++r) {
-      if (tid < N / 2) {
+      for (int k = tid; k < H; k += NT) {
         int p, q;
-        round_pair(N, r, tid, p, q);
-        const double apq = a[p][q];
+        round_pair(N, r, k, p, q);
+        const double apq = a[cur][p][q];
         double c = 1.0, s = 0.0;
-        if (fabs(apq) > 1e-15 * sqrt(fabs(a[p][p] * a[q][q]))) {
-          const double tau = (a[q][q] - a[p][p]) / (2.0 * apq);
+        if (fabs(apq) > 1e-15 * sqrt(fabs(a[cur][p][p] * a[cur][q][q]))) {
+          const double tau = (a[cur][q][q] - a[cur][p][p]) / (2.0 * apq);
           const double t = (tau >= 0.0 ? 1.0 : -1.0) / (fabs(tau) + sqrt(1.0 + tau * tau));
           c = 1.0 / sqrt(1.0 + t * t);
           s = t * c;
           rotated = 1;
         }
-        rot_p[tid] = p;
-        rot_q[tid] = q;
-        rot_c[tid] = c;
-        rot_s[tid] = s;
+        rot_p[k] = p;
+        rot_q[k] = q;
+        rot_c[k] = c;
+        rot_s[k] = s;
       }
       __syncthreads();
-      // A <- J^T A (rows p and q)
-      for (int it = tid; it < (N / 2) * N; it += 256) {
-        const int k = it / N, j = it - (it / N) * N;
-        const int p = rot_p[k], q = rot_q[k];
-        const double c = rot_c[k], s = rot_s[k];
-        const double x = a[p][j], y = a[q][j];
-        a[p][j] = c * x - s * y;
-        a[q][j] = s * x + c * y;
+      const int nxt = cur ^ 1;
+      for (int it = tid; it < H * H + H * N; it += NT) {
+        if (it < H * H) {
+          const int k = it / H, m = it - (it / H) * H;
+          const int p = rot_p[k], q = rot_q[k], pm = rot_p[m], qm = rot_q[m];
+          const double ck = rot_c[k], sk = rot_s[k], cm = rot_c[m], sm = rot_s[m];
+          const double x00 = a[cur][p][pm], x01 = a[cur][p][qm], x10 = a[cur][q][pm], x11 = a[cur][q][qm];
+          // rows: J_k^T (first row c x - s y, second s x + c y)
+          const double y00 = ck * x00 - sk * x10, y01 = ck * x01 - sk * x11;
+          const double y10 = sk * x00 + ck * x10, y11 = sk * x01 + ck * x11;
+          // columns: J_m
+          a[nxt][p][pm] = cm * y00 - sm * y01;
+          a[nxt][p][qm] = sm * y00 + cm * y01;
+          a[nxt][q][pm] = cm * y10 - sm * y11;
+          a[nxt][q][qm] = sm * y10 + cm * y11;
+        } else {
+          const int u = it - H * H;
+          const int k = u / N, i = u - (u / N) * N;
+          const int p = rot_p[k], q = rot_q[k];
+          const double c = rot_c[k], s = rot_s[k];
+          const double vx = v[i][p], vy = v[i][q];
+          v[i][p] = c * vx - s * vy;
+          v[i][q] = s * vx + c * vy;
+        }
       }
       __syncthreads();
-      // A <- A J and V <- V J (columns p and q)
-      for (int it = tid; it < (N / 2) * N; it += 256) {
-        const int k = it / N, i = it - (it / N) * N;
-        const int p = rot_p[k], q = rot_q[k];
-        const double c = rot_c[k], s = rot_s[k];
-        const double x = a[i][p], y = a[i][q];
-        a[i][p] = c * x - s * y;
-        a[i][q] = s * x + c * y;
-        const double vx = v[i][p], vy = v[i][q];
-        v[i][p] = c * vx - s * vy;
-        v[i][q] = s * vx + c * vy;
-      }
-      __syncthreads();
+      cur = nxt;
     }
     const int done = (rotated == 0);   // read by every thread after the barrier above
     __syncthreads();                   // ... before thread 0 clears it again
@@ -186,43 +286,48 @@ __global__ __launch_bounds__(256) void lm_eig_kernel(LmEigArgs args) {
   }
 
   // eigenvalues in descending order (ties by index)
-  if (tid < N) {
-    const double d = a[tid][tid];
+  for (int i = tid; i < N; i += NT) {
+    const double d = a[cur][i][i];
     int rank = 0;
     for (int j = 0; j < N; ++j) {
-      const double dj = a[j][j];
-      rank += (dj > d || (dj == d && j < tid)) ? 1 : 0;
+      const double dj = a[cur][j][j];
+      rank += (dj > d || (dj == d && j < i)) ? 1 : 0;
     }
-    order[rank] = tid;
+    order[rank] = i;
   }
   __syncthreads();
-  const double dmax = a[order[0]][order[0]];
+  const double dmax = a[cur][order[0]][order[0]];
   const double floor_d = args.cutoff * dmax;
   float *out = cl.out + (int64_t)mat * cl.out_stride;
   if (args.mode == kLmOrth) {
     // out[j][i] = W[i][j], W[:, j] = v[:, order[j]] / sqrt(d_order[j]) for kept j
-    for (int e = tid; e < kLmSlot; e += 256) {
+    for (int e = tid; e < kLmSlot; e += NT) {
       const int j = e / kLmKP, i = e - (e / kLmKP) * kLmKP;
       float w = 0.f;
       if (j < N && i < N) {
         const int o = order[j];
-        const double d = a[o][o];
+        const double d = a[cur][o][o];
         if (dmax > 0.0 && d > floor_d) w = (float)(v[i][o] / sqrt(d));
       }
       out[e] = w;
     }
   } else {
+    // T = U U^T with U[:, m] = v[:, order[m]] / d^(1/4) over the kept m
+    // (reusing the other A buffer for U)
     const int keep = min(args.rank, N);
-    for (int e = tid; e < kLmSlot; e += 256) {
+    double (*U)[kLmKP + 1] = a[cur ^ 1];
+    for (int e = tid; e < N * keep; e += NT) {
+      const int i = e / keep, m = e - (e / keep) * keep;
+      const int o = order[m];
+      const double d = a[cur][o][o];
+      U[i][m] = (dmax > 0.0 && d > floor_d) ? v[i][o] / sqrt(sqrt(d)) : 0.0;
+    }
+    __syncthreads();
+    for (int e = tid; e < kLmSlot; e += NT) {
       const int i = e / kLmKP, j = e - (e / kLmKP) * kLmKP;
       double t = 0.0;
-      if (i < N && j < N && dmax > 0.0) {
-        for (int m = 0; m < keep; ++m) {
-          const int o = order[m];
-          const double d = a[o][o];
-          if (d > floor_d) t += v[i][o] * v[j][o] / sqrt(d);
-        }
-      }
+      if (i < N && j < N)
+        for (int m = 0; m < keep; ++m) t += U[i][m] * U[j][m];
       out[e] = (float)t;
     }
   }
@@ -246,15 +351,17 @@ __global__ __launch_bounds__(256) void lm_pad_kernel(LmPadArgs args) {
 
 }  // namespace
 
-hipError_t launch_lm_gram(const LmGramArgs &args, int blocks, hipStream_t s) {
+hipError_t launch_lm_thin(const LmThinArgs &args, int nb, int blocks, hipStream_t s) {
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(lm_gram_kernel, dim3(blocks), dim3(256), 0, s, args);
+  if (nb == 32) hipLaunchKernelGGL(lm_thin_kernel<32>, dim3(blocks), dim3(256), 0, s, args);
+  else if (nb == 64) hipLaunchKernelGGL(lm_thin_kernel<64>, dim3(blocks), dim3(256), 0, s, args);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
 hipError_t launch_lm_eig(const LmEigArgs &args, int blocks, hipStream_t s) {
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(lm_eig_kernel, dim3(blocks), dim3(256), 0, s, args);
+  hipLaunchKernelGGL(lm_eig_kernel, dim3(blocks), dim3(args.n <= 32 ? 64 : 256), 0, s, args);
   return hipGetLastError();
 }
 

@@ -83,7 +83,7 @@ struct ClassInfo {
   size_t sq[5] = {0, 0, 0, 0, 0};   // direct: A, B ; gram: R, T, P, Q, Qspare
   size_t lm[kLmBufs] = {};         // LiMuon panels
   int lm_part_base = 0;            // first fp64 Gram partial slot (LiMuon)
-  int lm_chunks_s = 0, lm_chunks_l = 0;   // partial chunks of an s-row / l-row panel
+  int lm_chunks_s = 0, lm_chunks_l = 0;   // Gram partials (64-row tiles) of an s-row / l-row panel
 };
 
 struct Plan {
@@ -253,8 +253,9 @@ muon_status build_plan(const muon_param *p, int n, int ns_steps, muon_variant v,
       ClassInfo ci;
       ci.s = s;
       ci.l = l;
-      // LiMuon's panels are kLmKP wide: every product uses the 64 tile
-      ci.tile = (v == MUON_LIMUON) ? 64 : pick_tile(s, l, plan.set.ns_dtype);
+      // (LiMuon: fp32, so 64 or 128; the 128 tile's staged epilogue writes
+      // the weight update of its last product along W's rows)
+      ci.tile = pick_tile(s, l, plan.set.ns_dtype);
       ci.Sp = round_up(s, ci.tile);
       ci.Lp = round_up(l, ci.tile);
       plan.classes.push_back(ci);
@@ -304,13 +305,14 @@ muon_status build_plan(const muon_param *p, int n, int ns_steps, muon_variant v,
                                      kp * kp * 4 * cnt, kp * kp * 4 * cnt,                       // w, t
                                      (size_t)c.Sp * kp * 4 * cnt};                               // p
       for (int j = 0; j < kLmBufs; ++j) { c.lm[j] = off; off = align256(off + sizes[j]); }
-      c.lm_chunks_s = (int)((c.s + kLmChunk - 1) / kLmChunk);
-      c.lm_chunks_l = (int)((c.l + kLmChunk - 1) / kLmChunk);
+      c.lm_chunks_s = (int)(c.Sp / kThinRows);
+      c.lm_chunks_l = (int)(c.Lp / kThinRows);
       c.lm_part_base = slots;
       slots += (int)cnt * c.lm_chunks_l;
     }
+    const size_t kp = (size_t)(plan.set.rank + plan.set.oversample);
     plan.off_lm_parts = off;
-    off = align256(off + (size_t)slots * kLmSlot * sizeof(double));
+    off = align256(off + (size_t)slots * kp * kp * sizeof(double));
   } else {
     for (ClassInfo &c : plan.classes) {
       const size_t cnt = c.members.size();
@@ -896,22 +898,24 @@ muon_status run_gram(const Plan &plan, char *ws, Tracer &st, double sx0, float l
 // ---------------------------------------------------------------- LiMuon
 // Randomized SVD of X (X0 in its wide orientation, s x l) in place of
 // Newton-Schulz (LiMuon digest, "Метод"; Halko, Martinsson & Tropp 2011,
-// Algorithms 4.4 and 5.1), with kp = k + p test vectors padded to kLmKP:
+// Algorithms 4.4 and 5.1), with kp = k + p test vectors (panels nb = 32 or
+// 64 columns wide, stored kLmKP wide):
 //   Y = X Omega ; Q = orth(Y)
 //   q times: Z = orth(X^T Q) ; Q = orth(X Z)     (the last Q orthonormalised twice)
 //   B^T = X^T Q ; H = B B^T = V D V^T ; T = V_k D_k^{-1/2} V_k^T
-//   O^T = B^T (Q T)^T   (= V_k U_k^T ... in the tall orientation), fused with
-//                        the weight update
+//   O^T = B^T (Q T)^T, fused with the weight update
 // orth(P) = P W with W = V_r D_r^{-1/2} from the fp64 Jacobi eigen-
-// decomposition of P^T P (directions at most 1e-12 of the largest
-// eigenvalue dropped).  Every product is a grouped fp32 GEMM on 64 tiles;
-// the Gram partials and eigen-decompositions are the lm_* kernels.
+// decomposition of the Gram matrix P^T P (directions at most 1e-12 of the
+// largest eigenvalue dropped).  Every product against a panel runs in
+// lm_thin_kernel, which also writes the fp64 Gram partials of its result;
+// the final product is a grouped fp32 GEMM on 64 tiles.
 muon_status run_limuon(const Plan &plan, char *ws, Tracer &st, float lr, float wd) {
   const int kp = plan.set.rank + plan.set.oversample;
+  const int nb = kp <= 32 ? 32 : 64;
   const int KP = kLmKP;
   double *parts = (double *)(ws + plan.off_lm_parts);
   const size_t es = 4;
-  const size_t pan_s = 0, pan_l = 1;   // panel kinds: s rows or l rows
+  const int pan_s = 0, pan_l = 1;   // panel kinds: s rows or l rows
 
   // pad the caller's test matrix into each class's [KP x Lp] buffer
   {
@@ -950,166 +954,172 @@ muon_status run_limuon(const Plan &plan, char *ws, Tracer &st, float lr, float w
     if (e != MUON_OK) return e;
   }
 
-  // fp64 Gram partials of one panel per matrix, then the eigen stage
-  auto gram_eig = [&](int buf, size_t kind, int mode, int out_buf) -> muon_status {
-    {
-      LmGramArgs a;
-      std::memset(&a, 0, sizeof(a));
-      for (int j = 0; j < kLmMaxClasses; ++j) a.block_begin[j] = INT32_MAX;
-      a.n = kp;
-      a.partials = parts;
-      int blocks = 0;
-      double bytes = 0.0;
-      auto go = [&]() -> muon_status {
-        if (a.nclass == 0) return MUON_OK;
-        HIP_TRY(st.run(MUON_STAGE_SMALL, bytes, [&]() { return launch_lm_gram(a, blocks, st.s); }));
-        a.nclass = 0;
-        blocks = 0;
-        bytes = 0.0;
-        for (int j = 0; j < kLmMaxClasses; ++j) a.block_begin[j] = INT32_MAX;
-        return MUON_OK;
-      };
-      for (const ClassInfo &cl : plan.classes) {
-        if (a.nclass == kLmMaxClasses) {
-          muon_status e = go();
-          if (e != MUON_OK) return e;
-        }
-        const int64_t rows = kind == pan_s ? cl.s : cl.l;
-        const int64_t prows = kind == pan_s ? cl.Sp : cl.Lp;
-        LmGramClass &c = a.cls[a.nclass];
-        c.panel = (const float *)(ws + cl.lm[buf]);
-        c.stride = prows * KP;
-        c.rows = (int32_t)rows;
-        c.nchunks = kind == pan_s ? cl.lm_chunks_s : cl.lm_chunks_l;
-        c.count = (int32_t)cl.members.size();
-        c.part_base = cl.lm_part_base;
-        a.block_begin[a.nclass++] = blocks;
-        blocks += c.count * c.nchunks;
-        bytes += (double)rows * kp * 4.0 * c.count;
-      }
-      muon_status e = go();
-      if (e != MUON_OK) return e;
-    }
-    {
-      LmEigArgs a;
-      std::memset(&a, 0, sizeof(a));
+  // One thin product per class: C = A B^T over K, A's rows `kind` (s or l
+  // padded), optionally C^T and the Gram partials of C.
+  struct Thin {
+    const float *a;
+    int64_t sa, lda;
+    const float *b;
+    int64_t sb, ldb;
+    int64_t K;
+    int kind;
+    float *c, *c2;
+    int64_t sc, ldc, sc2, ldc2;
+    bool gram;
+    double flops;
+  };
+  auto thin = [&](auto &&make) -> muon_status {
+    LmThinArgs a;
+    std::memset(&a, 0, sizeof(a));
+    for (int j = 0; j < kLmMaxClasses; ++j) a.begin[j] = INT32_MAX;
+    a.n = kp;
+    a.partials = parts;
+    int blocks = 0;
+    double flops = 0.0;
+    auto go = [&]() -> muon_status {
+      if (a.nclass == 0) return MUON_OK;
+      HIP_TRY(st.run(MUON_STAGE_GEMM, flops, [&]() { return launch_lm_thin(a, nb, blocks, st.s); }));
+      a.nclass = 0;
+      blocks = 0;
+      flops = 0.0;
       for (int j = 0; j < kLmMaxClasses; ++j) a.begin[j] = INT32_MAX;
-      a.n = kp;
-      a.mode = mode;
-      a.rank = plan.set.rank;
-      a.cutoff = mode == kLmOrth ? 1e-12 : plan.set.rcond * plan.set.rcond;
-      a.partials = parts;
-      int blocks = 0;
-      auto go = [&]() -> muon_status {
-        if (a.nclass == 0) return MUON_OK;
-        HIP_TRY(st.run(MUON_STAGE_SMALL, 0.0, [&]() { return launch_lm_eig(a, blocks, st.s); }));
-        a.nclass = 0;
-        blocks = 0;
-        for (int j = 0; j < kLmMaxClasses; ++j) a.begin[j] = INT32_MAX;
-        return MUON_OK;
-      };
-      for (const ClassInfo &cl : plan.classes) {
-        if (a.nclass == kLmMaxClasses) {
-          muon_status e = go();
-          if (e != MUON_OK) return e;
-        }
-        LmEigClass &c = a.cls[a.nclass];
-        c.out = (float *)(ws + cl.lm[out_buf]);
-        c.out_stride = (int64_t)KP * KP;
-        c.count = (int32_t)cl.members.size();
-        c.nchunks = kind == pan_s ? cl.lm_chunks_s : cl.lm_chunks_l;
-        c.part_base = cl.lm_part_base;
-        a.begin[a.nclass++] = blocks;
-        blocks += c.count;
+      return MUON_OK;
+    };
+    for (const ClassInfo &cl : plan.classes) {
+      if (a.nclass == kLmMaxClasses) {
+        muon_status e = go();
+        if (e != MUON_OK) return e;
       }
-      muon_status e = go();
-      if (e != MUON_OK) return e;
+      const Thin t = make(cl);
+      LmThinClass &c = a.cls[a.nclass];
+      c.a = t.a;
+      c.sa = t.sa;
+      c.lda = (int32_t)t.lda;
+      c.b = t.b;
+      c.sb = t.sb;
+      c.ldb = (int32_t)t.ldb;
+      c.c = t.c;
+      c.c2 = t.c2;
+      c.sc = t.sc;
+      c.ldc = (int32_t)t.ldc;
+      c.sc2 = t.sc2;
+      c.ldc2 = (int32_t)t.ldc2;
+      c.K = (int32_t)t.K;
+      c.tiles = t.kind == pan_s ? cl.lm_chunks_s : cl.lm_chunks_l;
+      c.count = (int32_t)cl.members.size();
+      c.part_base = t.gram ? cl.lm_part_base : -1;
+      a.begin[a.nclass++] = blocks;
+      blocks += c.count * c.tiles;
+      flops += t.flops * (double)c.count;
     }
-    return MUON_OK;
+    return go();
   };
-
-  // C (m x KP or l x KP) = panel (rows x KP) W, and optionally C^T
-  auto apply_w = [&](int in_buf, size_t kind, int w_buf, int out_buf, int out_t_buf) -> muon_status {
-    StageBuilder sb(plan, ws, st);
-    for (size_t ci = 0; ci < plan.classes.size(); ++ci) {
-      const ClassInfo &cl = plan.classes[ci];
-      const int64_t prows = kind == pan_s ? cl.Sp : cl.Lp;
-      GemmClass g = make_gemm(cl, es, ws, cl.lm[in_buf], prows, KP, cl.lm[w_buf], KP, KP, KP, false);
-      set_out(g, ws, cl.lm[out_buf], prows, KP, true);
-      if (out_t_buf >= 0) set_out2(g, ws, cl.lm[out_t_buf], KP, prows);
-      sb.per_class[ci] = g;
-      sb.per_flops[ci] = 2.0 * (double)(kind == pan_s ? cl.s : cl.l) * kp * kp;
+  auto eig = [&](int kind, int mode, int out_buf) -> muon_status {
+    LmEigArgs a;
+    std::memset(&a, 0, sizeof(a));
+    for (int j = 0; j < kLmMaxClasses; ++j) a.begin[j] = INT32_MAX;
+    a.n = kp;
+    a.mode = mode;
+    a.rank = plan.set.rank;
+    a.cutoff = mode == kLmOrth ? 1e-12 : plan.set.rcond * plan.set.rcond;
+    a.partials = parts;
+    int blocks = 0;
+    auto go = [&]() -> muon_status {
+      if (a.nclass == 0) return MUON_OK;
+      HIP_TRY(st.run(MUON_STAGE_SMALL, 0.0, [&]() { return launch_lm_eig(a, blocks, st.s); }));
+      a.nclass = 0;
+      blocks = 0;
+      for (int j = 0; j < kLmMaxClasses; ++j) a.begin[j] = INT32_MAX;
+      return MUON_OK;
+    };
+    for (const ClassInfo &cl : plan.classes) {
+      if (a.nclass == kLmMaxClasses) {
+        muon_status e = go();
+        if (e != MUON_OK) return e;
+      }
+      LmEigClass &c = a.cls[a.nclass];
+      c.out = (float *)(ws + cl.lm[out_buf]);
+      c.out_stride = (int64_t)KP * KP;
+      c.count = (int32_t)cl.members.size();
+      c.nchunks = kind == pan_s ? cl.lm_chunks_s : cl.lm_chunks_l;
+      c.part_base = cl.lm_part_base;
+      a.begin[a.nclass++] = blocks;
+      blocks += c.count;
     }
-    HIP_TRY(sb.launch());
-    return MUON_OK;
+    return go();
   };
-  auto orth = [&](int in_buf, size_t kind, int out_buf, int out_t_buf) -> muon_status {
-    muon_status e = gram_eig(in_buf, kind, kLmOrth, kLmW);
-    if (e != MUON_OK) return e;
-    return apply_w(in_buf, kind, kLmW, out_buf, out_t_buf);
+  auto buf = [&](const ClassInfo &cl, int i) { return (float *)(ws + cl.lm[i]); };
+  // panel (rows x KP) times a KP x KP factor stored as its transpose's rows
+  auto apply = [&](int in_buf, int kind, int w_buf, int out_buf, int out_t_buf, bool gram) -> muon_status {
+    return thin([&](const ClassInfo &cl) {
+      const int64_t rows = kind == pan_s ? cl.Sp : cl.Lp;
+      Thin t{};
+      t.a = buf(cl, in_buf); t.sa = rows * KP; t.lda = KP;
+      t.b = buf(cl, w_buf); t.sb = (int64_t)KP * KP; t.ldb = KP;
+      t.K = nb; t.kind = kind;
+      t.c = buf(cl, out_buf); t.sc = rows * KP; t.ldc = KP;
+      if (out_t_buf >= 0) { t.c2 = buf(cl, out_t_buf); t.sc2 = (int64_t)KP * rows; t.ldc2 = rows; }
+      t.gram = gram;
+      t.flops = 2.0 * (double)(kind == pan_s ? cl.s : cl.l) * kp * kp;
+      return t;
+    });
   };
-  // X-panel products: long = X (s x l) times an l-row panel stored
-  // transposed [KP x Lp]; short = X^T (l x s) times an s-row panel stored
-  // transposed [KP x Sp]
+  // X (s x l) times an l-row panel given as its transpose [KP x Lp]
   auto x_times = [&](int bt_buf, bool shared_b, int out_buf) -> muon_status {
-    StageBuilder sb(plan, ws, st);
-    for (size_t ci = 0; ci < plan.classes.size(); ++ci) {
-      const ClassInfo &cl = plan.classes[ci];
-      GemmClass g = make_gemm(cl, es, ws, cl.X[0], cl.Sp, cl.Lp, cl.lm[bt_buf], KP, cl.Lp, cl.Lp, false);
-      if (shared_b) g.sb = 0;
-      set_out(g, ws, cl.lm[out_buf], cl.Sp, KP, true);
-      sb.per_class[ci] = g;
-      sb.per_flops[ci] = 2.0 * (double)cl.s * (double)cl.l * kp;
-    }
-    HIP_TRY(sb.launch());
-    return MUON_OK;
+    return thin([&](const ClassInfo &cl) {
+      Thin t{};
+      t.a = (const float *)(ws + cl.X[0]); t.sa = cl.Sp * cl.Lp; t.lda = cl.Lp;
+      t.b = buf(cl, bt_buf); t.sb = shared_b ? 0 : (int64_t)KP * cl.Lp; t.ldb = cl.Lp;
+      t.K = cl.Lp; t.kind = pan_s;
+      t.c = buf(cl, out_buf); t.sc = cl.Sp * KP; t.ldc = KP;
+      t.gram = true;
+      t.flops = 2.0 * (double)cl.s * (double)cl.l * kp;
+      return t;
+    });
   };
+  // X^T (l x s) times an s-row panel given as its transpose [KP x Sp]
   auto xt_times = [&](int bt_buf, int out_buf) -> muon_status {
-    StageBuilder sb(plan, ws, st);
-    for (size_t ci = 0; ci < plan.classes.size(); ++ci) {
-      const ClassInfo &cl = plan.classes[ci];
-      GemmClass g = make_gemm(cl, es, ws, cl.XT[0], cl.Lp, cl.Sp, cl.lm[bt_buf], KP, cl.Sp, cl.Sp, false);
-      set_out(g, ws, cl.lm[out_buf], cl.Lp, KP, true);
-      sb.per_class[ci] = g;
-      sb.per_flops[ci] = 2.0 * (double)cl.s * (double)cl.l * kp;
-    }
-    HIP_TRY(sb.launch());
-    return MUON_OK;
+    return thin([&](const ClassInfo &cl) {
+      Thin t{};
+      t.a = (const float *)(ws + cl.XT[0]); t.sa = cl.Lp * cl.Sp; t.lda = cl.Sp;
+      t.b = buf(cl, bt_buf); t.sb = (int64_t)KP * cl.Sp; t.ldb = cl.Sp;
+      t.K = cl.Sp; t.kind = pan_l;
+      t.c = buf(cl, out_buf); t.sc = cl.Lp * KP; t.ldc = KP;
+      t.gram = true;
+      t.flops = 2.0 * (double)cl.s * (double)cl.l * kp;
+      return t;
+    });
+  };
+  // orth of an s-row panel into Q (and Q^T), once or twice
+  auto orth_s = [&](int in_buf, bool twice) -> muon_status {
+    muon_status e = eig(pan_s, kLmOrth, kLmW);
+    if (e != MUON_OK) return e;
+    if (!twice) return apply(in_buf, pan_s, kLmW, kLmQ, kLmQt, false);
+    if ((e = apply(in_buf, pan_s, kLmW, kLmQ2, -1, true)) != MUON_OK) return e;
+    if ((e = eig(pan_s, kLmOrth, kLmW)) != MUON_OK) return e;
+    return apply(kLmQ2, pan_s, kLmW, kLmQ, kLmQt, false);
   };
 
   muon_status e;
-  // Y = X Omega ; Q = orth(Y)   (twice when no power iteration follows)
-  if ((e = x_times(kLmOmt, true, kLmY)) != MUON_OK) return e;
   const int q = plan.set.power_iters;
-  if (q == 0) {
-    if ((e = orth(kLmY, pan_s, kLmQ2, -1)) != MUON_OK) return e;
-    if ((e = orth(kLmQ2, pan_s, kLmQ, kLmQt)) != MUON_OK) return e;
-  } else {
-    if ((e = orth(kLmY, pan_s, kLmQ, kLmQt)) != MUON_OK) return e;
-  }
+  if ((e = x_times(kLmOmt, true, kLmY)) != MUON_OK) return e;          // Y = X Omega (+ Gram)
+  if ((e = orth_s(kLmY, q == 0)) != MUON_OK) return e;
   for (int it = 0; it < q; ++it) {
-    // Z = orth(X^T Q), Y = X Z, Q = orth(Y) (orthonormalised twice at the end)
-    if ((e = xt_times(kLmQt, kLmZ)) != MUON_OK) return e;
-    if ((e = orth(kLmZ, pan_l, kLmZ2, kLmZ2t)) != MUON_OK) return e;
-    if ((e = x_times(kLmZ2t, false, kLmY)) != MUON_OK) return e;
-    if (it + 1 < q) {
-      if ((e = orth(kLmY, pan_s, kLmQ, kLmQt)) != MUON_OK) return e;
-    } else {
-      if ((e = orth(kLmY, pan_s, kLmQ2, -1)) != MUON_OK) return e;
-      if ((e = orth(kLmQ2, pan_s, kLmQ, kLmQt)) != MUON_OK) return e;
-    }
+    if ((e = xt_times(kLmQt, kLmZ)) != MUON_OK) return e;              // Z = X^T Q (+ Gram)
+    if ((e = eig(pan_l, kLmOrth, kLmW)) != MUON_OK) return e;
+    if ((e = apply(kLmZ, pan_l, kLmW, kLmZ2, kLmZ2t, false)) != MUON_OK) return e;
+    if ((e = x_times(kLmZ2t, false, kLmY)) != MUON_OK) return e;       // Y = X Z (+ Gram)
+    if ((e = orth_s(kLmY, it + 1 == q)) != MUON_OK) return e;
   }
-  // B^T = X^T Q (into Z) ; T from B B^T
-  if ((e = xt_times(kLmQt, kLmZ)) != MUON_OK) return e;
-  if ((e = gram_eig(kLmZ, pan_l, kLmTrunc, kLmT)) != MUON_OK) return e;
-  // P = Q T
-  if ((e = apply_w(kLmQ, pan_s, kLmT, kLmP, -1)) != MUON_OK) return e;
+  if ((e = xt_times(kLmQt, kLmZ)) != MUON_OK) return e;                // B^T = X^T Q (+ Gram: B B^T)
+  if ((e = eig(pan_l, kLmTrunc, kLmT)) != MUON_OK) return e;
+  if ((e = apply(kLmQ, pan_s, kLmT, kLmP, -1, false)) != MUON_OK) return e;   // P = Q T
   // O^T = B^T P^T (tall orientation), fused with the weight update
   {
     StageBuilder sb(plan, ws, st);
     for (size_t ci = 0; ci < plan.classes.size(); ++ci) {
       const ClassInfo &cl = plan.classes[ci];
-      GemmClass g = make_gemm(cl, es, ws, cl.lm[kLmZ], cl.Lp, KP, cl.lm[kLmP], cl.Sp, KP, KP, false);
+      GemmClass g = make_gemm(cl, es, ws, cl.lm[kLmZ], cl.Lp, KP, cl.lm[kLmP], cl.Sp, KP, nb, false);
       set_final(g, plan, cl, ws, lr, wd);
       g.alpha = 1.0f;
       sb.per_class[ci] = g;

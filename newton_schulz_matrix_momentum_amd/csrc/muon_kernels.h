@@ -247,28 +247,37 @@ struct AdamArgs {
 
 // ------------------------------------------------------------------ LiMuon
 // Small-matrix stages of the randomized-SVD orthogonaliser: the sketch
-// width k + p is padded to kLmKP; panels are fp32 [rows x kLmKP] row-major.
-constexpr int kLmKP = 64;             // padded sketch width (k + p <= 64)
-constexpr int kLmChunk = 256;         // panel rows per Gram partial
+// width k + p is padded to kLmKP in the panels' storage; panels are fp32
+// [rows x kLmKP] row-major.
+constexpr int kLmKP = 64;             // panel storage width (k + p <= 64)
 constexpr int kLmMaxClasses = 8;
-constexpr int kLmSlot = kLmKP * kLmKP;   // doubles per partial / per small matrix
+constexpr int kLmSlot = kLmKP * kLmKP;   // floats per small matrix (W, T)
 
-// Gram partials G_c = sum over rows of chunk c of p_row^T p_row (fp64),
-// first n columns only; one block per (matrix, chunk).
-struct LmGramClass {
-  const float *panel;      // first matrix's panel
-  int64_t stride;          // elements between matrices' panels
-  int32_t rows;            // rows summed (the true rows of the panel)
-  int32_t nchunks;         // ceil(rows / kLmChunk)
-  int32_t count;           // matrices
-  int32_t part_base;       // first partial slot of the class
+// Thin products C (M x NB) = A (M x K) B^T with B given as NB x K rows (NB =
+// 32 or 64 >= k + p; rows of B past k + p are zero), fp32, one block per 64
+// rows of one matrix (M is the padded row count, a multiple of 64).  Also
+// writes C^T (c2, optional) and, when part_base >= 0, the fp64 Gram matrix
+// of the block's 64 rows of C over its first n columns into slot
+// part_base + matrix * tiles + tile (n x n doubles per slot).
+constexpr int kThinRows = 64;
+struct LmThinClass {
+  const float *a;
+  const float *b;
+  float *c;
+  float *c2;
+  int64_t sa, sb, sc, sc2;   // per-matrix element strides (sb = 0: B shared by the class)
+  int32_t lda, ldb, ldc, ldc2;
+  int32_t K;                 // multiple of 32
+  int32_t tiles;             // M / kThinRows
+  int32_t count;
+  int32_t part_base;         // first Gram slot, or -1
 };
-struct LmGramArgs {
+struct LmThinArgs {
   int32_t nclass;
-  int32_t n;                             // columns used (k + p)
-  int32_t block_begin[kLmMaxClasses];    // first block of each class; unused = INT32_MAX
-  double *partials;                      // workspace, kLmSlot doubles per slot
-  LmGramClass cls[kLmMaxClasses];
+  int32_t n;                 // k + p: columns in the Gram partials
+  int32_t begin[kLmMaxClasses];   // first block of each class; unused = INT32_MAX
+  double *partials;
+  LmThinClass cls[kLmMaxClasses];
 };
 
 // Symmetric eigen-decomposition (fp64 Jacobi) of the sum of a matrix's Gram
@@ -282,7 +291,7 @@ struct LmEigClass {
   float *out;              // first matrix's kLmKP x kLmKP result
   int64_t out_stride;      // elements between matrices' results
   int32_t count;
-  int32_t nchunks;
+  int32_t nchunks;         // Gram partials per matrix (n x n doubles each)
   int32_t part_base;
   int32_t pad;
 };
@@ -315,7 +324,7 @@ struct LmPadArgs {
 };
 constexpr int kLmPadElems = 4096;     // padded elements per pad block
 
-hipError_t launch_lm_gram(const LmGramArgs &args, int blocks, hipStream_t s);
+hipError_t launch_lm_thin(const LmThinArgs &args, int nb, int blocks, hipStream_t s);
 hipError_t launch_lm_eig(const LmEigArgs &args, int blocks, hipStream_t s);
 hipError_t launch_lm_pad(const LmPadArgs &args, int blocks, hipStream_t s);
 
