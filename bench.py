@@ -43,6 +43,10 @@ def parse():
     ap.add_argument("--adamw", type=int, default=0, metavar="MELEMS",
                     help="only time muon_adamw_step over a synthetic set of MELEMS million vector-parameter "
                          "elements (bf16 grads) and print its own JSON line")
+    ap.add_argument("--grad-kind", default=None, choices=("gaussian", "spectral", "spike", "expert"),
+                    help="replace the workload's gradient recipe (counter runs: the profiler's counter mode "
+                         "faults inside the QR the spectral and spike recipes call; the product launches "
+                         "do not depend on the values)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB --steps times (counter calibration)")
     return ap.parse_args()
@@ -476,9 +480,12 @@ def main():
         adamw_probe(args)
         return
     w = WORKLOADS[args.workload]
+    if args.grad_kind and args.grad_kind != w.grad_kind:
+        import dataclasses
+        w = dataclasses.replace(w, grad_kind=args.grad_kind)
     variant = args.variant or w.variants[0]
-    print("bench: workload %s variant %s, %d matrices, %d warmup + %d timed steps" %
-          (w.name, variant, len(w.shapes), args.warmup, args.steps), file=sys.stderr, flush=True)
+    print("bench: workload %s variant %s, %d matrices, %s gradients, %d warmup + %d timed steps" %
+          (w.name, variant, len(w.shapes), w.grad_kind, args.warmup, args.steps), file=sys.stderr, flush=True)
     params, ms, wall, per_stage, launches, graphed, spread, first_ms, sclk = gpu_timing(args, w, variant)
     print("bench: gpu timing done (%.4f ms/step)" % ms, file=sys.stderr, flush=True)
 
@@ -540,7 +547,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name + ("+mona_lite" if args.mona_lite and w.mona else ""), "matrices": len(w.shapes),
                    "params": w.numel, "variant": variant,
-                   "ns_steps": w.ns_steps, "coeffs": w.coeffs, "grad_dtype": w.grad_dtype, "ns_dtype": ns_dtype,
+                   "ns_steps": w.ns_steps, "coeffs": w.coeffs, "grad_dtype": w.grad_dtype, "grads": w.grad_kind,
+                   "ns_dtype": ns_dtype,
                    "mona": ("lite" if args.mona_lite else True) if w.mona else False, "hip_graph": graphed, "parallelism": "single_gpu"},
         "ns_tflops": ns_tflops,
         "ns_frac_of_peak": ns_tflops / peak,

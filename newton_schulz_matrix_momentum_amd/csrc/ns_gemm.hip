@@ -1050,6 +1050,10 @@ __global__ __launch_bounds__(kThreads, 2) void ns_gemm_kernel(GemmArgs args) {
 #define MUON_A_AHEAD 3
 #endif
 constexpr int kAAhead = MUON_A_AHEAD;     // A fragments read this many 16-row blocks ahead
+#ifndef MUON_WIDE_DEFER
+#define MUON_WIDE_DEFER 1
+#endif
+constexpr int kWideDefer = MUON_WIDE_DEFER;   // fragment groups whose MFMAs run after the stage barrier
 
 // ---------------------------------------------------------------------------
 // TILE x TILE block tile for fp16 / bf16 (TILE = 256: eight waves, two per
@@ -1094,7 +1098,7 @@ __global__ __launch_bounds__(TILE * 2, TILE == 256 ? 1 : 2) void ns_gemm_wide_ke
   const GemmClass &cl = args.cls[tr.ci];
   const int mat = tr.mat, tm = tr.tm, tn = tr.tn;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: scalar arithmetic
   const int wm = wave / WN_WAVES, wn = wave % WN_WAVES;
 
   const char *A = (const char *)cl.a + ((int64_t)mat * cl.sa + (int64_t)tm * TILE * cl.lda) * 2;
@@ -1103,11 +1107,15 @@ __global__ __launch_bounds__(TILE * 2, TILE == 256 ? 1 : 2) void ns_gemm_wide_ke
 
   // DMA: wave w moves rows [8 DMA_PER_WAVE w, +8 DMA_PER_WAVE) of A and of
   // B, 8 rows per instruction; lane L covers row L / 8 of the group and
-  // physical chunk L % 8, which holds logical chunk (L % 8) ^ (L / 8).
+  // physical chunk L % 8, which holds logical chunk (L % 8) ^ (L / 8).  The
+  // source address is a wave-uniform base plus a 32-bit lane offset, so the
+  // loads take the scalar-base form and need no vector address arithmetic.
   const int dma_row = lane >> 3;
   const int dma_chunk = (lane & 7) ^ dma_row;
-  const char *a_src = A + (int64_t)(wave * 8 * DMA_PER_WAVE + dma_row) * lda_b + dma_chunk * 16;
-  const char *b_src = B + (int64_t)(wave * 8 * DMA_PER_WAVE + dma_row) * ldb_b + dma_chunk * 16;
+  const char *a_base = A + (int64_t)(wave * 8 * DMA_PER_WAVE) * lda_b;
+  const char *b_base = B + (int64_t)(wave * 8 * DMA_PER_WAVE) * ldb_b;
+  const uint32_t a_off = (uint32_t)(dma_row * lda_b + dma_chunk * 16);
+  const uint32_t b_off = (uint32_t)(dma_row * ldb_b + dma_chunk * 16);
 
   // fragment of k-step ks (32 k) for row block base + lane % 16: logical
   // chunk 4 ks + lane / 16, physical chunk logical ^ (lane % 8)
@@ -1129,48 +1137,92 @@ __global__ __launch_bounds__(TILE * 2, TILE == 256 ? 1 : 2) void ns_gemm_wide_ke
       char *dst = lds + (kb & 1) * kWideStage + wave * DMA_PER_WAVE * 1024;
 #pragma unroll
       for (int j = 0; j < DMA_PER_WAVE; ++j)
-        __builtin_amdgcn_global_load_lds(
-            (const void __attribute__((address_space(1))) *)(a_src + (int64_t)j * 8 * lda_b + (int64_t)kb * kWideRowBytes),
-            (void __attribute__((address_space(3))) *)(dst + j * 1024), 16, 0, 0);
+      {
+        // the empty asm keeps each row group's base in scalar registers, so
+        // the compiler cannot fold the lane offset into per-lane addresses
+        const char *sa = a_base + (int64_t)j * 8 * lda_b + (int64_t)kb * kWideRowBytes;
+        asm volatile("" : "+s"(sa));
+        __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)(sa + a_off),
+                                         (void __attribute__((address_space(3))) *)(dst + j * 1024), 16, 0, 0);
+      }
 #pragma unroll
-      for (int j = 0; j < DMA_PER_WAVE; ++j)
-        __builtin_amdgcn_global_load_lds(
-            (const void __attribute__((address_space(1))) *)(b_src + (int64_t)j * 8 * ldb_b + (int64_t)kb * kWideRowBytes),
-            (void __attribute__((address_space(3))) *)(dst + TILE * kWideRowBytes + j * 1024), 16, 0, 0);
+      for (int j = 0; j < DMA_PER_WAVE; ++j) {
+        const char *sb = b_base + (int64_t)j * 8 * ldb_b + (int64_t)kb * kWideRowBytes;
+        asm volatile("" : "+s"(sb));
+        __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)(sb + b_off),
+                                         (void __attribute__((address_space(3))) *)(dst + TILE * kWideRowBytes + j * 1024),
+                                         16, 0, 0);
+      }
     };
     // fragment group g = FM ks + i: A row block i at k-step ks
     auto rd_a = [&](const char *slot, int g) -> u32x4 {
       return *(const u32x4 *)(slot + a_frag + (g % FM) * 16 * kWideRowBytes + ((g / FM) ? chunk1 : chunk0));
     };
+    constexpr int NQ = kAAhead + 1;             // A fragment ring entries
+    constexpr int D = kWideDefer;
+    static_assert(D >= 0 && D < NQ && D <= FM, "deferred groups: k-step 1 only, within the A ring");
+    // The deferred groups NG-D .. NG-1 hold ring entries NQ-D .. NQ-1 (NG is a
+    // multiple of NQ); the next stage's first PRE A fragments go to the others.
+    constexpr int PRE = kAAhead < NQ - D ? kAAhead : NQ - D;
+    u32x4 b0[FN], b1[FN], a_q[NQ];
+    auto mfma_group = [&](auto gc) {
+      constexpr int g = decltype(gc)::value;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) Mma<T>::run(a_q[g % NQ], (g < FM) ? b0[j] : b1[j], acc[g % FM][j]);
+    };
+    auto stage_head = [&](const char *slot, int lo, int hi) {
+#pragma unroll
+      for (int q = 0; q < kAAhead; ++q)
+        if (q >= lo && q < hi) a_q[q] = rd_a(slot, q);
+    };
     dma(0);
     if (nk > 1) dma(1);
     waitcnt_vm((nk > 1 ? 1 : 0) * PER_STAGE);
     __syncthreads();
+#pragma unroll
+    for (int j = 0; j < FN; ++j) b0[j] = *(const u32x4 *)(lds + b_frag + j * 16 * kWideRowBytes + chunk0);
+    stage_head(lds, 0, kAAhead);
 #pragma unroll 1
     for (int kb = 0; kb < nk; ++kb) {
       const char *slot = lds + (kb & 1) * kWideStage;
-      u32x4 b0[FN], b1[FN], a_q[kAAhead + 1];
-#pragma unroll
-      for (int j = 0; j < FN; ++j) b0[j] = *(const u32x4 *)(slot + b_frag + j * 16 * kWideRowBytes + chunk0);
-#pragma unroll
-      for (int q = 0; q < kAAhead; ++q) a_q[q] = rd_a(slot, q);
       static_for<0, NG>([&](auto gc) {
         constexpr int g = decltype(gc)::value;
-        constexpr int i = g % FM;
-        if constexpr (g + kAAhead < NG) a_q[(g + kAAhead) % (kAAhead + 1)] = rd_a(slot, g + kAAhead);
+        if constexpr (g + kAAhead < NG) a_q[(g + kAAhead) % NQ] = rd_a(slot, g + kAAhead);
         if constexpr (g < FN) b1[g] = *(const u32x4 *)(slot + b_frag + g * 16 * kWideRowBytes + chunk1);
         __builtin_amdgcn_sched_barrier(0);   // reads issue before the MFMAs that hide them
-#pragma unroll
-        for (int j = 0; j < FN; ++j) Mma<T>::run(a_q[g % (kAAhead + 1)], (g < FM) ? b0[j] : b1[j], acc[i][j]);
+        if constexpr (g < NG - D) mfma_group(gc);
         __builtin_amdgcn_sched_barrier(0);
       });
-      // stage kb+1 has landed (its DMA is the only one outstanding) and every
-      // wave is done with stage kb: its slot takes stage kb+2
+      // every fragment read of stage kb has returned (the deferred groups'
+      // operands are in registers), stage kb+1 has landed (its DMA is the
+      // only one outstanding) and every wave is past both: slot kb takes
+      // stage kb+2
+      if constexpr (D > 0) __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
       waitcnt_vm(0);
       __builtin_amdgcn_sched_barrier(0);
       asm volatile("s_barrier" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
       if (kb + 2 < nk) dma(kb + 2);
+      // stage kb+1's first fragments go out before the deferred MFMAs of
+      // stage kb, which cover their latency
+      const char *next = lds + ((kb + 1) & 1) * kWideStage;
+      const bool more = kb + 1 < nk;
+      if (more) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) b0[j] = *(const u32x4 *)(next + b_frag + j * 16 * kWideRowBytes + chunk0);
+        stage_head(next, 0, PRE);
+      }
+      // MFMAs have no memory effects and would float back above the barrier:
+      // their A operands pass through an empty asm that stays after the reads
+      static_assert(D <= 2, "two deferred groups at most");
+      if constexpr (D >= 1) asm volatile("" : "+v"(a_q[NQ - 1]) :: "memory");
+      if constexpr (D >= 2) asm volatile("" : "+v"(a_q[NQ - 2]) :: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      static_for<NG - D, NG>([&](auto gc) { mfma_group(gc); });
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (PRE < kAAhead) {
+        if (more) stage_head(next, PRE, kAAhead);
+      }
     }
   }
   static_assert(NWAVES * 64 == 2 * TILE, "epilogue_u8 takes 2 TILE threads");
