@@ -10,17 +10,21 @@
 //   lm_thin_kernel  the products against a (k + p)-wide panel, with the
 //                   fp64 Gram partials of the result fused in
 //   lm_eig_kernel   one block per matrix: fixed-order sum of its partials,
-//                   cyclic Jacobi eigen-decomposition in fp64 (parallel
-//                   round-robin pair order), then either the orthonormalising
-//                   factor W = V D^{-1/2} (numerical range of the panel) or
-//                   the truncated inverse square root V_k D_k^{-1/2} V_k^T
+//                   then either the orthonormalising factor of the panel
+//                   (pivoted Cholesky of the Gram matrix in fp64, stopped at
+//                   the panel's numerical rank, and the inverse of its
+//                   triangular factor) or, from a cyclic Jacobi
+//                   eigen-decomposition in fp64 (parallel round-robin pair
+//                   order), the truncated inverse square root
+//                   V_k D_k^{-1/2} V_k^T
 //   lm_pad_kernel   the caller's Gaussian test matrix into zero-padded
 //                   per-class buffers
 //
 // Working from Gram matrices in fp64 (the fp32 panels' products are exact in
 // fp64) keeps the orthonormalisation rank-revealing: a direction whose
-// eigenvalue falls under the cutoff is dropped instead of amplified.  Every
-// reduction has a fixed order, so results are bitwise reproducible.
+// pivot or eigenvalue falls under the cutoff is dropped instead of
+// amplified.  Every reduction has a fixed order, so results are bitwise
+// reproducible.
 #include "muon_kernels.h"
 
 #include <math.h>
@@ -179,12 +183,107 @@ __device__ __forceinline__ void round_pair(int N, int r, int k, int &p, int &q) 
   q = max(a, c);
 }
 
+// Orthonormalising factor from the Gram matrix G = P^T P of an n-column
+// panel P (Golub & Van Loan, "Matrix Computations", section 4.2, Cholesky
+// with symmetric pivoting): at step j the remaining index with the largest
+// Schur-complement diagonal is the pivot p_j, L[:, j] = S[:, p_j] / sqrt(S_pp)
+// and S <- S - L[:, j] L[:, j]^T; the factorisation stops when that diagonal
+// falls to cutoff * max(diag G) (the panel's numerical rank r).  With the
+// lower-triangular C[a][c] = L[p_a][c] (a, c < r), the selected columns
+// satisfy P_sel^T P_sel = C C^T, so P W with W[p_a][m] = (C^-1)[m][a] has r
+// orthonormal columns spanning P's range (the other columns of W are 0).
+// Writes W^T (out[m][i] = W[i][m]).  Runs on the block's first n threads
+// per step; s holds G on entry.
+__device__ void lm_orth_cholesky(int n, double cutoff, double (*S)[kLmKP + 1], double (*L)[kLmKP + 1],
+                                 double (*X)[kLmKP + 1], int *piv, int *chosen, int *ctl, double *tau_s,
+                                 float *out) {
+  const int tid = threadIdx.x, NT = (int)blockDim.x;
+  for (int i = tid; i < kLmKP; i += NT) chosen[i] = 0;
+  if (tid == 0) {
+    double dmax = 0.0;
+    bool bad = false;
+    for (int i = 0; i < n; ++i) {
+      const double d = S[i][i];
+      bad = bad || !(d >= 0.0) || isinf(d);
+      dmax = fmax(dmax, d);
+    }
+    ctl[1] = bad ? 1 : 0;              // non-finite (or negative) diagonal: NaN result
+    *tau_s = cutoff * dmax;
+  }
+  __syncthreads();
+  const double tau = *tau_s;
+  int r = 0;
+  if (ctl[1] == 0) {
+    for (int j = 0; j < n; ++j) {
+      if (tid < 64) {
+        // pivot: the unchosen index with the largest diagonal (lowest index on ties)
+        double best = (tid < n && !chosen[tid]) ? S[tid][tid] : -1.0;
+        int p = (tid < n && !chosen[tid]) ? tid : kLmKP;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+          const double ob = __shfl_xor(best, off);
+          const int op = __shfl_xor(p, off);
+          if (ob > best || (ob == best && op < p)) { best = ob; p = op; }
+        }
+        if (tid == 0) {
+          const bool go = p < n && best > tau && best > 0.0;
+          piv[j] = go ? p : -1;
+          if (go) chosen[p] = 1;
+        }
+      }
+      __syncthreads();
+      const int p = piv[j];
+      if (p < 0) break;                  // uniform: every thread read the same piv[j]
+      // L[:, j] = S[:, p] / sqrt(S_pp) and S <- S - L[:, j] L[:, j]^T on the
+      // unchosen indices, in one pass: column p is not updated (p is chosen)
+      const double inv = 1.0 / sqrt(S[p][p]);
+      for (int e = tid; e < n * n; e += NT) {
+        const int i = e / n, k = e - (e / n) * n;
+        if (k == p) L[i][j] = (i == p) ? S[p][p] * inv : (chosen[i] ? 0.0 : S[i][p] * inv);
+        else if (!chosen[i] && !chosen[k]) S[i][k] -= (S[i][p] * inv) * (S[k][p] * inv);
+      }
+      __syncthreads();
+      r = j + 1;
+    }
+  }
+  // X = C^-1 (lower triangular), column b by thread b: forward substitution
+  if (tid < r) {
+    const int b = tid;
+    for (int a = 0; a < b; ++a) X[a][b] = 0.0;
+    for (int a = b; a < r; ++a) {
+      const double *Ca = L[piv[a]];
+      double t = (a == b) ? 1.0 : 0.0;
+      for (int c = b; c < a; ++c) t -= Ca[c] * X[c][b];
+      X[a][b] = t / Ca[a];
+    }
+  }
+  __syncthreads();
+  // W^T staged in S (no longer needed): row m of W^T holds column m of W
+  for (int e = tid; e < kLmSlot; e += NT) {
+    const int m = e / kLmKP, i = e - (e / kLmKP) * kLmKP;
+    S[m][i] = ctl[1] ? __builtin_nan("") : 0.0;
+  }
+  __syncthreads();
+  for (int e = tid; e < r * r; e += NT) {
+    const int m = e / r, a = e - (e / r) * r;
+    if (a <= m) S[m][piv[a]] = X[m][a];
+  }
+  __syncthreads();
+  for (int e = tid; e < kLmSlot; e += NT) {
+    const int m = e / kLmKP, i = e - (e / kLmKP) * kLmKP;
+    out[e] = (float)S[m][i];
+  }
+}
+
 __global__ __launch_bounds__(256) void lm_eig_kernel(LmEigArgs args) {
   __shared__ double a[2][kLmKP][kLmKP + 1];   // double-buffered: each round reads one, writes the other
   __shared__ double v[kLmKP][kLmKP + 1];
   __shared__ double rot_c[kLmKP / 2], rot_s[kLmKP / 2];
   __shared__ int rot_p[kLmKP / 2], rot_q[kLmKP / 2];
   __shared__ int order[kLmKP];
+  __shared__ int chosen[kLmKP];
+  __shared__ int ctl[2];
+  __shared__ double tau_s;
   __shared__ int rotated;
   const int b = (int)blockIdx.x;
   const int ci = class_of(args.begin, b);
@@ -194,7 +293,7 @@ __global__ __launch_bounds__(256) void lm_eig_kernel(LmEigArgs args) {
   const int N = (n + 1) & ~1;   // even size for the pair schedule (a zero row/column pads an odd n)
   const int H = N / 2;          // pairs per round
   const int tid = threadIdx.x;
-  const int NT = (int)blockDim.x;   // 64 (one wave) for n <= 32, else 256
+  const int NT = (int)blockDim.x;
 
   // fixed-order sum of the matrix's partials; V = I
   const int nn = n * n;
@@ -219,6 +318,11 @@ __global__ __launch_bounds__(256) void lm_eig_kernel(LmEigArgs args) {
     v[i][j] = (i == j) ? 1.0 : 0.0;
   }
   __syncthreads();
+  if (args.mode == kLmOrth) {
+    lm_orth_cholesky(n, args.cutoff, a[0], a[1], v, order, chosen, ctl, &tau_s,
+                     cl.out + (int64_t)mat * cl.out_stride);
+    return;
+  }
 
   // cyclic Jacobi (Golub & Van Loan, "Matrix Computations", section 8.5):
   // a rotation J in rows / columns (p, q) with J_pp = J_qq = c, J_pq = s,
@@ -299,37 +403,23 @@ __global__ __launch_bounds__(256) void lm_eig_kernel(LmEigArgs args) {
   const double dmax = a[cur][order[0]][order[0]];
   const double floor_d = args.cutoff * dmax;
   float *out = cl.out + (int64_t)mat * cl.out_stride;
-  if (args.mode == kLmOrth) {
-    // out[j][i] = W[i][j], W[:, j] = v[:, order[j]] / sqrt(d_order[j]) for kept j
-    for (int e = tid; e < kLmSlot; e += NT) {
-      const int j = e / kLmKP, i = e - (e / kLmKP) * kLmKP;
-      float w = 0.f;
-      if (j < N && i < N) {
-        const int o = order[j];
-        const double d = a[cur][o][o];
-        if (dmax > 0.0 && d > floor_d) w = (float)(v[i][o] / sqrt(d));
-      }
-      out[e] = w;
-    }
-  } else {
-    // T = U U^T with U[:, m] = v[:, order[m]] / d^(1/4) over the kept m
-    // (reusing the other A buffer for U)
-    const int keep = min(args.rank, N);
-    double (*U)[kLmKP + 1] = a[cur ^ 1];
-    for (int e = tid; e < N * keep; e += NT) {
-      const int i = e / keep, m = e - (e / keep) * keep;
-      const int o = order[m];
-      const double d = a[cur][o][o];
-      U[i][m] = (dmax > 0.0 && d > floor_d) ? v[i][o] / sqrt(sqrt(d)) : 0.0;
-    }
-    __syncthreads();
-    for (int e = tid; e < kLmSlot; e += NT) {
-      const int i = e / kLmKP, j = e - (e / kLmKP) * kLmKP;
-      double t = 0.0;
-      if (i < N && j < N)
-        for (int m = 0; m < keep; ++m) t += U[i][m] * U[j][m];
-      out[e] = (float)t;
-    }
+  // T = U U^T with U[:, m] = v[:, order[m]] / d^(1/4) over the kept m
+  // (reusing the other A buffer for U)
+  const int keep = min(args.rank, N);
+  double (*U)[kLmKP + 1] = a[cur ^ 1];
+  for (int e = tid; e < N * keep; e += NT) {
+    const int i = e / keep, m = e - (e / keep) * keep;
+    const int o = order[m];
+    const double d = a[cur][o][o];
+    U[i][m] = (dmax > 0.0 && d > floor_d) ? v[i][o] / sqrt(sqrt(d)) : 0.0;
+  }
+  __syncthreads();
+  for (int e = tid; e < kLmSlot; e += NT) {
+    const int i = e / kLmKP, j = e - (e / kLmKP) * kLmKP;
+    double t = 0.0;
+    if (i < N && j < N)
+      for (int m = 0; m < keep; ++m) t += U[i][m] * U[j][m];
+    out[e] = (float)t;
   }
 }
 
@@ -361,7 +451,7 @@ hipError_t launch_lm_thin(const LmThinArgs &args, int nb, int blocks, hipStream_
 
 hipError_t launch_lm_eig(const LmEigArgs &args, int blocks, hipStream_t s) {
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(lm_eig_kernel, dim3(blocks), dim3(args.n <= 32 ? 64 : 256), 0, s, args);
+  hipLaunchKernelGGL(lm_eig_kernel, dim3(blocks), dim3(256), 0, s, args);
   return hipGetLastError();
 }
 

@@ -280,12 +280,13 @@ struct LmThinArgs {
   LmThinClass cls[kLmMaxClasses];
 };
 
-// Symmetric eigen-decomposition (fp64 Jacobi) of the sum of a matrix's Gram
+// Small symmetric factorisations (fp64) of the sum of a matrix's Gram
 // partials, one block per matrix, writing a kLmKP x kLmKP fp32 result:
-//   kLmOrth:  W^T with W = V_r D_r^{-1/2} over eigenvalues > cutoff * d_max
-//             (P W has orthonormal columns spanning the panel's range)
-//   kLmTrunc: T = V_k D_k^{-1/2} V_k^T over the `rank` largest eigenvalues
-//             that exceed cutoff * d_max
+//   kLmOrth:  W^T with P W orthonormal columns spanning the panel P's range:
+//             pivoted Cholesky, stopped where the pivot falls to
+//             cutoff * max(diag), and the inverse of its triangular factor
+//   kLmTrunc: T = V_k D_k^{-1/2} V_k^T (Jacobi eigen-decomposition) over the
+//             `rank` largest eigenvalues that exceed cutoff * d_max
 enum LmEigMode : int32_t { kLmOrth = 0, kLmTrunc = 1 };
 struct LmEigClass {
   float *out;              // first matrix's kLmKP x kLmKP result
@@ -300,7 +301,7 @@ struct LmEigArgs {
   int32_t n;
   int32_t mode;
   int32_t rank;
-  double cutoff;                         // relative to the largest eigenvalue
+  double cutoff;                         // relative to the largest diagonal / eigenvalue
   int32_t begin[kLmMaxClasses];          // first block (matrix) of each class
   const double *partials;
   LmEigClass cls[kLmMaxClasses];
