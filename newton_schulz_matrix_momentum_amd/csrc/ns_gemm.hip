@@ -1054,6 +1054,12 @@ constexpr int kAAhead = MUON_A_AHEAD;     // A fragments read this many 16-row b
 #define MUON_WIDE_DEFER 1
 #endif
 constexpr int kWideDefer = MUON_WIDE_DEFER;   // fragment groups whose MFMAs run after the stage barrier
+#ifndef MUON_WIDE_DMA_SPREAD
+#define MUON_WIDE_DMA_SPREAD 1
+#endif
+// 256 tile: DMA instructions per fragment group when a stage's DMA is spread
+// over the previous stage instead of issued at its start (0: at its start)
+constexpr int kWideSpreadPer = MUON_WIDE_DMA_SPREAD;
 
 // ---------------------------------------------------------------------------
 // TILE x TILE block tile for fp16 / bf16 (TILE = 256: eight waves, two per
@@ -1089,6 +1095,10 @@ __global__ __launch_bounds__(TILE * 2, TILE == 256 ? 1 : 2) void ns_gemm_wide_ke
   constexpr int kWideStage = (TILE + TILE) * kWideRowBytes;
   constexpr int DMA_PER_WAVE = TILE / 8 / NWAVES;   // 1 KB DMA instructions per operand per stage
   constexpr int PER_STAGE = 2 * DMA_PER_WAVE;    // DMA instructions per stage and wave
+  // the 128 tile's 8 groups per stage leave too little lead for a spread DMA
+  constexpr int SPREAD = TILE == 256 ? kWideSpreadPer : 0;
+  constexpr bool kWideSpread = SPREAD > 0;
+  static_assert(SPREAD == 0 || (PER_STAGE % SPREAD == 0 && PER_STAGE / SPREAD <= NG), "spread DMA");
   constexpr int kEpiBytes = 128 * (TILE + 4) * 4;   // epilogue_u8's staging band
   constexpr int kLdsBytes = 2 * kWideStage > kEpiBytes ? 2 * kWideStage : kEpiBytes;
   static_assert(kLdsBytes <= 160 * 1024, "LDS");
@@ -1133,26 +1143,23 @@ __global__ __launch_bounds__(TILE * 2, TILE == 256 ? 1 : 2) void ns_gemm_wide_ke
 
   const int nk = cl.K / (kWideRowBytes / 2);
   if (nk > 0) {
-    auto dma = [&](int kb) {
+    // DMA instruction q of stage kb (q < DMA_PER_WAVE: A rows, else B rows)
+    auto dma_piece = [&](int kb, int q) {
       char *dst = lds + (kb & 1) * kWideStage + wave * DMA_PER_WAVE * 1024;
+      const bool is_a = q < DMA_PER_WAVE;
+      const int j = is_a ? q : q - DMA_PER_WAVE;
+      // the empty asm keeps each row group's base in scalar registers, so
+      // the compiler cannot fold the lane offset into per-lane addresses
+      const char *sp = is_a ? a_base + (int64_t)j * 8 * lda_b + (int64_t)kb * kWideRowBytes
+                            : b_base + (int64_t)j * 8 * ldb_b + (int64_t)kb * kWideRowBytes;
+      asm volatile("" : "+s"(sp));
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)(sp + (is_a ? a_off : b_off)),
+                                       (void __attribute__((address_space(3))) *)(dst + (is_a ? 0 : TILE * kWideRowBytes) + j * 1024),
+                                       16, 0, 0);
+    };
+    auto dma = [&](int kb) {
 #pragma unroll
-      for (int j = 0; j < DMA_PER_WAVE; ++j)
-      {
-        // the empty asm keeps each row group's base in scalar registers, so
-        // the compiler cannot fold the lane offset into per-lane addresses
-        const char *sa = a_base + (int64_t)j * 8 * lda_b + (int64_t)kb * kWideRowBytes;
-        asm volatile("" : "+s"(sa));
-        __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)(sa + a_off),
-                                         (void __attribute__((address_space(3))) *)(dst + j * 1024), 16, 0, 0);
-      }
-#pragma unroll
-      for (int j = 0; j < DMA_PER_WAVE; ++j) {
-        const char *sb = b_base + (int64_t)j * 8 * ldb_b + (int64_t)kb * kWideRowBytes;
-        asm volatile("" : "+s"(sb));
-        __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)(sb + b_off),
-                                         (void __attribute__((address_space(3))) *)(dst + TILE * kWideRowBytes + j * 1024),
-                                         16, 0, 0);
-      }
+      for (int q = 0; q < PER_STAGE; ++q) dma_piece(kb, q);
     };
     // fragment group g = FM ks + i: A row block i at k-step ks
     auto rd_a = [&](const char *slot, int g) -> u32x4 {
@@ -1176,8 +1183,10 @@ __global__ __launch_bounds__(TILE * 2, TILE == 256 ? 1 : 2) void ns_gemm_wide_ke
         if (q >= lo && q < hi) a_q[q] = rd_a(slot, q);
     };
     dma(0);
-    if (nk > 1) dma(1);
-    waitcnt_vm((nk > 1 ? 1 : 0) * PER_STAGE);
+    if constexpr (!kWideSpread) {
+      if (nk > 1) dma(1);
+    }
+    waitcnt_vm((!kWideSpread && nk > 1 ? 1 : 0) * PER_STAGE);
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < FN; ++j) b0[j] = *(const u32x4 *)(lds + b_frag + j * 16 * kWideRowBytes + chunk0);
@@ -1187,6 +1196,14 @@ __global__ __launch_bounds__(TILE * 2, TILE == 256 ? 1 : 2) void ns_gemm_wide_ke
       const char *slot = lds + (kb & 1) * kWideStage;
       static_for<0, NG>([&](auto gc) {
         constexpr int g = decltype(gc)::value;
+        // spread: stage kb+1's DMA goes out SPREAD instructions per group over
+        // the first groups (its slot was freed by the previous barrier)
+        if constexpr (kWideSpread && g < PER_STAGE / (SPREAD > 0 ? SPREAD : 1)) {
+          if (kb + 1 < nk) {
+#pragma unroll
+            for (int q = 0; q < SPREAD; ++q) dma_piece(kb + 1, g * SPREAD + q);
+          }
+        }
         if constexpr (g + kAAhead < NG) a_q[(g + kAAhead) % NQ] = rd_a(slot, g + kAAhead);
         if constexpr (g < FN) b1[g] = *(const u32x4 *)(slot + b_frag + g * 16 * kWideRowBytes + chunk1);
         __builtin_amdgcn_sched_barrier(0);   // reads issue before the MFMAs that hide them
@@ -1202,7 +1219,9 @@ __global__ __launch_bounds__(TILE * 2, TILE == 256 ? 1 : 2) void ns_gemm_wide_ke
       __builtin_amdgcn_sched_barrier(0);
       asm volatile("s_barrier" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
-      if (kb + 2 < nk) dma(kb + 2);
+      if constexpr (!kWideSpread) {
+        if (kb + 2 < nk) dma(kb + 2);
+      }
       // stage kb+1's first fragments go out before the deferred MFMAs of
       // stage kb, which cover their latency
       const char *next = lds + ((kb + 1) & 1) * kWideStage;
