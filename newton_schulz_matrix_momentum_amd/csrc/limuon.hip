@@ -69,17 +69,28 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // consumed by four MFMAs).  The epilogue writes C, optionally C^T, and
 // optionally the fp64 Gram matrix of the block's rows of C (the next
 // orthonormalisation's input), so no Gram pass re-reads the panel.
-// Six stages: two blocks fit a CU at NB = 32 (72 KB each), so the second
-// block's waves hide each stage's LDS and barrier latency.
-constexpr int kThinRing = 6;
+// A stage's work is a few LDS reads and 16 MFMAs per wave, so a block is
+// bound by its per-stage latency (the wait, the barrier, the reads): many
+// small blocks per CU stream faster than a few deep rings.  Two stages and
+// six blocks per CU at a 32-wide panel (five at 64): 4.26 against 4.65 ms
+// per LiMuon step of the Llama-shaped set with six stages and two blocks,
+// 4.31 with three stages and four blocks.
+#ifndef MUON_THIN_RING
+#define MUON_THIN_RING 2
+#endif
+#ifndef MUON_THIN_BLOCKS
+#define MUON_THIN_BLOCKS 6
+#endif
+constexpr int kThinRing = MUON_THIN_RING;
+constexpr int kThinBlocks = MUON_THIN_BLOCKS;   // blocks per CU at a 32-wide panel (one fewer at 64)
 
 template <int NB>
-__global__ __launch_bounds__(256, NB == 32 ? 2 : 1) void lm_thin_kernel(LmThinArgs args) {
+__global__ __launch_bounds__(256, NB == 32 ? kThinBlocks : (kThinBlocks > 1 ? kThinBlocks - 1 : 1)) void lm_thin_kernel(LmThinArgs args) {
   constexpr int ROWS = kThinRows + NB;      // rows per stage: A then B
   constexpr int CHUNKS = ROWS / 8;          // 1 KB DMA instructions per stage
   constexpr int STAGE = ROWS * 128;         // bytes per stage
   constexpr int FN = NB / 16;
-  static_assert(kThinRing * STAGE <= (NB == 32 ? 80 : 128) * 1024, "LDS");
+  static_assert(kThinRing * STAGE * (NB == 32 ? kThinBlocks : (kThinBlocks > 1 ? kThinBlocks - 1 : 1)) <= 160 * 1024, "LDS");
   __shared__ __attribute__((aligned(1024))) char lds[kThinRing * STAGE];
   const int b = (int)blockIdx.x;
   const int ci = class_of(args.begin, b);
