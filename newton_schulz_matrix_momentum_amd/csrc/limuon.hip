@@ -434,6 +434,82 @@ __global__ __launch_bounds__(256) void lm_eig_kernel(LmEigArgs args) {
   }
 }
 
+// ------------------------------------------------------------------ final
+// W <- W - lr (gamma O + wd W) with O = P Z^T: a wide W (rows = s) takes
+// W[r][c] = sum_m P[r][m] Z[c][m], a tall one W[r][c] = sum_m Z[r][m] P[c][m].
+// The tile's 64 U rows and 64 V rows (kp columns each, rows padded to kp + 1
+// floats: distinct banks for the 16 V rows a wave reads) are staged in LDS;
+// thread t owns columns c0 + 4 (t % 16) .. + 3 of rows r0 + t / 16 + 16 q,
+// q = 0..3, so every W access is a 16-byte vector along a row.  O is an
+// fp32 sum over m in increasing order.
+__global__ __launch_bounds__(256) void lm_final_kernel(LmFinalArgs args) {
+  extern __shared__ float lm_final_smem[];   // U then V rows, kp + 1 floats each
+  const int ld = args.kp + 1;
+  float *su = lm_final_smem, *sv = lm_final_smem + kLmFinalTile * ld;
+  const int b = (int)blockIdx.x;
+  const int ci = class_of(args.begin, b);
+  const LmFinalClass &cl = args.cls[ci];
+  const int local = b - args.begin[ci];
+  const int mat = local / cl.tiles, t = local - mat * cl.tiles;
+  const FinalDesc fd = args.desc[cl.desc_base + mat];
+  const int tcn = (fd.cols + kLmFinalTile - 1) / kLmFinalTile;
+  const int r0 = (t / tcn) * kLmFinalTile, c0 = (t - (t / tcn) * tcn) * kLmFinalTile;
+  const float *P = cl.p + (int64_t)mat * cl.sp, *Z = cl.z + (int64_t)mat * cl.sz;
+  const float *U = fd.wide ? P : Z, *V = fd.wide ? Z : P;
+  const int kp = args.kp;
+  for (int e = threadIdx.x; e < kLmFinalTile * kp; e += 256) {
+    const int r = e / kp, m = e - (e / kp) * kp;
+    su[r * ld + m] = U[(int64_t)(r0 + r) * kLmKP + m];
+    sv[r * ld + m] = V[(int64_t)(c0 + r) * kLmKP + m];
+  }
+  __syncthreads();
+  const int cq = threadIdx.x & 15, rr = threadIdx.x >> 4;
+  float o[4][4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[q][e] = 0.f;
+  for (int m = 0; m < kp; ++m) {
+    float u[4], v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) u[q] = su[(rr + 16 * q) * ld + m];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = sv[(4 * cq + e) * ld + m];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[q][e] = fmaf(u[q], v[e], o[q][e]);
+  }
+  const float lr = args.lr, wd = args.wd, gm = fd.gamma;
+  const int c = c0 + 4 * cq;
+  const bool vec = (fd.cols & 3) == 0 && ((((uintptr_t)fd.weight) | ((uintptr_t)fd.ortho_out)) & 15) == 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = r0 + rr + 16 * q;
+    if (r >= fd.rows) continue;
+    float *w = fd.weight + (int64_t)r * fd.cols;
+    float *oo = fd.ortho_out ? fd.ortho_out + (int64_t)r * fd.cols : nullptr;
+    if (vec && c + 4 <= fd.cols) {
+      float4 x = *(const float4 *)(w + c);
+      x.x = x.x - lr * (gm * o[q][0] + wd * x.x);
+      x.y = x.y - lr * (gm * o[q][1] + wd * x.y);
+      x.z = x.z - lr * (gm * o[q][2] + wd * x.z);
+      x.w = x.w - lr * (gm * o[q][3] + wd * x.w);
+      *(float4 *)(w + c) = x;
+      if (oo) *(float4 *)(oo + c) = make_float4(o[q][0], o[q][1], o[q][2], o[q][3]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (c + e < fd.cols) {
+          const float x = w[c + e];
+          w[c + e] = x - lr * (gm * o[q][e] + wd * x);
+          if (oo) oo[c + e] = o[q][e];
+        }
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ pad
 __global__ __launch_bounds__(256) void lm_pad_kernel(LmPadArgs args) {
   const int b = (int)blockIdx.x;
@@ -463,6 +539,13 @@ hipError_t launch_lm_thin(const LmThinArgs &args, int nb, int blocks, hipStream_
 hipError_t launch_lm_eig(const LmEigArgs &args, int blocks, hipStream_t s) {
   if (blocks <= 0) return hipSuccess;
   hipLaunchKernelGGL(lm_eig_kernel, dim3(blocks), dim3(256), 0, s, args);
+  return hipGetLastError();
+}
+
+hipError_t launch_lm_final(const LmFinalArgs &args, int blocks, hipStream_t s) {
+  if (blocks <= 0) return hipSuccess;
+  const size_t smem = (size_t)2 * kLmFinalTile * (args.kp + 1) * sizeof(float);
+  hipLaunchKernelGGL(lm_final_kernel, dim3(blocks), dim3(256), smem, s, args);
   return hipGetLastError();
 }
 

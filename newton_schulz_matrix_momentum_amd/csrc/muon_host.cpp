@@ -46,7 +46,9 @@ muon_status fail(muon_status s, const char *fmt, ...) {
 
 constexpr int kMaxSteps = 64;
 static_assert(sizeof(GemmArgs) <= 4096 && sizeof(E1Args) <= 4096 && sizeof(E2Args) <= 4096 &&
-                  sizeof(E3Args) <= 4096 && sizeof(NormArgs) <= 4096 && sizeof(AdamArgs) <= 4096,
+                  sizeof(E3Args) <= 4096 && sizeof(NormArgs) <= 4096 && sizeof(AdamArgs) <= 4096 &&
+                  sizeof(LmThinArgs) <= 4096 && sizeof(LmEigArgs) <= 4096 && sizeof(LmPadArgs) <= 4096 &&
+                  sizeof(LmFinalArgs) <= 4096,
               "kernel arguments must stay within 4 KB");
 constexpr int64_t kMaxDim = int64_t(1) << 20;
 constexpr int64_t kMaxNumel = (int64_t(1) << 31) - 1;
@@ -914,7 +916,6 @@ muon_status run_limuon(const Plan &plan, char *ws, Tracer &st, float lr, float w
   const int nb = kp <= 32 ? 32 : 64;
   const int KP = kLmKP;
   double *parts = (double *)(ws + plan.off_lm_parts);
-  const size_t es = 4;
   const int pan_s = 0, pan_l = 1;   // panel kinds: s rows or l rows
 
   // pad the caller's test matrix into each class's [KP x Lp] buffer
@@ -1114,18 +1115,44 @@ muon_status run_limuon(const Plan &plan, char *ws, Tracer &st, float lr, float w
   if ((e = xt_times(kLmQt, kLmZ)) != MUON_OK) return e;                // B^T = X^T Q (+ Gram: B B^T)
   if ((e = eig(pan_l, kLmTrunc, kLmT)) != MUON_OK) return e;
   if ((e = apply(kLmQ, pan_s, kLmT, kLmP, -1, false)) != MUON_OK) return e;   // P = Q T
-  // O^T = B^T P^T (tall orientation), fused with the weight update
+  // O = P Z^T (Z = B^T) and the weight update, tile by tile of W
   {
-    StageBuilder sb(plan, ws, st);
-    for (size_t ci = 0; ci < plan.classes.size(); ++ci) {
-      const ClassInfo &cl = plan.classes[ci];
-      GemmClass g = make_gemm(cl, es, ws, cl.lm[kLmZ], cl.Lp, KP, cl.lm[kLmP], cl.Sp, KP, nb, false);
-      set_final(g, plan, cl, ws, lr, wd);
-      g.alpha = 1.0f;
-      sb.per_class[ci] = g;
-      sb.per_flops[ci] = 2.0 * (double)cl.s * (double)cl.l * kp;
+    LmFinalArgs a;
+    std::memset(&a, 0, sizeof(a));
+    for (int j = 0; j < kLmMaxClasses; ++j) a.begin[j] = INT32_MAX;
+    a.kp = kp;
+    a.lr = lr;
+    a.wd = wd;
+    a.desc = (const FinalDesc *)(ws + plan.off_desc);
+    int blocks = 0;
+    double flops = 0.0;
+    auto go = [&]() -> muon_status {
+      if (a.nclass == 0) return MUON_OK;
+      HIP_TRY(st.run(MUON_STAGE_GEMM, flops, [&]() { return launch_lm_final(a, blocks, st.s); }));
+      a.nclass = 0;
+      blocks = 0;
+      flops = 0.0;
+      for (int j = 0; j < kLmMaxClasses; ++j) a.begin[j] = INT32_MAX;
+      return MUON_OK;
+    };
+    for (const ClassInfo &cl : plan.classes) {
+      if (a.nclass == kLmMaxClasses) {
+        muon_status e2 = go();
+        if (e2 != MUON_OK) return e2;
+      }
+      LmFinalClass &c = a.cls[a.nclass];
+      c.p = buf(cl, kLmP);
+      c.z = buf(cl, kLmZ);
+      c.sp = cl.Sp * KP;
+      c.sz = cl.Lp * KP;
+      c.desc_base = cl.desc_base;
+      c.count = (int32_t)cl.members.size();
+      c.tiles = (int32_t)(((cl.s + kLmFinalTile - 1) / kLmFinalTile) * ((cl.l + kLmFinalTile - 1) / kLmFinalTile));
+      a.begin[a.nclass++] = blocks;
+      blocks += c.count * c.tiles;
+      flops += 2.0 * (double)cl.s * (double)cl.l * kp * (double)c.count;
     }
-    HIP_TRY(sb.launch());
+    if ((e = go()) != MUON_OK) return e;
   }
   return MUON_OK;
 }

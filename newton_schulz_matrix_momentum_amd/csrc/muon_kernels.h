@@ -307,6 +307,30 @@ struct LmEigArgs {
   LmEigClass cls[kLmMaxClasses];
 };
 
+// Weight update of the LiMuon step: O = P Z^T (P: s-row panel Q T, Z: l-row
+// panel X^T Q, both [rows x kLmKP], the first kp columns used) and
+// W <- W - lr (gamma O + wd W) in W's own orientation, one block per 64 x 64
+// tile of W; per-matrix W, gamma, orientation and the optional O copy come
+// from the FinalDesc table E1 wrote.
+constexpr int kLmFinalTile = 64;
+struct LmFinalClass {
+  const float *p;          // first matrix's P panel
+  const float *z;          // first matrix's Z panel
+  int64_t sp, sz;          // elements between matrices' panels
+  int32_t desc_base;       // FinalDesc slot of the class's first matrix
+  int32_t count;
+  int32_t tiles;           // 64 x 64 tiles of W per matrix
+  int32_t pad;
+};
+struct LmFinalArgs {
+  int32_t nclass;
+  int32_t kp;
+  float lr, wd;
+  int32_t begin[kLmMaxClasses];
+  const FinalDesc *desc;
+  LmFinalClass cls[kLmMaxClasses];
+};
+
 // Copy the caller's test matrix (kp rows of the long-side length, row
 // stride ld) into each class's zero-padded [kLmKP x lp] buffer.
 struct LmPadClass {
@@ -328,6 +352,7 @@ constexpr int kLmPadElems = 4096;     // padded elements per pad block
 hipError_t launch_lm_thin(const LmThinArgs &args, int nb, int blocks, hipStream_t s);
 hipError_t launch_lm_eig(const LmEigArgs &args, int blocks, hipStream_t s);
 hipError_t launch_lm_pad(const LmPadArgs &args, int blocks, hipStream_t s);
+hipError_t launch_lm_final(const LmFinalArgs &args, int blocks, hipStream_t s);
 
 // Record `msg` as the calling thread's muon_last_error() and return `s`.
 muon_status record_error(muon_status s, const char *msg);

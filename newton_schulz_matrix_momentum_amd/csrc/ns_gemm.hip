@@ -1118,8 +1118,9 @@ __global__ __launch_bounds__(TILE * 2, TILE == 256 ? 1 : 2) void ns_gemm_wide_ke
   // DMA: wave w moves rows [8 DMA_PER_WAVE w, +8 DMA_PER_WAVE) of A and of
   // B, 8 rows per instruction; lane L covers row L / 8 of the group and
   // physical chunk L % 8, which holds logical chunk (L % 8) ^ (L / 8).  The
-  // source address is a wave-uniform base plus a 32-bit lane offset, so the
-  // loads take the scalar-base form and need no vector address arithmetic.
+  // source address is a wave-uniform base (scalar registers) plus a 32-bit
+  // lane offset: one vector add per load, and the LDS destination (M0) is
+  // scalar arithmetic.
   const int dma_row = lane >> 3;
   const int dma_chunk = (lane & 7) ^ dma_row;
   const char *a_base = A + (int64_t)(wave * 8 * DMA_PER_WAVE) * lda_b;
@@ -1212,8 +1213,8 @@ __global__ __launch_bounds__(TILE * 2, TILE == 256 ? 1 : 2) void ns_gemm_wide_ke
       });
       // every fragment read of stage kb has returned (the deferred groups'
       // operands are in registers), stage kb+1 has landed (its DMA is the
-      // only one outstanding) and every wave is past both: slot kb takes
-      // stage kb+2
+      // only one outstanding) and every wave is past both: slot kb is free
+      // for stage kb+2 (issued right here, or spread over the next stage)
       if constexpr (D > 0) __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
       waitcnt_vm(0);
       __builtin_amdgcn_sched_barrier(0);

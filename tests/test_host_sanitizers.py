@@ -19,7 +19,7 @@ STUBS = r'''
 namespace muon {
 #define STUB(name, T) hipError_t name(const T &, int, hipStream_t) { return hipErrorNotSupported; }
 STUB(launch_e1, E1Args) STUB(launch_e2, E2Args) STUB(launch_e3, E3Args) STUB(launch_adamw, AdamArgs)
-STUB(launch_lm_eig, LmEigArgs) STUB(launch_lm_pad, LmPadArgs)
+STUB(launch_lm_eig, LmEigArgs) STUB(launch_lm_pad, LmPadArgs) STUB(launch_lm_final, LmFinalArgs)
 hipError_t launch_lm_thin(const LmThinArgs &, int, int, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_norm(const NormArgs &, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_gemm(const GemmArgs &, int, int, hipStream_t) { return hipErrorNotSupported; }
