@@ -905,12 +905,12 @@ muon_status run_gram(const Plan &plan, char *ws, Tracer &st, double sx0, float l
 //   Y = X Omega ; Q = orth(Y)
 //   q times: Z = orth(X^T Q) ; Q = orth(X Z)     (the last Q orthonormalised twice)
 //   B^T = X^T Q ; H = B B^T = V D V^T ; T = V_k D_k^{-1/2} V_k^T
-//   O^T = B^T (Q T)^T, fused with the weight update
-// orth(P) = P W with W = V_r D_r^{-1/2} from the fp64 Jacobi eigen-
-// decomposition of the Gram matrix P^T P (directions at most 1e-12 of the
-// largest eigenvalue dropped).  Every product against a panel runs in
-// lm_thin_kernel, which also writes the fp64 Gram partials of its result;
-// the final product is a grouped fp32 GEMM on 64 tiles.
+//   O = (Q T) B, fused with the weight update (lm_final_kernel)
+// orth(P) = P W from the fp64 Gram matrix P^T P: Cholesky with symmetric
+// pivoting, stopped where the pivot falls to 1e-12 of the largest diagonal,
+// and the inverse of the triangular factor.  Every product against a panel
+// runs in lm_thin_kernel, which also writes the fp64 Gram partials of its
+// result.
 muon_status run_limuon(const Plan &plan, char *ws, Tracer &st, float lr, float wd) {
   const int kp = plan.set.rank + plan.set.oversample;
   const int nb = kp <= 32 ? 32 : 64;
