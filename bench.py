@@ -499,7 +499,19 @@ def main():
     peak = PEAK_TFLOPS[ns_dtype]
     # dominant kernel by time per step
     dom = max(per_stage.items(), key=lambda kv: kv[1]["ms"])[0]
-    if dom == "gemm":
+    if dom == "gemm" and variant == "limuon":
+        # LiMuon's product launches (fp32, against k + p-wide panels) are
+        # bound by reading X and updating W, not by MFMA: algorithmic bytes
+        # are X read by the 2 + 2q products against it and W read + written
+        q = w.limuon_settings()["power_iters"]
+        step_bytes = w.numel * (4.0 * (2 + 2 * q) + 8.0)
+        per_launch_ms = gemm["ms"] / gemm["launches"]
+        per_launch_work = step_bytes / gemm["launches"]
+        roof = {"kernel": "LiMuon product launches (fp32 thin products against X, panel updates, weight "
+                          "update; all %g launches of a step, averaged)" % gemm["launches"], "bound": "hbm",
+                "achieved": per_launch_work / (per_launch_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "avg_launch_us": per_launch_ms * 1e3, "work_per_launch": per_launch_work, "traffic": None}
+    elif dom == "gemm":
         per_launch_work = gemm["work"] / gemm["launches"]
         per_launch_ms = gemm["ms"] / gemm["launches"]
         roof = {"kernel": "Newton-Schulz products (%s; all %g product launches of a step, averaged)"
