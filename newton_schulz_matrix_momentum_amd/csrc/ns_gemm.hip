@@ -1132,7 +1132,10 @@ __global__ __launch_bounds__(TILE * 2, TILE == 256 ? 1 : 2) void ns_gemm_wide_ke
   // chunk 4 ks + lane / 16, physical chunk logical ^ (lane % 8)
   const int fr_row = lane & 15;
   const int a_frag = (wm * WTM + fr_row) * kWideRowBytes;
-  const int b_frag = (TILE + wn * WTN + fr_row) * kWideRowBytes;
+  // a diagonal tile of a symmetric product (the same panel as A and B) moves
+  // the panel once and reads B's fragments from A's rows
+  const bool same_ab = tm == tn && cl.a == cl.b && cl.sa == cl.sb && cl.lda == cl.ldb;
+  const int b_frag = ((same_ab ? 0 : TILE) + wn * WTN + fr_row) * kWideRowBytes;
   const int chunk0 = (((lane >> 4)) ^ (lane & 7)) * 16;       // ks = 0
   const int chunk1 = ((4 + (lane >> 4)) ^ (lane & 7)) * 16;   // ks = 1
 
@@ -1148,6 +1151,7 @@ __global__ __launch_bounds__(TILE * 2, TILE == 256 ? 1 : 2) void ns_gemm_wide_ke
     auto dma_piece = [&](int kb, int q) {
       char *dst = lds + (kb & 1) * kWideStage + wave * DMA_PER_WAVE * 1024;
       const bool is_a = q < DMA_PER_WAVE;
+      if (!is_a && same_ab) return;
       const int j = is_a ? q : q - DMA_PER_WAVE;
       // the empty asm keeps each row group's base in scalar registers, so
       // the compiler cannot fold the lane offset into per-lane addresses
@@ -1187,7 +1191,8 @@ __global__ __launch_bounds__(TILE * 2, TILE == 256 ? 1 : 2) void ns_gemm_wide_ke
     if constexpr (!kWideSpread) {
       if (nk > 1) dma(1);
     }
-    waitcnt_vm((!kWideSpread && nk > 1 ? 1 : 0) * PER_STAGE);
+    // stage 0 landed: only stage 1's DMA (half of it on a diagonal tile) may be outstanding
+    waitcnt_vm(!kWideSpread && nk > 1 ? (same_ab ? DMA_PER_WAVE : PER_STAGE) : 0);
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < FN; ++j) b0[j] = *(const u32x4 *)(lds + b_frag + j * 16 * kWideRowBytes + chunk0);
