@@ -4,7 +4,8 @@ The bench line's roofline.traffic comes from a rocprofv3 summary in
 profiles/, keyed to a hash of the product kernels' code; these tests pin that
 the lookup returns the figure only for the code it was measured on, that the
 hash ignores comments and whitespace, and that the committed summaries of the
-default (tall Gram) set and the NanoChat set match the code as it stands.
+default (tall Gram) set, the Llama-shaped, MoE and NanoChat sets match the
+code as it stands.
 """
 import os
 import shutil
@@ -37,7 +38,8 @@ def _write_profile(tmp_path, workload, sha, nbytes):
         % (workload, sha, nbytes))
 
 
-@pytest.mark.parametrize("workload", ["gram_tall_32x4096x16384", "nanochat_6l_d192"])
+@pytest.mark.parametrize("workload", ["gram_tall_32x4096x16384", "llama430m_24l_d1024", "moe_64e_d2048",
+                                      "nanochat_6l_d192"])
 def test_committed_traffic_profiles_match_current_code(workload):
     traffic = bench.recorded_traffic(workload)
     assert traffic is not None and traffic > 0, (
