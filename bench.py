@@ -465,7 +465,7 @@ def cpu_baseline(args, w, variant, params, single_thread=False, seconds=None):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path (got --gpus %d)" % args.gpus,
+        print("bench.py runs on one GPU only: libmuon has no multi-GPU path (got --gpus %d)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
     import torch

@@ -55,7 +55,7 @@ extern "C" {
 typedef enum muon_status {
   MUON_OK = 0,
   MUON_ERR_INVALID_ARG = 1,        /* NULL pointer, bad size, non-finite scalar, aliasing */
-  MUON_ERR_UNSUPPORTED = 2,        /* valid request this build cannot serve */
+  MUON_ERR_UNSUPPORTED = 2,        /* valid request the library cannot serve */
   MUON_ERR_WORKSPACE_TOO_SMALL = 3,
   MUON_ERR_HIP = 4                 /* a HIP launch or runtime call failed */
 } muon_status;
