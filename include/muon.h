@@ -188,7 +188,8 @@ size_t muon_workspace_size(const muon_param *params, int n, int ns_steps,
  * rank + oversample > 64, power_iters outside [0, 16], rcond outside [0, 1),
  * sketch_ld below a long side, a sketch overlapping another buffer;
  * MUON_ERR_UNSUPPORTED for an unknown dtype (and for MUON_LIMUON with a
- * 16-bit ns_dtype); MUON_ERR_WORKSPACE_TOO_SMALL;
+ * 16-bit ns_dtype), and for a matrix with rows or cols above 2^20 or more
+ * than 2^31 - 1 elements; MUON_ERR_WORKSPACE_TOO_SMALL;
  * MUON_ERR_HIP when a launch fails. */
 muon_status muon_step(const muon_param *params, int n,
                       float lr, float mu, float beta_a, float alpha, float lambda,

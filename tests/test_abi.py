@@ -167,6 +167,9 @@ def test_unsupported(lib):
     assert step(lib, [param(0)], o=opts(lib, grad_dtype=9)) == U
     assert step(lib, [param(0)], o=opts(lib, ns_dtype=-1)) == U
     assert step(lib, [param(0, rows=1 << 21, cols=2)]) == U
+    assert step(lib, [param(0, rows=2, cols=(1 << 20) + 1)]) == U
+    assert step(lib, [param(0, rows=46341, cols=46341)]) == U      # 2^31 + 4633 elements
+    assert "exceeds the supported size" in _lib.last_error()
 
 
 def test_overlap_rejected(lib):

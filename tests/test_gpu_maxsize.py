@@ -1,0 +1,73 @@
+"""The largest matrix muon_step accepts (2^31 - 1 elements at most), in both
+orientations: 32768 x 65535 (direct, bf16) and 65535 x 32768 (Gram, fp16,
+restart every 3, divisor 1.03) -- element offsets past 2^31 inside one matrix
+in every stage, and workspace offsets past 4 GiB.
+
+The oracle cannot run a Newton-Schulz step at this size, so the gradient is
+built so that the answer is known exactly: a few nonzero entries G[a_i, b_i]
+on distinct rows and columns.  Its singular vectors are coordinate vectors,
+so every iterate keeps that support, O[a_i, b_i] is what the oracle gives
+for the compact r x r matrix with the same values, and every other entry of
+O -- hence of W_new - W_old with W_old = 0 -- is exactly zero (products of
+zeros).  Momentum must equal the gradient (first step from M = 0).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import rel_fro, tol_for
+
+pytestmark = pytest.mark.gpu
+
+ROWS_IDX = [0, 7, 1000, 20000, 32766, 32767]          # along the short side (32768)
+COLS_IDX = [65534, 3, 40000, 65533, 12345, 0]         # along the long side (65535)
+SIGMAS = [1.0, 0.5, 0.1, 0.03, 1e-2, 3e-3]
+
+
+def _run(rows, cols, variant, ns_dtype, divisor, restart):
+    import newton_schulz_matrix_momentum_amd as nsm
+    dev = torch.device("cuda:0")
+    tall = rows > cols
+    ai, bi = (COLS_IDX, ROWS_IDX) if tall else (ROWS_IDX, COLS_IDX)
+    print("max-size case: %d x %d, %s, %s" % (rows, cols, variant, ns_dtype), flush=True)
+    sig = torch.tensor(SIGMAS, dtype=torch.float32).to(torch.bfloat16)
+    grad = torch.zeros(rows, cols, dtype=torch.bfloat16, device=dev)
+    r_idx = torch.tensor(ai, device=dev)
+    c_idx = torch.tensor(bi, device=dev)
+    grad[r_idx, c_idx] = sig.to(dev)
+    p = {"weight": torch.zeros(rows, cols, dtype=torch.float32, device=dev), "grad": grad,
+         "momentum": torch.zeros(rows, cols, dtype=torch.float32, device=dev)}
+    lr, mu, wd = 0.02, 0.95, 0.01
+    coeffs = oracle.coefficient_table("quintic", 5)
+    nsm.muon_step([p], lr=lr, mu=mu, weight_decay=wd, ns_steps=5, variant=variant, ns_dtype=ns_dtype,
+                  divisor=divisor, restart_every=restart, step=0)
+    torch.cuda.synchronize()
+    # the compact problem: value i at (i, i)
+    n = len(SIGMAS)
+    g_small = np.zeros((n, n))
+    g_small[np.arange(n), np.arange(n)] = sig.double().numpy()
+    ref = oracle.muon_step_matrix(np.zeros((n, n)), g_small, np.zeros((n, n)), lr=lr, mu=mu, weight_decay=wd,
+                                  coeffs=coeffs, variant=variant, divisor=divisor, restart_every=restart)
+    w_sup = p["weight"][r_idx, c_idx].double().cpu().numpy()
+    m_sup = p["momentum"][r_idx, c_idx].double().cpu().numpy()
+    err = rel_fro(w_sup, np.diag(ref["weight"]))
+    print("  O on the support: rel err %.3g (tol %.0e)" % (err, tol_for(ns_dtype)), flush=True)
+    assert err <= tol_for(ns_dtype)
+    assert np.array_equal(m_sup, sig.double().numpy())
+    # everything off the support is exactly zero
+    p["weight"][r_idx, c_idx] = 0.0
+    p["momentum"][r_idx, c_idx] = 0.0
+    assert float(p["weight"].abs().max()) == 0.0
+    assert float(p["momentum"].abs().max()) == 0.0
+    del p, grad
+    torch.cuda.empty_cache()
+
+
+def test_max_size_wide_direct_bf16():
+    assert 32768 * 65535 <= (1 << 31) - 1
+    _run(32768, 65535, "direct", "bf16", 1.0, 0)
+
+
+def test_max_size_tall_gram_f16():
+    _run(65535, 32768, "gram", "f16", 1.03, 3)
