@@ -71,3 +71,35 @@ def test_max_size_wide_direct_bf16():
 
 def test_max_size_tall_gram_f16():
     _run(65535, 32768, "gram", "f16", 1.03, 3)
+
+
+def test_max_size_wide_limuon():
+    """LiMuon (rank 8 >= the gradient's rank 6, so the range finder is exact
+    and O is the polar factor: 1 at every (a_i, b_i)) at the largest size; O
+    is computed in fp32 and is zero outside the 6 x 6 block of the support's
+    rows and columns."""
+    import newton_schulz_matrix_momentum_amd as nsm
+    from workloads import make_sketch
+    rows, cols = 32768, 65535
+    dev = torch.device("cuda:0")
+    print("max-size case: %d x %d, limuon, f32" % (rows, cols), flush=True)
+    sig = torch.tensor(SIGMAS, dtype=torch.float32).to(torch.bfloat16)
+    grad = torch.zeros(rows, cols, dtype=torch.bfloat16, device=dev)
+    r_idx = torch.tensor(ROWS_IDX, device=dev)
+    c_idx = torch.tensor(COLS_IDX, device=dev)
+    grad[r_idx, c_idx] = sig.to(dev)
+    p = {"weight": torch.zeros(rows, cols, dtype=torch.float32, device=dev), "grad": grad,
+         "momentum": torch.zeros(rows, cols, dtype=torch.float32, device=dev)}
+    lr = 0.02
+    sketch = make_sketch(16, cols, 91, device=dev)
+    nsm.muon_step([p], lr=lr, mu=0.95, weight_decay=0.01, variant="limuon", ns_dtype="f32", sketch=sketch, rank=8,
+                  oversample=8, power_iters=1, step=0)
+    torch.cuda.synchronize()
+    block = p["weight"][r_idx[:, None], c_idx[None, :]].double().cpu().numpy()
+    err = rel_fro(block, -lr * np.eye(len(SIGMAS)))
+    print("  O on the support block: rel err %.3g (tol 1e-05)" % err, flush=True)
+    assert err <= 1e-5
+    p["weight"][r_idx[:, None], c_idx[None, :]] = 0.0
+    assert float(p["weight"].abs().max()) == 0.0
+    del p, grad
+    torch.cuda.empty_cache()
