@@ -8,8 +8,10 @@ built so that the answer is known exactly: a few nonzero entries G[a_i, b_i]
 on distinct rows and columns.  Its singular vectors are coordinate vectors,
 so every iterate keeps that support, O[a_i, b_i] is what the oracle gives
 for the compact r x r matrix with the same values, and every other entry of
-O -- hence of W_new - W_old with W_old = 0 -- is exactly zero (products of
-zeros).  Momentum must equal the gradient (first step from M = 0).
+O -- hence of W with W_0 = 0 -- is exactly zero (products of zeros).  The
+direct case runs two MONA steps on the same support, so momentum, MONA's
+acceleration and the stored previous gradient follow the compact problem's
+too, and are zero elsewhere.
 """
 import numpy as np
 import pytest
@@ -25,48 +27,64 @@ COLS_IDX = [65534, 3, 40000, 65533, 12345, 0]         # along the long side (655
 SIGMAS = [1.0, 0.5, 0.1, 0.03, 1e-2, 3e-3]
 
 
-def _run(rows, cols, variant, ns_dtype, divisor, restart):
+SIGMAS_STEP1 = [0.2, 0.9, 0.05, 0.3, 2e-3, 1e-2]       # second step (MONA): same support
+
+
+def _run(rows, cols, variant, ns_dtype, divisor, restart, mona=False):
     import newton_schulz_matrix_momentum_amd as nsm
     dev = torch.device("cuda:0")
     tall = rows > cols
     ai, bi = (COLS_IDX, ROWS_IDX) if tall else (ROWS_IDX, COLS_IDX)
-    print("max-size case: %d x %d, %s, %s" % (rows, cols, variant, ns_dtype), flush=True)
-    sig = torch.tensor(SIGMAS, dtype=torch.float32).to(torch.bfloat16)
-    grad = torch.zeros(rows, cols, dtype=torch.bfloat16, device=dev)
+    steps = 2 if mona else 1
+    print("max-size case: %d x %d, %s, %s, %d step(s)%s" % (rows, cols, variant, ns_dtype, steps,
+                                                            ", MONA" if mona else ""), flush=True)
     r_idx = torch.tensor(ai, device=dev)
     c_idx = torch.tensor(bi, device=dev)
-    grad[r_idx, c_idx] = sig.to(dev)
-    p = {"weight": torch.zeros(rows, cols, dtype=torch.float32, device=dev), "grad": grad,
+    p = {"weight": torch.zeros(rows, cols, dtype=torch.float32, device=dev),
+         "grad": torch.zeros(rows, cols, dtype=torch.bfloat16, device=dev),
          "momentum": torch.zeros(rows, cols, dtype=torch.float32, device=dev)}
-    lr, mu, wd = 0.02, 0.95, 0.01
+    if mona:
+        p["accel"] = torch.zeros(rows, cols, dtype=torch.float32, device=dev)
+        p["prev_grad"] = torch.zeros(rows, cols, dtype=torch.bfloat16, device=dev)
+    lr, mu, wd, beta_a, alpha = 0.02, 0.95, 0.01, 0.9, 0.5
     coeffs = oracle.coefficient_table("quintic", 5)
-    nsm.muon_step([p], lr=lr, mu=mu, weight_decay=wd, ns_steps=5, variant=variant, ns_dtype=ns_dtype,
-                  divisor=divisor, restart_every=restart, step=0)
-    torch.cuda.synchronize()
-    # the compact problem: value i at (i, i)
+    # the compact problem: value i at (i, i), advanced from its own outputs
     n = len(SIGMAS)
-    g_small = np.zeros((n, n))
-    g_small[np.arange(n), np.arange(n)] = sig.double().numpy()
-    ref = oracle.muon_step_matrix(np.zeros((n, n)), g_small, np.zeros((n, n)), lr=lr, mu=mu, weight_decay=wd,
-                                  coeffs=coeffs, variant=variant, divisor=divisor, restart_every=restart)
-    w_sup = p["weight"][r_idx, c_idx].double().cpu().numpy()
-    m_sup = p["momentum"][r_idx, c_idx].double().cpu().numpy()
-    err = rel_fro(w_sup, np.diag(ref["weight"]))
-    print("  O on the support: rel err %.3g (tol %.0e)" % (err, tol_for(ns_dtype)), flush=True)
+    z = np.zeros((n, n))
+    st = {"weight": z, "momentum": z, "accel": z if mona else None, "prev_grad": z if mona else None}
+    for step in range(steps):
+        sig = torch.tensor(SIGMAS if step == 0 else SIGMAS_STEP1, dtype=torch.float32).to(torch.bfloat16)
+        p["grad"][r_idx, c_idx] = sig.to(dev)
+        nsm.muon_step([p], lr=lr, mu=mu, beta_a=beta_a, alpha=alpha, weight_decay=wd, ns_steps=5, variant=variant,
+                      ns_dtype=ns_dtype, divisor=divisor, restart_every=restart, step=step)
+        g_small = np.zeros((n, n))
+        g_small[np.arange(n), np.arange(n)] = sig.double().numpy()
+        ref = oracle.muon_step_matrix(st["weight"], g_small, st["momentum"], lr=lr, mu=mu, weight_decay=wd,
+                                      coeffs=coeffs, variant=variant, divisor=divisor, restart_every=restart,
+                                      accel=st["accel"], prev_grad=st["prev_grad"], beta_a=beta_a, alpha=alpha,
+                                      step=step)
+        st = {"weight": ref["weight"], "momentum": ref["momentum"], "accel": ref.get("accel"),
+              "prev_grad": ref.get("prev_grad")}
+    torch.cuda.synchronize()
+    sup = lambda k: p[k][r_idx, c_idx].double().cpu().numpy()
+    err = rel_fro(sup("weight"), np.diag(st["weight"]))
+    print("  W on the support: rel err %.3g (tol %.0e)" % (err, tol_for(ns_dtype)), flush=True)
     assert err <= tol_for(ns_dtype)
-    assert np.array_equal(m_sup, sig.double().numpy())
+    assert rel_fro(sup("momentum"), np.diag(st["momentum"])) <= 1e-6
+    if mona:
+        assert rel_fro(sup("accel"), np.diag(st["accel"])) <= 1e-6
+        assert np.array_equal(sup("prev_grad"), np.diag(st["prev_grad"]))
     # everything off the support is exactly zero
-    p["weight"][r_idx, c_idx] = 0.0
-    p["momentum"][r_idx, c_idx] = 0.0
-    assert float(p["weight"].abs().max()) == 0.0
-    assert float(p["momentum"].abs().max()) == 0.0
-    del p, grad
+    for k in [k for k in ("weight", "momentum", "accel", "prev_grad") if k in p]:
+        p[k][r_idx, c_idx] = 0
+        assert float(p[k].abs().max()) == 0.0, k
+    del p
     torch.cuda.empty_cache()
 
 
-def test_max_size_wide_direct_bf16():
+def test_max_size_wide_direct_bf16_mona():
     assert 32768 * 65535 <= (1 << 31) - 1
-    _run(32768, 65535, "direct", "bf16", 1.0, 0)
+    _run(32768, 65535, "direct", "bf16", 1.0, 0, mona=True)
 
 
 def test_max_size_tall_gram_f16():
